@@ -1,0 +1,222 @@
+"""Pins of the oracle's attention steps.
+
+* The fp64 exact mode is checked against a NumPy/SciPy brute-force softmax
+  attention and against the softmax invariants (rows of P sum to one, the
+  output is unchanged when every score of a row shifts by the same amount --
+  the property smooth_k relies on -- and causal masking hides future keys).
+* The quantized (emulated) mode is checked against exact attention evaluated
+  on its own dequantized operands, within the error bound that rounding P to
+  fp16 or FP8 allows, against a closed form that uses torch's float8 cast on
+  a single key tile, against exact integer score dumps, and against the
+  closed-form log-sum-exp.
+
+Sources: SageAttention deployment guide (pwwt.cn), sec. 1 (softmax(QK^T)V with
+INT8 Q/K and FP8 V), sec. 4.1 (sm_scale default 1/sqrt(head_dim), is_causal,
+return_lse), sec. 4.2 (smooth_k); SageAttention 2.2.0 on the RX 9070 XT
+(pnsm.cn), sec. 2 (blockwise softmax as in FlashAttention).
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special as sps
+import torch
+
+import oracle
+
+
+def _half(shape, rng, scale=1.0, bias=0.0):
+    return (rng.standard_normal(shape) * scale + bias).astype(np.float16).astype(np.float32)
+
+
+def _brute(q, k, v, sm, causal):
+    s = (q.astype(np.float64) @ k.astype(np.float64).T) * sm
+    if causal:
+        s = np.where(np.arange(k.shape[0])[None, :] <= np.arange(q.shape[0])[:, None], s, -np.inf)
+    p = sps.softmax(s, axis=1)
+    return p @ v.astype(np.float64), sps.logsumexp(s, axis=1)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq,nk,d", [(37, 37, 16), (20, 75, 40), (64, 33, 128)])
+def test_exact_mode_matches_bruteforce(causal, nq, nk, d):
+    rng = np.random.default_rng(nq * 7 + nk + d)
+    q, k, v = _half((1, 2, nq, d), rng), _half((1, 2, nk, d), rng), _half((1, 2, nk, d), rng)
+    r = oracle.exact_forward(q, k, v, layout="HND", causal=causal)
+    for h in range(2):
+        o, l = _brute(q[0, h], k[0, h], v[0, h], 1 / math.sqrt(d), causal)
+        assert np.max(np.abs(r["out"][0][h] - o)) < 1e-12
+        assert np.max(np.abs(r["lse"][0][h] - l)) < 1e-12
+
+
+def test_exact_mode_invariants():
+    rng = np.random.default_rng(3)
+    nq, nk, d = 48, 80, 64
+    q, k, v = _half((1, 1, nq, d), rng), _half((1, 1, nk, d), rng), _half((1, 1, nk, d), rng)
+    # rows of P sum to one: V = 1 gives out = 1
+    r1 = oracle.exact_forward(q, k, np.ones_like(v), causal=True)
+    assert np.max(np.abs(r1["out"][0] - 1.0)) < 1e-13
+    # a per-channel shift of K shifts every score of a row by q_i.delta:
+    # the output is unchanged and lse moves by sm_scale * q_i.delta
+    delta = rng.standard_normal(d).astype(np.float64) * 3
+    r0 = oracle.exact_forward(q, k, v)
+    k2 = k.astype(np.float64) + delta[None, None, None, :]
+    r2 = oracle.exact_forward(q.astype(np.float64), k2, v.astype(np.float64))
+    assert np.max(np.abs(r2["out"][0] - r0["out"][0])) < 1e-12
+    corr = (q[0, 0].astype(np.float64) @ delta) / math.sqrt(d)
+    assert np.max(np.abs(r2["lse"][0][0] - r0["lse"][0][0] - corr)) < 1e-11
+    # causal: perturbing keys/values after row i leaves row i unchanged
+    rc = oracle.exact_forward(q, k, v, causal=True)
+    kp, vp = k.copy(), v.copy()
+    kp[:, :, 30:] += 5.0
+    vp[:, :, 30:] -= 7.0
+    rp = oracle.exact_forward(q, kp, vp, causal=True)
+    assert np.array_equal(rc["out"][0][:, :30], rp["out"][0][:, :30])
+    assert not np.allclose(rc["out"][0][:, 30:], rp["out"][0][:, 30:])
+
+
+def _dequantized(r, b, h, hk, gran, v_dtype, dtype):
+    """q_hat = q8 * qscale, k_hat = k8 * kscale (smoothed K), v_hat = operand
+    values with the V scale and mean applied."""
+    gq, gk = oracle.Q_GROUP[gran], oracle.K_GROUP[gran]
+    q8, k8 = r["q8"][b][h].astype(np.float64), r["k8"][b][hk].astype(np.float64)
+    qs = np.repeat(r["q_scale"][b][h], gq)[:q8.shape[0]].astype(np.float64)
+    ks = np.repeat(r["k_scale"][b][hk], gk)[:k8.shape[0]].astype(np.float64)
+    if v_dtype == "fp8":
+        vv = oracle.e4m3_decode(r["v8"][b][hk]).astype(np.float64) * r["v_scale"][b][hk][None, :]
+    else:
+        vv = r["v16"][b][hk].astype(np.float64)
+    return q8 * qs[:, None], k8 * ks[:, None], vv, r["v_mean"][b][hk].astype(np.float64)
+
+
+@pytest.mark.parametrize("gran", ["per_block", "per_warp", "per_thread"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_path_matches_exact_on_dequantized(gran, causal):
+    """With P rounded to fp16 the emulation differs from exact attention on its
+    own dequantized operands only by that rounding: |P~ - p| <= 2^-11 p for
+    normal p plus 2^-25 absolute (fp16 subnormal half-step), so
+    |out - out_exact| <= 2^-11 max|v| + n_k 2^-25 max|v| / l with l >= 1."""
+    rng = np.random.default_rng(21)
+    nq, nk, d = 150, 200, 48
+    q = _half((1, 3, nq, d), rng)
+    k = _half((1, 3, nk, d), rng, bias=0.7)
+    v = _half((1, 3, nk, d), rng, bias=-0.3)
+    r = oracle.reference_forward(q, k, v, dtype="fp16", gran=gran, v_dtype="fp16", smooth_k=True,
+                                 smooth_v=True, causal=causal, bk=64)
+    for h in range(3):
+        qh, kh, vh, vm = _dequantized(r, 0, h, h, gran, "fp16", "fp16")
+        vfull = vh + vm[None, :]
+        ex = oracle.exact_forward(qh[None, None], kh[None, None], vfull[None, None], causal=causal,
+                                  sm_scale=1 / math.sqrt(d))
+        bound = (2.0 ** -11 + nk * 2.0 ** -25) * np.abs(vh).max() + 1e-6
+        err = np.abs(r["out"][0][h] - ex["out"][0][0][:, :d]).max()
+        assert err <= bound, (err, bound)
+
+
+@pytest.mark.parametrize("tau", [0, 3])
+def test_fp8_single_tile_closed_form(tau):
+    """One key tile: P8 = E4M3(fl32(p * 448 / 2^tau)) with p = 2^(s - max),
+    out = sum_j dec(P8_j) v_j vscale / (448/2^tau * sum_j p_j); the FP8 cast
+    here is torch's."""
+    rng = np.random.default_rng(22)
+    nq, nk, d = 40, 100, 64
+    q, k, v = _half((1, 1, nq, d), rng), _half((1, 1, nk, d), rng), _half((1, 1, nk, d), rng)
+    r = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_warp", v_dtype="fp8", bk=128, tau=tau)
+    qh, kh, vh, vm = _dequantized(r, 0, 0, 0, "per_warp", "fp8", "fp16")
+    s = (qh @ kh.T) / math.sqrt(d) * math.log2(math.e)
+    p = np.exp2(s - s.max(axis=1, keepdims=True)).astype(np.float32)
+    pscale = 448.0 / 2 ** tau
+    scaled = (p.astype(np.float64) * pscale).astype(np.float32)
+    p8 = torch.from_numpy(scaled).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = (p8 @ vh) / (pscale * p.astype(np.float64).sum(axis=1, keepdims=True))
+    diff = np.abs(r["out"][0][0] - ref)
+    # s is formed in fp32 by the oracle and in fp64 here: a rare P8 tie may flip
+    assert np.mean(diff > 1e-6) < 0.01
+    assert diff.max() < 2e-3
+
+
+def test_fp8_schedule_without_max_updates_equals_single_tile():
+    """If every row's maximum lies in the first key tile, later tiles never
+    move the reference maximum, so a 16-key schedule reproduces the one-tile
+    result exactly (up to fp64 summation order)."""
+    rng = np.random.default_rng(23)
+    nq, nk, d = 32, 96, 64
+    q = np.abs(_half((1, 1, nq, d), rng))
+    k = _half((1, 1, nk, d), rng)
+    k[0, 0, :16] = np.abs(k[0, 0, :16]) + 2.0      # first tile dominates every row
+    v = _half((1, 1, nk, d), rng)
+    a = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_thread", smooth_k=False, bk=16)
+    b = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_thread", smooth_k=False, bk=96)
+    assert np.max(np.abs(a["out"][0] - b["out"][0])) < 1e-12
+    # with the maximum in the last tile the schedules differ (P8 rounds at
+    # different reference maxima) but both stay within the FP8 bound
+    k2 = k.copy()
+    k2[0, 0, :16] = _half((16, d), rng)
+    k2[0, 0, 80:] = np.abs(k2[0, 0, 80:]) + 2.0
+    a2 = oracle.reference_forward(q, k2, v, dtype="fp16", gran="per_thread", smooth_k=False, bk=16)
+    b2 = oracle.reference_forward(q, k2, v, dtype="fp16", gran="per_thread", smooth_k=False, bk=96)
+    d2 = np.abs(a2["out"][0] - b2["out"][0])
+    assert d2.max() > 1e-9 and d2.max() < 2 * 2.0 ** -4 * np.abs(v).max()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_path_within_bound_and_scores_exact(causal):
+    """E4M3 rounding of P (scaled to 448) has relative error <= 2^-4 for normal
+    values and absolute error <= 2^-10/448 below 2^-6/448, giving
+    |out - out_exact| <= (2^-4 + n_k 2^-10 / 448) max|v_hat|."""
+    rng = np.random.default_rng(24)
+    nq, nk, d = 130, 190, 128
+    q, k, v = _half((2, 2, nq, d), rng), _half((2, 2, nk, d), rng, bias=0.5), _half((2, 2, nk, d), rng)
+    r = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_thread", v_dtype="fp8", causal=causal,
+                                 want_scores=True, smooth_v=True)
+    for b in range(2):
+        for h in range(2):
+            S = r["q8"][b][h].astype(np.int64) @ r["k8"][b][h].astype(np.int64).T
+            assert np.array_equal(r["scores"][b][h], S)
+            qh, kh, vh, vm = _dequantized(r, b, h, h, "per_thread", "fp8", "fp16")
+            ex = oracle.exact_forward(qh[None, None], kh[None, None], (vh + vm[None, :])[None, None],
+                                      causal=causal, sm_scale=1 / math.sqrt(d))
+            bound = (2.0 ** -4 + nk * 2.0 ** -10 / 448) * np.abs(vh).max()
+            err = np.abs(r["out"][b][h] - ex["out"][0][0]).max()
+            assert err <= bound, (err, bound)
+            # typical error is far below the worst-case bound
+            assert np.sqrt(np.mean((r["out"][b][h] - ex["out"][0][0]) ** 2)) < 0.05 * bound
+
+
+def test_lse_closed_form_with_smoothing():
+    """lse is the log-sum-exp of the unsmoothed dequantized scores:
+    ln sum_j exp(sm_scale q_hat_i.(k_hat'_j + mean_k))."""
+    rng = np.random.default_rng(25)
+    nq, nk, d = 64, 150, 64
+    q, k, v = _half((1, 2, nq, d), rng), _half((1, 2, nk, d), rng, bias=1.5), _half((1, 2, nk, d), rng)
+    for causal in (False, True):
+        r = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_warp", smooth_k=True, causal=causal)
+        for h in range(2):
+            qh, kh, _, _ = _dequantized(r, 0, h, h, "per_warp", "fp8", "fp16")
+            km = r["k_mean"][0][h].astype(np.float64)
+            s = (qh @ (kh + km[None, :]).T) / math.sqrt(d)
+            if causal:
+                s = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None], s, -np.inf)
+            ref = sps.logsumexp(s, axis=1)
+            assert np.max(np.abs(r["lse"][0][h] - ref)) < 2e-5
+
+
+def test_gqa_and_varlen_slicing():
+    """GQA uses K/V head h // (Hq/Hkv); a packed varlen batch equals separate
+    dense problems (means, groups and scales restart per sequence)."""
+    rng = np.random.default_rng(26)
+    lens = [70, 33, 129]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    q, k, v = _half((T, 4, 64), rng), _half((T, 2, 64), rng, bias=1.0), _half((T, 2, 64), rng)
+    r = oracle.reference_forward(q, k, v, dtype="fp16", cu_seqlens_q=cu, cu_seqlens_k=cu, causal=True,
+                                 gran="per_thread")
+    for b, n in enumerate(lens):
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        qb = q[sl].transpose(1, 0, 2)[None].copy()
+        kb = np.repeat(k[sl].transpose(1, 0, 2), 2, axis=0)[None].copy()
+        vb = np.repeat(v[sl].transpose(1, 0, 2), 2, axis=0)[None].copy()
+        rb = oracle.reference_forward(qb, kb, vb, dtype="fp16", causal=True, gran="per_thread")
+        assert np.array_equal(r["out"][b], rb["out"][0])
+        assert np.array_equal(r["q8"][b], rb["q8"][0])
+        assert np.array_equal(r["k8"][b], rb["k8"][0][::2])
