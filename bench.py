@@ -1,0 +1,181 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized attention forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch already resident in
+HBM: sage_quant_qk (K mean, INT8 Q/K), sage_quant_v (V statistics, FP8 V^T)
+and sage_attn_fwd (INT8 QK^T, online softmax, FP8 P.V).  The default workload
+is B=2, H=8, N=4096, head_dim=128, fp16, per_warp INT8 Q/K, FP8 V.
+
+Prints ONE JSON line.  `value` is whole-step TOPS (4*B*H*Nq*Nk*d per step,
+halved for causal).  `roofline` describes the attention kernel, timed with HIP
+events on the stream it runs on; `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TOPS = {"fp8": 5000.0, "fp16": 2.0 / (1.0 / 5000.0 + 1.0 / 2500.0)}   # dense INT8/FP8; blended with fp16 PV
+METRIC = "quantized-attention TOPS at 1 GPU (seq 4096 & 17.5k) and % of INT8/FP8 MFMA peak"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("attn.hip", "sage_device.h", "sage_kernels.h"):
+        with open(os.path.join(ROOT, "quantized_attention_smooth_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from committed rocprofv3 counter runs,
+    if they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_attn_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_src_sha") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, seconds: float) -> dict:
+    """The oracle as it stands, on the host cores, over whole (sequence, head)
+    problems of the workload until about `seconds` of work: quantization of
+    the head's Q/K/V, then every query row of the attention."""
+    import numpy as np
+    import oracle
+    import workloads
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    q, k, v = (inp[x].float().numpy() for x in ("q", "k", "v"))
+    ops, heads, t_total = 0.0, 0, 0.0
+    grp = w.Hq // w.Hkv
+    for h in range(w.Hq):
+        hk = h // grp
+        if w.layout == "HND":
+            qs, ks, vs = q[:1, h:h + 1], k[:1, hk:hk + 1], v[:1, hk:hk + 1]
+        else:
+            qs, ks, vs = q[:1, :, h:h + 1], k[:1, :, hk:hk + 1], v[:1, :, hk:hk + 1]
+        t0 = time.perf_counter()
+        oracle.reference_forward(np.ascontiguousarray(qs), np.ascontiguousarray(ks), np.ascontiguousarray(vs),
+                                 dtype=w.dtype, layout=w.layout, causal=w.causal, gran=w.gran,
+                                 v_dtype=w.v_dtype, smooth_k=w.smooth_k, smooth_v=w.smooth_v)
+        t_total += time.perf_counter() - t0
+        heads += 1
+        per = 4.0 * w.Nq * w.Nk * w.d
+        ops += per / 2 if w.causal else per
+        if t_total >= seconds:
+            break
+    return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {w.B * w.Hq} (batch, head) problems of {w.name}, all {w.Nq} query rows, "
+                      f"quantization included; {t_total:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="b2h8n4096d128")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the quantized attention forward here runs on a single "
+              "MI355X (--gpus 1); multi-GPU sharding is not part of this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    import quantized_attention_smooth_amd as sage
+
+    w = workloads.WORKLOADS[args.workload]
+    if w.varlen:
+        raise SystemExit("the benchmark workload must be dense")
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    nk = w.Nk
+    ws = torch.empty(sage.workspace_bytes(w.B, w.Hkv, nk, w.d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        qk = sage.sage_quant_qk(q, k, tensor_layout=w.layout, qk_quant_gran=w.gran, smooth_k=w.smooth_k,
+                                workspace=ws)
+        qv = sage.sage_quant_v(v, tensor_layout=w.layout, v_dtype=w.v_dtype, smooth_v=w.smooth_v, workspace=ws)
+        if ev is not None:
+            ev[1].record(stream)
+        out = sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, is_causal=w.causal,
+                                 return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
+        if ev is not None:
+            ev[2].record(stream)
+        return out
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+
+    ops = workloads.attention_ops(w)
+    value = ops / (ms_per_step * 1e-3) / 1e12
+    attn_tops = ops / (attn_ms * 1e-3) / 1e12
+    peak = PEAK_TOPS[w.v_dtype]
+    # quantize-pass bytes: read Q, K, V once, K and V a second time for the
+    # statistics, write INT8 Q/K and FP8 V (+ small scale arrays)
+    elem = w.B * (w.Hq * w.Nq + 2 * w.Hkv * w.Nk) * w.d
+    quant_bytes = 2 * elem + 2 * 2 * w.B * w.Hkv * w.Nk * w.d + elem
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8+fp8" if w.v_dtype == "fp8" else "i8+fp16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "seq_len": w.Nq, "head_dim": w.d,
+                   "in_dtype": w.dtype, "layout": w.layout, "causal": w.causal, "qk_quant_gran": w.gran,
+                   "v_dtype": w.v_dtype, "pv_accum_dtype": w.pv_accum, "smooth_k": w.smooth_k,
+                   "smooth_v": w.smooth_v, "parallelism": "none (1 GPU)"},
+        "attn_kernel_ms": round(attn_ms, 5),
+        "attn_kernel_tops": round(attn_tops, 2),
+        "attn_pct_of_peak": round(100.0 * attn_tops / peak, 2),
+        "quant_ms": round(quant_ms, 5),
+        "quant_gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": peak, "unit": "TOPS",
+                     "frac": round(attn_tops / peak, 4), "traffic": measured_traffic(w.name)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,243 @@
+/*
+ * sage.h -- C ABI of the MI355X (gfx950) quantized attention forward.
+ *
+ * The library computes the SageAttention-style forward
+ *     out = softmax(Q K^T * sm_scale) V
+ * in the steps the SageAttention pages describe:
+ *   - smooth_k: subtract K's per-channel mean along the sequence before
+ *     quantizing K ("SageAttention deployment guide", pwwt.cn, sec. 4.2 table);
+ *   - Q and K quantized to INT8 with fp32 scale factors per block, per warp or
+ *     per thread (deployment guide, sec. 1 first bullet and sec. 4.2
+ *     qk_quant_gran); QK^T by 8-bit integer products with int32 accumulation;
+ *   - softmax computed online, block by block, as in FlashAttention
+ *     ("SageAttention 2.2.0 on the RX 9070 XT", pnsm.cn, sec. 2);
+ *   - V kept in FP16 or lowered to FP8, P.V accumulated in fp32
+ *     (deployment guide, sec. 1 second bullet, sec. 4 dispatch table and the
+ *     pv_accum_dtype row of sec. 4.2); smooth_v subtracts V's mean;
+ *   - output in FP16/BF16, same dtype as the inputs (deployment guide, sec. 1
+ *     third bullet), optionally with the log-sum-exp (sec. 4.1 return_lse).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *   allocates nothing and keeps no state between calls.
+ * - Every call is asynchronous on the caller's HIP stream (`stream`, a
+ *   hipStream_t; NULL = the legacy default stream) and on the current HIP
+ *   device.  Nothing is synchronised on the host.
+ * - Return value: SAGE_OK (0) or a negative error code.  All argument checks
+ *   run on the host before the first HIP call, so an invalid call launches
+ *   nothing and writes nothing.  sage_last_error() then returns a message
+ *   (thread-local, valid until the next call on the same thread).
+ * - Element strides are in elements; the channel (last) dimension must be
+ *   contiguous (stride 1), as the deployment guide's sec. 4.1 input rules ask.
+ * - head_dim d: 1..128.  d <= 64 is zero-padded to Dp = 64, 64 < d <= 128 to
+ *   Dp = 128 (deployment guide, sec. 4.1); d > 128 is SAGE_EINVAL.
+ * - Grouped K/V heads (GQA): Hq must be a multiple of Hkv; query head h reads
+ *   K/V head h / (Hq / Hkv) (deployment guide, sec. 4.1).
+ * - Nq and Nk may differ (deployment guide, sec. 4.1).
+ *
+ * Quantized tensor layouts (produced by sage_quant_qk / sage_quant_v and
+ * consumed by sage_attn_fwd / sage_attn_varlen_fwd):
+ *   Nq_pad = round_up(Nq, 128), Nk_pad = round_up(Nk, 128); for varlen calls
+ *   Nq, Nk are the maximum sequence lengths and B the number of sequences.
+ *   q8      int8   [B][Hq ][Nq_pad][Dp]   rows >= Nq (per sequence) are 0
+ *   q_scale float  [B][Hq ][Nq_pad / Gq]  Gq = 128 / 32 / 1 for
+ *                                          per_block / per_warp / per_thread
+ *   k8      int8   [B][Hkv][Nk_pad][Dp]
+ *   k_scale float  [B][Hkv][Nk_pad / Gk]  Gk = 64 / 64 / 16
+ *   k_mean  float  [B][Hkv][Dp]           written when smooth_k
+ *   vt      FP8 (E4M3FN bytes) or fp16/bf16, [B][Hkv][Dp][Nk_pad]: V
+ *           transposed, each aligned block of 64 keys stored in the order
+ *           pos = 32*h + 16*b + 4*r + e  for key = 32*b + 8*r + 4*h + e
+ *           (b in 0..1, r in 0..3, h in 0..1, e in 0..3); keys >= Nk are 0
+ *   v_scale float  [B][Hkv][Dp]           FP8 only: amax_c / 448
+ *   v_mean  float  [B][Hkv][Dp]           written when smooth_v
+ * Quantizer (all fp32, round to nearest even): per group, scale = amax/127,
+ * code = rint(x * fl32(127/amax)); all-zero group -> scale 0, codes 0.
+ * V (FP8): per channel c over the sequence, code = E4M3FN(clamp(v' *
+ * fl32(448/amax_c), +-448)), v' = fl32(v - v_mean_c) when smooth_v.
+ * Means are fl32(fl64(exact sum) / N), independent of summation order.
+ */
+#ifndef SAGE_H
+#define SAGE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAGE_OK 0
+#define SAGE_EINVAL (-1)        /* invalid argument; nothing launched          */
+#define SAGE_EUNSUPPORTED (-2)  /* valid request the library does not serve    */
+#define SAGE_EHIP (-3)          /* a HIP runtime call or launch failed         */
+
+#define SAGE_ABI_VERSION 1
+
+enum sage_dtype { SAGE_F16 = 0, SAGE_BF16 = 1 };
+enum sage_layout { SAGE_HND = 0, SAGE_NHD = 1 };
+enum sage_gran { SAGE_PER_BLOCK = 0, SAGE_PER_WARP = 1, SAGE_PER_THREAD = 2 };
+enum sage_vdtype { SAGE_V_FP8 = 0, SAGE_V_FP16 = 1 };
+/* pv_accum_dtype (deployment guide, sec. 4.2: fp16 / fp32 / fp16+fp32, also
+ * written fp32+fp16 and fp32+fp32 in sec. 4's dispatch table).  Every CDNA4
+ * matrix instruction accumulates in fp32, so every mode accumulates P.V in
+ * fp32, which is at least as accurate as the mode named. */
+enum sage_pv_accum { SAGE_ACC_FP32 = 0, SAGE_ACC_FP16 = 1, SAGE_ACC_FP16_FP32 = 2, SAGE_ACC_FP32_FP32 = 3 };
+
+/* ---------------------------------------------------------------------------
+ * sage_quant_qk: smooth K (optional) and quantize Q and K to INT8.
+ * Deployment guide sec. 1 (INT8 Q/K with per-block/per-thread scales) and
+ * sec. 4.2 (qk_quant_gran, smooth_k).
+ *
+ * Inputs: q, k in `dtype`; element (b, h, n, c) of q lives at
+ *   q + b*q_stride_b + h*q_stride_h + n*q_stride_n + c            (dense)
+ *   q + (cu_seqlens_q[b] + n)*q_stride_n + h*q_stride_h + c       (varlen)
+ * (same for k).  cu_seqlens_q/k: device int32 [B+1], non-decreasing, starting
+ * at 0, or both NULL for a dense batch; with them, Nq/Nk are upper bounds on
+ * every sequence length (max_seqlen) and means, groups and scales restart at
+ * each sequence.
+ * Outputs: q8, q_scale, k8, k_scale (layouts above); k_mean when smooth_k
+ * (may be NULL otherwise).
+ * workspace: device scratch of at least sage_quant_workspace_size() bytes
+ * (contents need not be initialised).
+ * Errors: SAGE_EINVAL for null/misaligned pointers (16-byte alignment for
+ * q8, k8 and the workspace; 4-byte for scales and means), d outside 1..128,
+ * B/H/N < 1, Hq % Hkv != 0, unknown enums, workspace too small.
+ * ------------------------------------------------------------------------- */
+typedef struct sage_quant_qk_params {
+    size_t struct_size;                 /* sizeof(sage_quant_qk_params) */
+    const void* q;
+    const void* k;
+    int dtype;                          /* enum sage_dtype */
+    int B, Hq, Hkv, Nq, Nk, d;
+    int64_t q_stride_b, q_stride_h, q_stride_n;
+    int64_t k_stride_b, k_stride_h, k_stride_n;
+    const int32_t* cu_seqlens_q;        /* device or NULL */
+    const int32_t* cu_seqlens_k;        /* device or NULL */
+    int gran;                           /* enum sage_gran */
+    int smooth_k;                       /* 0 / 1 */
+    int8_t* q8;
+    float* q_scale;
+    int8_t* k8;
+    float* k_scale;
+    float* k_mean;                      /* required when smooth_k */
+    void* workspace;
+    size_t workspace_bytes;
+} sage_quant_qk_params;
+
+int sage_quant_qk(const sage_quant_qk_params* p, void* stream);
+
+/* Scratch bytes sage_quant_qk and sage_quant_v need for the exact per-channel
+ * sums, for B sequences, H heads, N (max) tokens and head_dim d.  Returns 0
+ * for invalid sizes. */
+size_t sage_quant_workspace_size(int B, int H, int N, int d);
+
+/* ---------------------------------------------------------------------------
+ * sage_quant_v: smooth V (optional) and lay it out for the P.V product, in
+ * FP8 E4M3FN with a per-channel scale, or in the input dtype.
+ * Deployment guide sec. 1 second bullet (V lowered to FP8) and sec. 4.2
+ * (smooth_v).
+ * Inputs: v, strides and cu_seqlens_k as k in sage_quant_qk.
+ * Outputs: vt (FP8 bytes when v_dtype = SAGE_V_FP8, else `dtype` elements),
+ * v_scale (FP8 only), v_mean (when smooth_v).
+ * Errors: as sage_quant_qk.
+ * ------------------------------------------------------------------------- */
+typedef struct sage_quant_v_params {
+    size_t struct_size;
+    const void* v;
+    int dtype;
+    int B, Hkv, Nk, d;
+    int64_t v_stride_b, v_stride_h, v_stride_n;
+    const int32_t* cu_seqlens_k;
+    int v_dtype;                        /* enum sage_vdtype */
+    int smooth_v;
+    void* vt;
+    float* v_scale;                     /* required for FP8 */
+    float* v_mean;                      /* required when smooth_v */
+    void* workspace;
+    size_t workspace_bytes;
+} sage_quant_v_params;
+
+int sage_quant_v(const sage_quant_v_params* p, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sage_attn_fwd: the fused attention forward on quantized operands.
+ * Deployment guide sec. 1 (INT8 QK^T, FP8/FP16 P.V with fp32 accumulation,
+ * FP16/BF16 output), sec. 4.1 (tensor_layout, is_causal, sm_scale default
+ * 1/sqrt(head_dim), return_lse), sec. 4.2 (pv_accum_dtype); RX 9070 XT page
+ * sec. 2 (blockwise softmax).
+ *
+ * Per query row i of (b, h): S_ij = sum_c q8_ic k8_jc (int32);
+ * s_ij = S_ij * q_scale_i * k_scale_j * sm_scale (log2 domain inside); online
+ * softmax over 64-key tiles in ascending key order; P rounded to FP8 (scaled
+ * by 448) or to the input dtype; out = (P.V) * v_scale / l + v_mean.
+ * is_causal: key j is visible to query i iff j <= i (top-left alignment).
+ * lse (optional, fp32 [B][Hq][Nq]): natural-log log-sum-exp of the scores of
+ * the unsmoothed K, sm_scale * q_hat_i . k_j (adds sm_scale * q_hat_i . k_mean
+ * when k_mean is given).
+ * out: element (b, h, n, c) at out + b*o_stride_b + h*o_stride_h +
+ * n*o_stride_n + c for c < d, dtype out_dtype.
+ * Errors: SAGE_EINVAL for invalid sizes/enums/pointers (q8/k8/vt 16-byte
+ * aligned), sm_scale not finite; SAGE_EUNSUPPORTED for none.
+ * ------------------------------------------------------------------------- */
+typedef struct sage_attn_params {
+    size_t struct_size;
+    const int8_t* q8;
+    const float* q_scale;
+    const int8_t* k8;
+    const float* k_scale;
+    const float* k_mean;                /* NULL: K was not smoothed (no LSE term) */
+    const void* vt;
+    const float* v_scale;               /* FP8 only */
+    const float* v_mean;                /* NULL: V was not smoothed */
+    int B, Hq, Hkv, Nq, Nk, d;
+    int gran;                           /* must match sage_quant_qk */
+    int v_dtype;                        /* enum sage_vdtype */
+    int pv_accum;                       /* enum sage_pv_accum (all fp32 here) */
+    int is_causal;
+    float sm_scale;                     /* <= 0: 1/sqrt(d) */
+    int in_dtype;                       /* dtype q/k/v had (P precision on the FP16 path) */
+    void* out;
+    int out_dtype;                      /* enum sage_dtype */
+    int64_t o_stride_b, o_stride_h, o_stride_n;
+    float* lse;                         /* NULL: no LSE */
+} sage_attn_params;
+
+int sage_attn_fwd(const sage_attn_params* p, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sage_attn_varlen_fwd: as sage_attn_fwd for a packed batch of sequences
+ * (deployment guide sec. 4.2, sageattn_varlen with cu_seqlens_q/k).  The
+ * quantized operands use the layouts above with B = number of sequences and
+ * Nq/Nk = max_seqlen_q/k.  Causal masking is per sequence.  out is packed
+ * token-major: token (cu_seqlens_q[b] + n), head h, channel c at
+ * out + (cu_seqlens_q[b] + n)*o_stride_n + h*o_stride_h + c.
+ * lse (optional): fp32 [Hq][total_q], total_q = cu_seqlens_q[B].
+ * ------------------------------------------------------------------------- */
+typedef struct sage_attn_varlen_params {
+    sage_attn_params base;              /* o_stride_b is ignored */
+    const int32_t* cu_seqlens_q;        /* device int32 [B+1] */
+    const int32_t* cu_seqlens_k;        /* device int32 [B+1] */
+    int total_q;                        /* cu_seqlens_q[B] (for the LSE layout) */
+} sage_attn_varlen_params;
+
+int sage_attn_varlen_fwd(const sage_attn_varlen_params* p, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sage_debug_qk_scores: the int32 scores S = q8 k8^T of the attention kernel's
+ * own QK^T tile code, for checking them exactly.  mode 0: full dump,
+ * scores int32 [B][Hq][Nq][Nk]; mode 1: per-row checksums, int64
+ * [B][Hq][Nq][2] = (sum_j S_ij, sum_j (j+1) S_ij) modulo 2^64.  Dense only.
+ * Errors: as sage_attn_fwd.
+ * ------------------------------------------------------------------------- */
+int sage_debug_qk_scores(const sage_attn_params* p, int mode, void* scores, void* stream);
+
+const char* sage_last_error(void);
+int sage_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_H */

@@ -1,0 +1,292 @@
+"""Python binding of the C ABI (include/sage.h).
+
+torch is used only to allocate device memory and to take the current HIP
+stream; every computation runs in libsage.so's gfx950 kernels.  The entry
+points carry the C names (sage_quant_qk, sage_quant_v, sage_attn_fwd,
+sage_attn_varlen_fwd); sageattn / sageattn_varlen chain them the way the
+SageAttention deployment guide's API is used (pwwt.cn, sec. 4.1 signature:
+q, k, v, tensor_layout, is_causal, sm_scale, return_lse; sec. 4.2 knobs:
+qk_quant_gran, pv_accum_dtype, smooth_k, smooth_v; sageattn_varlen with
+cu_seqlens_q / cu_seqlens_k).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import math
+from typing import Optional
+
+import torch
+
+from . import _abi as A
+
+_GRAN = {"per_block": A.SAGE_PER_BLOCK, "per_warp": A.SAGE_PER_WARP, "per_thread": A.SAGE_PER_THREAD}
+_QG = {"per_block": 128, "per_warp": 32, "per_thread": 1}
+_KG = {"per_block": 64, "per_warp": 64, "per_thread": 16}
+_ACC = {"fp32": A.SAGE_ACC_FP32, "fp16": A.SAGE_ACC_FP16, "fp16+fp32": A.SAGE_ACC_FP16_FP32,
+        "fp32+fp16": A.SAGE_ACC_FP16_FP32, "fp32+fp32": A.SAGE_ACC_FP32_FP32}
+_DT = {torch.float16: A.SAGE_F16, torch.bfloat16: A.SAGE_BF16}
+PAD = 128
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def padded_head_dim(d: int) -> int:
+    if d < 1 or d > 128:
+        raise ValueError(f"head_dim {d} unsupported: must be 1..128 (deployment guide sec. 4.1)")
+    return 64 if d <= 64 else 128
+
+
+def _round_up(x: int, m: int) -> int:
+    return (x + m - 1) // m * m
+
+
+@dataclasses.dataclass
+class Geometry:
+    B: int
+    H: int
+    N: int
+    d: int
+    sb: int
+    sh: int
+    sn: int
+
+
+def _geometry(x: torch.Tensor, layout: str, cu: Optional[torch.Tensor], max_seqlen: Optional[int]) -> Geometry:
+    if x.dtype not in _DT:
+        raise ValueError(f"dtype {x.dtype} unsupported: fp16 or bf16")
+    if x.stride(-1) != 1:
+        raise ValueError("the last (head_dim) dimension must be contiguous")
+    if cu is not None:
+        if x.dim() != 3:
+            raise ValueError("varlen tensors are packed (total_tokens, heads, head_dim)")
+        if max_seqlen is None:
+            c = cu.to("cpu")
+            max_seqlen = int((c[1:] - c[:-1]).max())
+        return Geometry(cu.numel() - 1, x.shape[1], int(max_seqlen), x.shape[2], 0, x.stride(1), x.stride(0))
+    if x.dim() != 4:
+        raise ValueError("dense tensors are 4-D (HND or NHD)")
+    if layout == "HND":
+        return Geometry(x.shape[0], x.shape[1], x.shape[2], x.shape[3], x.stride(0), x.stride(1), x.stride(2))
+    if layout == "NHD":
+        return Geometry(x.shape[0], x.shape[2], x.shape[1], x.shape[3], x.stride(0), x.stride(2), x.stride(1))
+    raise ValueError(f"tensor_layout must be 'HND' or 'NHD', not {layout!r}")
+
+
+@dataclasses.dataclass
+class QuantQK:
+    q8: torch.Tensor
+    q_scale: torch.Tensor
+    k8: torch.Tensor
+    k_scale: torch.Tensor
+    k_mean: Optional[torch.Tensor]
+    gran: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: torch.dtype
+
+
+@dataclasses.dataclass
+class QuantV:
+    vt: torch.Tensor
+    v_scale: Optional[torch.Tensor]
+    v_mean: Optional[torch.Tensor]
+    v_dtype: str
+
+
+def workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(A.load().sage_quant_workspace_size(B, H, N, d))
+
+
+def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, *, tensor_layout: str = "HND",
+                  qk_quant_gran: str = "per_thread", smooth_k: bool = True,
+                  cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
+                  max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                  workspace: Optional[torch.Tensor] = None) -> QuantQK:
+    L = A.load()
+    if qk_quant_gran not in _GRAN:
+        raise ValueError(f"qk_quant_gran must be one of {sorted(_GRAN)}")
+    if q.dtype != k.dtype or q.device != k.device:
+        raise ValueError("q and k must share dtype and device")
+    gq = _geometry(q, tensor_layout, cu_seqlens_q, max_seqlen_q)
+    gk = _geometry(k, tensor_layout, cu_seqlens_k, max_seqlen_k)
+    if gq.d != gk.d or gq.B != gk.B:
+        raise ValueError("q and k must share batch and head_dim")
+    dp = padded_head_dim(gq.d)
+    dev = q.device
+    nq_pad, nk_pad = _round_up(gq.N, PAD), _round_up(gk.N, PAD)
+    q8 = torch.empty((gq.B, gq.H, nq_pad, dp), dtype=torch.int8, device=dev)
+    qs = torch.empty((gq.B, gq.H, nq_pad // _QG[qk_quant_gran]), dtype=torch.float32, device=dev)
+    k8 = torch.empty((gk.B, gk.H, nk_pad, dp), dtype=torch.int8, device=dev)
+    ks = torch.empty((gk.B, gk.H, nk_pad // _KG[qk_quant_gran]), dtype=torch.float32, device=dev)
+    km = torch.empty((gk.B, gk.H, dp), dtype=torch.float32, device=dev) if smooth_k else None
+    if smooth_k and workspace is None:
+        workspace = torch.empty(workspace_bytes(gk.B, gk.H, gk.N, gk.d), dtype=torch.uint8, device=dev)
+    p = A.QuantQKParams()
+    p.struct_size = ctypes.sizeof(A.QuantQKParams)
+    p.q, p.k, p.dtype = _ptr(q), _ptr(k), _DT[q.dtype]
+    p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d = gq.B, gq.H, gk.H, gq.N, gk.N, gq.d
+    p.q_stride_b, p.q_stride_h, p.q_stride_n = gq.sb, gq.sh, gq.sn
+    p.k_stride_b, p.k_stride_h, p.k_stride_n = gk.sb, gk.sh, gk.sn
+    p.cu_seqlens_q, p.cu_seqlens_k = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k)
+    p.gran, p.smooth_k = _GRAN[qk_quant_gran], int(bool(smooth_k))
+    p.q8, p.q_scale, p.k8, p.k_scale, p.k_mean = _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(km)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    A.check(L.sage_quant_qk(ctypes.byref(p), _stream()))
+    return QuantQK(q8, qs, k8, ks, km, qk_quant_gran, gq.B, gq.H, gk.H, gq.N, gk.N, gq.d, q.dtype)
+
+
+def sage_quant_v(v: torch.Tensor, *, tensor_layout: str = "HND", v_dtype: str = "fp8", smooth_v: bool = False,
+                 cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_k: Optional[int] = None,
+                 workspace: Optional[torch.Tensor] = None) -> QuantV:
+    L = A.load()
+    if v_dtype not in ("fp8", "fp16"):
+        raise ValueError("v_dtype must be 'fp8' or 'fp16' (the input's 16-bit type)")
+    g = _geometry(v, tensor_layout, cu_seqlens_k, max_seqlen_k)
+    dp = padded_head_dim(g.d)
+    dev = v.device
+    nk_pad = _round_up(g.N, PAD)
+    fp8 = v_dtype == "fp8"
+    vt = torch.empty((g.B, g.H, dp, nk_pad), dtype=torch.uint8 if fp8 else v.dtype, device=dev)
+    vs = torch.empty((g.B, g.H, dp), dtype=torch.float32, device=dev) if fp8 else None
+    vm = torch.empty((g.B, g.H, dp), dtype=torch.float32, device=dev) if smooth_v else None
+    if (fp8 or smooth_v) and workspace is None:
+        workspace = torch.empty(workspace_bytes(g.B, g.H, g.N, g.d), dtype=torch.uint8, device=dev)
+    p = A.QuantVParams()
+    p.struct_size = ctypes.sizeof(A.QuantVParams)
+    p.v, p.dtype = _ptr(v), _DT[v.dtype]
+    p.B, p.Hkv, p.Nk, p.d = g.B, g.H, g.N, g.d
+    p.v_stride_b, p.v_stride_h, p.v_stride_n = g.sb, g.sh, g.sn
+    p.cu_seqlens_k = _ptr(cu_seqlens_k)
+    p.v_dtype = A.SAGE_V_FP8 if fp8 else A.SAGE_V_FP16
+    p.smooth_v = int(bool(smooth_v))
+    p.vt, p.v_scale, p.v_mean = _ptr(vt), _ptr(vs), _ptr(vm)
+    p.workspace = _ptr(workspace)
+    p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    A.check(L.sage_quant_v(ctypes.byref(p), _stream()))
+    return QuantV(vt, vs, vm, v_dtype)
+
+
+def _attn_params(qk: QuantQK, qv: QuantV, out: torch.Tensor, lse: Optional[torch.Tensor], is_causal: bool,
+                 sm_scale: Optional[float], pv_accum_dtype: str, strides) -> A.AttnParams:
+    if pv_accum_dtype not in _ACC:
+        raise ValueError(f"pv_accum_dtype must be one of {sorted(_ACC)}")
+    p = A.AttnParams()
+    p.struct_size = ctypes.sizeof(A.AttnParams)
+    p.q8, p.q_scale, p.k8, p.k_scale, p.k_mean = _ptr(qk.q8), _ptr(qk.q_scale), _ptr(qk.k8), _ptr(qk.k_scale), _ptr(qk.k_mean)
+    p.vt, p.v_scale, p.v_mean = _ptr(qv.vt), _ptr(qv.v_scale), _ptr(qv.v_mean)
+    p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d = qk.B, qk.Hq, qk.Hkv, qk.Nq, qk.Nk, qk.d
+    p.gran = _GRAN[qk.gran]
+    p.v_dtype = A.SAGE_V_FP8 if qv.v_dtype == "fp8" else A.SAGE_V_FP16
+    p.pv_accum = _ACC[pv_accum_dtype]
+    p.is_causal = int(bool(is_causal))
+    p.sm_scale = float(sm_scale) if sm_scale is not None else 0.0
+    p.in_dtype = _DT[qk.dtype]
+    p.out, p.out_dtype = _ptr(out), _DT[out.dtype]
+    p.o_stride_b, p.o_stride_h, p.o_stride_n = strides
+    p.lse = _ptr(lse)
+    return p
+
+
+def sage_attn_fwd(qk: QuantQK, qv: QuantV, *, tensor_layout: str = "HND", is_causal: bool = False,
+                  sm_scale: Optional[float] = None, return_lse: bool = False, pv_accum_dtype: str = "fp32+fp32",
+                  out: Optional[torch.Tensor] = None):
+    L = A.load()
+    dev = qk.q8.device
+    if out is None:
+        shape = (qk.B, qk.Hq, qk.Nq, qk.d) if tensor_layout == "HND" else (qk.B, qk.Nq, qk.Hq, qk.d)
+        out = torch.empty(shape, dtype=qk.dtype, device=dev)
+    g = _geometry(out, tensor_layout, None, None)
+    lse = torch.empty((qk.B, qk.Hq, qk.Nq), dtype=torch.float32, device=dev) if return_lse else None
+    p = _attn_params(qk, qv, out, lse, is_causal, sm_scale, pv_accum_dtype, (g.sb, g.sh, g.sn))
+    A.check(L.sage_attn_fwd(ctypes.byref(p), _stream()))
+    return (out, lse) if return_lse else out
+
+
+def sage_attn_varlen_fwd(qk: QuantQK, qv: QuantV, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                         total_q: int, *, is_causal: bool = False, sm_scale: Optional[float] = None,
+                         return_lse: bool = False, pv_accum_dtype: str = "fp32+fp32",
+                         out: Optional[torch.Tensor] = None):
+    L = A.load()
+    dev = qk.q8.device
+    if out is None:
+        out = torch.empty((total_q, qk.Hq, qk.d), dtype=qk.dtype, device=dev)
+    lse = torch.empty((qk.Hq, total_q), dtype=torch.float32, device=dev) if return_lse else None
+    vp = A.AttnVarlenParams()
+    vp.base = _attn_params(qk, qv, out, lse, is_causal, sm_scale, pv_accum_dtype, (0, out.stride(1), out.stride(0)))
+    vp.base.struct_size = ctypes.sizeof(A.AttnVarlenParams)
+    vp.cu_seqlens_q, vp.cu_seqlens_k, vp.total_q = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(total_q)
+    A.check(L.sage_attn_varlen_fwd(ctypes.byref(vp), _stream()))
+    return (out, lse) if return_lse else out
+
+
+def sage_debug_qk_scores(qk: QuantQK, checksums: bool = False) -> torch.Tensor:
+    """int32 scores [B, Hq, Nq, Nk] from the attention kernel's QK^T tile code,
+    or int64 row checksums [B, Hq, Nq, 2] (sum_j S_ij, sum_j (j+1) S_ij)."""
+    L = A.load()
+    dev = qk.q8.device
+    if checksums:
+        buf = torch.empty((qk.B, qk.Hq, qk.Nq, 2), dtype=torch.int64, device=dev)
+    else:
+        buf = torch.empty((qk.B, qk.Hq, qk.Nq, qk.Nk), dtype=torch.int32, device=dev)
+    p = A.AttnParams()
+    p.struct_size = ctypes.sizeof(A.AttnParams)
+    p.q8, p.k8 = _ptr(qk.q8), _ptr(qk.k8)
+    p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d = qk.B, qk.Hq, qk.Hkv, qk.Nq, qk.Nk, qk.d
+    p.gran = _GRAN[qk.gran]
+    A.check(L.sage_debug_qk_scores(ctypes.byref(p), 1 if checksums else 0, _ptr(buf), _stream()))
+    return buf
+
+
+def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND",
+             is_causal: bool = False, sm_scale: Optional[float] = None, return_lse: bool = False, *,
+             qk_quant_gran: str = "per_thread", pv_accum_dtype: str = "fp32+fp32", smooth_k: bool = True,
+             smooth_v: bool = False, v_dtype: str = "fp8"):
+    """Quantized attention forward: out = softmax(q k^T * sm_scale) v.
+
+    q, k, v: fp16/bf16 CUDA tensors, (B, H, N, D) for HND or (B, N, H, D) for
+    NHD, same dtype; Hq must be a multiple of Hkv; D <= 128.
+    Returns out (same dtype and layout as q) and, with return_lse, the fp32
+    log-sum-exp [B, Hq, Nq]."""
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have the same dtype (deployment guide sec. 4.1)")
+    if not (q.device == k.device == v.device) or q.device.type != "cuda":
+        raise ValueError("q, k, v must be on the same GPU")
+    qk = sage_quant_qk(q, k, tensor_layout=tensor_layout, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k)
+    qv = sage_quant_v(v, tensor_layout=tensor_layout, v_dtype=v_dtype, smooth_v=smooth_v)
+    return sage_attn_fwd(qk, qv, tensor_layout=tensor_layout, is_causal=is_causal, sm_scale=sm_scale,
+                         return_lse=return_lse, pv_accum_dtype=pv_accum_dtype)
+
+
+def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                    cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, is_causal: bool = False,
+                    sm_scale: Optional[float] = None, return_lse: bool = False, *,
+                    qk_quant_gran: str = "per_thread", pv_accum_dtype: str = "fp32+fp32", smooth_k: bool = True,
+                    smooth_v: bool = False, v_dtype: str = "fp8"):
+    """Packed variable-length batch: q (total_q, Hq, D), k/v (total_k, Hkv, D);
+    cu_seqlens_* int32 [B+1] on the GPU.  Causal masking is per sequence.
+    Returns out (total_q, Hq, D) and, with return_lse, fp32 [Hq, total_q]."""
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must have the same dtype")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    qk = sage_quant_qk(q, k, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k, cu_seqlens_q=cu_seqlens_q,
+                       cu_seqlens_k=cu_seqlens_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+    qv = sage_quant_v(v, v_dtype=v_dtype, smooth_v=smooth_v, cu_seqlens_k=cu_seqlens_k, max_seqlen_k=max_seqlen_k)
+    return sage_attn_varlen_fwd(qk, qv, cu_seqlens_q, cu_seqlens_k, q.shape[0], is_causal=is_causal,
+                                sm_scale=sm_scale, return_lse=return_lse, pv_accum_dtype=pv_accum_dtype)
+
+
+def default_sm_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,302 @@
+// sage_api.hip -- the C ABI (include/sage.h): argument validation on the
+// host, workspace layout, and the launch sequence of each entry point.
+//
+// Every entry point validates all of its arguments before the first HIP call,
+// so an invalid call launches nothing and writes nothing; errors are reported
+// as a status code plus a thread-local message (sage_last_error()).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "sage.h"
+#include "sage_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int ok() {
+    g_err.clear();
+    return SAGE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+int dp_of(int d) { return d <= 64 ? 64 : 128; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+int q_group_shift(int gran) { return gran == SAGE_PER_BLOCK ? 7 : gran == SAGE_PER_WARP ? 5 : 0; }
+int k_group_shift(int gran) { return gran == SAGE_PER_THREAD ? 4 : 6; }
+bool valid_gran(int g) { return g == SAGE_PER_BLOCK || g == SAGE_PER_WARP || g == SAGE_PER_THREAD; }
+bool valid_dtype(int t) { return t == SAGE_F16 || t == SAGE_BF16; }
+
+constexpr int64_t kMaxDim = 1 << 30;
+
+int check_sizes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1)
+        return fail(SAGE_EINVAL, "sizes must be >= 1 (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d)", B, Hq, Hkv, Nq, Nk);
+    if (d < 1 || d > 128) return fail(SAGE_EINVAL, "head_dim %d unsupported: must be 1..128", d);
+    if (Hq % Hkv != 0) return fail(SAGE_EINVAL, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if ((int64_t)B * Hq > kMaxDim || Nq > kMaxDim - 256 || Nk > kMaxDim - 256)
+        return fail(SAGE_EINVAL, "sizes too large");
+    return SAGE_OK;
+}
+
+struct WsLayout {
+    size_t sum_off, min_off, max_off, inv_off, total;
+    int chunks;
+};
+
+WsLayout ws_layout(int B, int H, int N, int d) {
+    WsLayout w{};
+    const int dp = dp_of(d);
+    w.chunks = (int)((N + sage::kStatsChunk - 1) / sage::kStatsChunk);
+    const size_t cells = (size_t)B * H * w.chunks * dp;
+    auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+    w.sum_off = 0;
+    w.min_off = al(cells * 8);
+    w.max_off = w.min_off + al(cells * 4);
+    w.inv_off = w.max_off + al(cells * 4);
+    w.total = w.inv_off + al((size_t)B * H * dp * 4);
+    return w;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SAGE_EHIP, "%s: %s", what, hipGetErrorString(e));
+    return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sage_last_error(void) { return g_err.c_str(); }
+int sage_version(void) { return SAGE_ABI_VERSION; }
+
+size_t sage_quant_workspace_size(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1 || d < 1 || d > 128) return 0;
+    return ws_layout(B, H, N, d).total;
+}
+
+int sage_quant_qk(const sage_quant_qk_params* p, void* stream) {
+    if (!p) return fail(SAGE_EINVAL, "params is NULL");
+    if (p->struct_size < sizeof(sage_quant_qk_params)) return fail(SAGE_EINVAL, "struct_size too small");
+    if (!valid_dtype(p->dtype)) return fail(SAGE_EINVAL, "unknown dtype %d", p->dtype);
+    if (int r = check_sizes(p->B, p->Hq, p->Hkv, p->Nq, p->Nk, p->d)) return r;
+    if (!valid_gran(p->gran)) return fail(SAGE_EINVAL, "unknown qk_quant_gran %d", p->gran);
+    if (!p->q || !p->k || !p->q8 || !p->q_scale || !p->k8 || !p->k_scale)
+        return fail(SAGE_EINVAL, "NULL tensor pointer");
+    if (p->smooth_k && !p->k_mean) return fail(SAGE_EINVAL, "smooth_k needs k_mean");
+    if (!aligned(p->q, 2) || !aligned(p->k, 2)) return fail(SAGE_EINVAL, "q/k not 2-byte aligned");
+    if (!aligned(p->q8, 16) || !aligned(p->k8, 16)) return fail(SAGE_EINVAL, "q8/k8 must be 16-byte aligned");
+    if (!aligned(p->q_scale, 4) || !aligned(p->k_scale, 4) || (p->k_mean && !aligned(p->k_mean, 4)))
+        return fail(SAGE_EINVAL, "scales/means must be 4-byte aligned");
+    if ((p->cu_seqlens_q == nullptr) != (p->cu_seqlens_k == nullptr))
+        return fail(SAGE_EINVAL, "cu_seqlens_q and cu_seqlens_k must both be given or both be NULL");
+    if (p->q_stride_n <= 0 || p->k_stride_n <= 0 || p->q_stride_h < 0 || p->k_stride_h < 0 ||
+        p->q_stride_b < 0 || p->k_stride_b < 0)
+        return fail(SAGE_EINVAL, "negative or zero token stride");
+    const WsLayout ws = ws_layout(p->B, p->Hkv, p->Nk, p->d);
+    if (p->smooth_k) {
+        if (!p->workspace || !aligned(p->workspace, 16)) return fail(SAGE_EINVAL, "workspace NULL or misaligned");
+        if (p->workspace_bytes < ws.total)
+            return fail(SAGE_EINVAL, "workspace too small: %zu < %zu bytes", p->workspace_bytes, ws.total);
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool bf16 = p->dtype == SAGE_BF16;
+    const int dp = dp_of(p->d);
+    const int nq_pad = (int)round_up(p->Nq, sage::kPad), nk_pad = (int)round_up(p->Nk, sage::kPad);
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(p->workspace);
+    if (p->smooth_k) {
+        sage::StatsArgs st{};
+        st.x = p->k; st.sb = p->k_stride_b; st.sh = p->k_stride_h; st.sn = p->k_stride_n;
+        st.cu = p->cu_seqlens_k; st.B = p->B; st.H = p->Hkv; st.N = p->Nk; st.d = p->d; st.dp = dp;
+        st.chunks = ws.chunks; st.want_minmax = 0;
+        st.part_sum = wsb + ws.sum_off; st.part_min = nullptr; st.part_max = nullptr;
+        if (int r = hip_status(sage::launch_stats(st, bf16, s), "K statistics launch")) return r;
+        sage::FinalizeArgs fa{};
+        fa.part_sum = st.part_sum; fa.cu = p->cu_seqlens_k; fa.B = p->B; fa.H = p->Hkv; fa.N = p->Nk;
+        fa.dp = dp; fa.chunks = ws.chunks; fa.mode = 0; fa.mean = p->k_mean;
+        if (int r = hip_status(sage::launch_finalize(fa, bf16, s), "K mean launch")) return r;
+    }
+    auto vec_ok = [&](const void* x, int64_t sb, int64_t sh, int64_t sn) {
+        return aligned(x, 16) && p->d % 8 == 0 && sb % 8 == 0 && sh % 8 == 0 && sn % 8 == 0;
+    };
+    sage::QuantRowsArgs qa{};
+    qa.x = p->q; qa.sb = p->q_stride_b; qa.sh = p->q_stride_h; qa.sn = p->q_stride_n; qa.cu = p->cu_seqlens_q;
+    qa.B = p->B; qa.H = p->Hq; qa.N = p->Nq; qa.npad = nq_pad; qa.d = p->d;
+    qa.group_shift = q_group_shift(p->gran); qa.mean = nullptr; qa.out = p->q8; qa.scale = p->q_scale;
+    if (int r = hip_status(sage::launch_quant_rows(qa, bf16, vec_ok(p->q, p->q_stride_b, p->q_stride_h, p->q_stride_n), s),
+                           "Q quantize launch"))
+        return r;
+    sage::QuantRowsArgs ka{};
+    ka.x = p->k; ka.sb = p->k_stride_b; ka.sh = p->k_stride_h; ka.sn = p->k_stride_n; ka.cu = p->cu_seqlens_k;
+    ka.B = p->B; ka.H = p->Hkv; ka.N = p->Nk; ka.npad = nk_pad; ka.d = p->d;
+    ka.group_shift = k_group_shift(p->gran); ka.mean = p->smooth_k ? p->k_mean : nullptr;
+    ka.out = p->k8; ka.scale = p->k_scale;
+    if (int r = hip_status(sage::launch_quant_rows(ka, bf16, vec_ok(p->k, p->k_stride_b, p->k_stride_h, p->k_stride_n), s),
+                           "K quantize launch"))
+        return r;
+    return ok();
+}
+
+int sage_quant_v(const sage_quant_v_params* p, void* stream) {
+    if (!p) return fail(SAGE_EINVAL, "params is NULL");
+    if (p->struct_size < sizeof(sage_quant_v_params)) return fail(SAGE_EINVAL, "struct_size too small");
+    if (!valid_dtype(p->dtype)) return fail(SAGE_EINVAL, "unknown dtype %d", p->dtype);
+    if (int r = check_sizes(p->B, p->Hkv, p->Hkv, p->Nk, p->Nk, p->d)) return r;
+    if (p->v_dtype != SAGE_V_FP8 && p->v_dtype != SAGE_V_FP16) return fail(SAGE_EINVAL, "unknown v_dtype %d", p->v_dtype);
+    const bool fp8 = p->v_dtype == SAGE_V_FP8;
+    if (!p->v || !p->vt) return fail(SAGE_EINVAL, "NULL tensor pointer");
+    if (fp8 && !p->v_scale) return fail(SAGE_EINVAL, "FP8 V needs v_scale");
+    if (p->smooth_v && !p->v_mean) return fail(SAGE_EINVAL, "smooth_v needs v_mean");
+    if (!aligned(p->v, 2)) return fail(SAGE_EINVAL, "v not 2-byte aligned");
+    if (!aligned(p->vt, 16)) return fail(SAGE_EINVAL, "vt must be 16-byte aligned");
+    if ((p->v_scale && !aligned(p->v_scale, 4)) || (p->v_mean && !aligned(p->v_mean, 4)))
+        return fail(SAGE_EINVAL, "scales/means must be 4-byte aligned");
+    if (p->v_stride_n <= 0 || p->v_stride_h < 0 || p->v_stride_b < 0)
+        return fail(SAGE_EINVAL, "negative or zero token stride");
+    const bool need_stats = fp8 || p->smooth_v;
+    const WsLayout ws = ws_layout(p->B, p->Hkv, p->Nk, p->d);
+    if (need_stats) {
+        if (!p->workspace || !aligned(p->workspace, 16)) return fail(SAGE_EINVAL, "workspace NULL or misaligned");
+        if (p->workspace_bytes < ws.total)
+            return fail(SAGE_EINVAL, "workspace too small: %zu < %zu bytes", p->workspace_bytes, ws.total);
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const bool bf16 = p->dtype == SAGE_BF16;
+    const int dp = dp_of(p->d);
+    const int nk_pad = (int)round_up(p->Nk, sage::kPad);
+    uint8_t* wsb = reinterpret_cast<uint8_t*>(p->workspace);
+    float* v_inv = need_stats ? reinterpret_cast<float*>(wsb + ws.inv_off) : nullptr;
+    if (need_stats) {
+        sage::StatsArgs st{};
+        st.x = p->v; st.sb = p->v_stride_b; st.sh = p->v_stride_h; st.sn = p->v_stride_n;
+        st.cu = p->cu_seqlens_k; st.B = p->B; st.H = p->Hkv; st.N = p->Nk; st.d = p->d; st.dp = dp;
+        st.chunks = ws.chunks; st.want_minmax = fp8 ? 1 : 0;
+        st.part_sum = wsb + ws.sum_off;
+        st.part_min = reinterpret_cast<float*>(wsb + ws.min_off);
+        st.part_max = reinterpret_cast<float*>(wsb + ws.max_off);
+        if (int r = hip_status(sage::launch_stats(st, bf16, s), "V statistics launch")) return r;
+        sage::FinalizeArgs fa{};
+        fa.part_sum = st.part_sum; fa.part_min = st.part_min; fa.part_max = st.part_max;
+        fa.cu = p->cu_seqlens_k; fa.B = p->B; fa.H = p->Hkv; fa.N = p->Nk; fa.dp = dp; fa.chunks = ws.chunks;
+        fa.mode = fp8 ? 1 : 0; fa.smooth = p->smooth_v; fa.mean = p->smooth_v ? p->v_mean : nullptr;
+        fa.v_scale = p->v_scale; fa.v_inv = v_inv;
+        if (int r = hip_status(sage::launch_finalize(fa, bf16, s), "V statistics finalize launch")) return r;
+    }
+    sage::QuantVArgs va{};
+    va.v = p->v; va.sb = p->v_stride_b; va.sh = p->v_stride_h; va.sn = p->v_stride_n; va.cu = p->cu_seqlens_k;
+    va.B = p->B; va.H = p->Hkv; va.N = p->Nk; va.npad = nk_pad; va.d = p->d;
+    va.mean = p->smooth_v ? p->v_mean : nullptr; va.inv = v_inv; va.vt = p->vt;
+    const bool vec = aligned(p->v, 16) && p->d % 8 == 0 && p->v_stride_b % 8 == 0 && p->v_stride_h % 8 == 0 &&
+                     p->v_stride_n % 8 == 0;
+    if (int r = hip_status(sage::launch_quant_v(va, bf16, fp8, vec, s), "V quantize launch")) return r;
+    return ok();
+}
+
+static int check_attn(const sage_attn_params* p, bool varlen) {
+    if (int r = check_sizes(p->B, p->Hq, p->Hkv, p->Nq, p->Nk, p->d)) return r;
+    if (!valid_gran(p->gran)) return fail(SAGE_EINVAL, "unknown qk_quant_gran %d", p->gran);
+    if (p->v_dtype != SAGE_V_FP8 && p->v_dtype != SAGE_V_FP16) return fail(SAGE_EINVAL, "unknown v_dtype %d", p->v_dtype);
+    if (p->pv_accum < SAGE_ACC_FP32 || p->pv_accum > SAGE_ACC_FP32_FP32)
+        return fail(SAGE_EINVAL, "unknown pv_accum %d", p->pv_accum);
+    if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype)) return fail(SAGE_EINVAL, "unknown dtype");
+    if (!p->q8 || !p->q_scale || !p->k8 || !p->k_scale || !p->vt || !p->out)
+        return fail(SAGE_EINVAL, "NULL tensor pointer");
+    if (p->v_dtype == SAGE_V_FP8 && !p->v_scale) return fail(SAGE_EINVAL, "FP8 V needs v_scale");
+    if (!aligned(p->q8, 16) || !aligned(p->k8, 16) || !aligned(p->vt, 16))
+        return fail(SAGE_EINVAL, "q8/k8/vt must be 16-byte aligned");
+    if (!aligned(p->q_scale, 4) || !aligned(p->k_scale, 4) || (p->v_scale && !aligned(p->v_scale, 4)) ||
+        (p->k_mean && !aligned(p->k_mean, 4)) || (p->v_mean && !aligned(p->v_mean, 4)) ||
+        (p->lse && !aligned(p->lse, 4)))
+        return fail(SAGE_EINVAL, "fp32 arrays must be 4-byte aligned");
+    if (!aligned(p->out, 2)) return fail(SAGE_EINVAL, "out not 2-byte aligned");
+    if (!std::isfinite(p->sm_scale)) return fail(SAGE_EINVAL, "sm_scale must be finite");
+    if (p->o_stride_n <= 0 || p->o_stride_h < 0 || (!varlen && p->o_stride_b < 0))
+        return fail(SAGE_EINVAL, "negative or zero output stride");
+    return SAGE_OK;
+}
+
+static sage::AttnArgs attn_args(const sage_attn_params* p) {
+    sage::AttnArgs a{};
+    a.q8 = p->q8; a.qs = p->q_scale; a.k8 = p->k8; a.ks = p->k_scale; a.kmean = p->k_mean;
+    a.vt = p->vt; a.vs = p->v_scale; a.vmean = p->v_mean; a.out = p->out; a.lse = p->lse;
+    a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.d = p->d;
+    a.nq_pad = (int)round_up(p->Nq, sage::kPad);
+    a.nk_pad = (int)round_up(p->Nk, sage::kPad);
+    a.gq_shift = q_group_shift(p->gran);
+    a.gk_shift = k_group_shift(p->gran);
+    a.causal = p->is_causal ? 1 : 0;
+    a.sm_scale = p->sm_scale > 0.f ? p->sm_scale : (float)(1.0 / std::sqrt((double)p->d));
+    a.ob = p->o_stride_b; a.oh = p->o_stride_h; a.on = p->o_stride_n;
+    a.out_vec4 = aligned(p->out, 8) && p->o_stride_n % 4 == 0 && p->o_stride_h % 4 == 0 && p->o_stride_b % 4 == 0;
+    a.n_qtiles = (int)((p->Nq + sage::kBQ - 1) / sage::kBQ);
+    a.num_wg = p->B * p->Hq * a.n_qtiles;
+    return a;
+}
+
+static int pv_kind(const sage_attn_params* p) {
+    return p->v_dtype == SAGE_V_FP8 ? 0 : (p->in_dtype == SAGE_BF16 ? 2 : 1);
+}
+
+int sage_attn_fwd(const sage_attn_params* p, void* stream) {
+    if (!p) return fail(SAGE_EINVAL, "params is NULL");
+    if (p->struct_size < sizeof(sage_attn_params)) return fail(SAGE_EINVAL, "struct_size too small");
+    if (int r = check_attn(p, false)) return r;
+    sage::AttnArgs a = attn_args(p);
+    if (int r = hip_status(sage::launch_attn(a, dp_of(p->d), pv_kind(p), p->out_dtype == SAGE_BF16,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                           "attention launch"))
+        return r;
+    return ok();
+}
+
+int sage_attn_varlen_fwd(const sage_attn_varlen_params* p, void* stream) {
+    if (!p) return fail(SAGE_EINVAL, "params is NULL");
+    if (p->base.struct_size < sizeof(sage_attn_varlen_params))
+        return fail(SAGE_EINVAL, "struct_size too small (pass sizeof(sage_attn_varlen_params))");
+    if (int r = check_attn(&p->base, true)) return r;
+    if (!p->cu_seqlens_q || !p->cu_seqlens_k) return fail(SAGE_EINVAL, "varlen needs cu_seqlens_q and cu_seqlens_k");
+    if (!aligned(p->cu_seqlens_q, 4) || !aligned(p->cu_seqlens_k, 4)) return fail(SAGE_EINVAL, "cu_seqlens misaligned");
+    if (p->base.lse && p->total_q < 1) return fail(SAGE_EINVAL, "total_q must be >= 1 with lse");
+    sage::AttnArgs a = attn_args(&p->base);
+    a.cu_q = p->cu_seqlens_q;
+    a.cu_k = p->cu_seqlens_k;
+    a.lse_varlen = 1;
+    a.total_q = p->total_q;
+    a.out_vec4 = aligned(p->base.out, 8) && p->base.o_stride_n % 4 == 0 && p->base.o_stride_h % 4 == 0;
+    if (int r = hip_status(sage::launch_attn(a, dp_of(p->base.d), pv_kind(&p->base), p->base.out_dtype == SAGE_BF16,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                           "varlen attention launch"))
+        return r;
+    return ok();
+}
+
+int sage_debug_qk_scores(const sage_attn_params* p, int mode, void* scores, void* stream) {
+    if (!p) return fail(SAGE_EINVAL, "params is NULL");
+    if (p->struct_size < sizeof(sage_attn_params)) return fail(SAGE_EINVAL, "struct_size too small");
+    if (int r = check_sizes(p->B, p->Hq, p->Hkv, p->Nq, p->Nk, p->d)) return r;
+    if (mode != 0 && mode != 1) return fail(SAGE_EINVAL, "mode must be 0 or 1");
+    if (!p->q8 || !p->k8 || !scores) return fail(SAGE_EINVAL, "NULL pointer");
+    if (!aligned(p->q8, 16) || !aligned(p->k8, 16) || !aligned(scores, 8))
+        return fail(SAGE_EINVAL, "misaligned pointer");
+    sage::AttnArgs a = attn_args(p);
+    a.dbg = scores;
+    a.dbg_mode = mode;
+    if (int r = hip_status(sage::launch_qk_scores(a, dp_of(p->d), reinterpret_cast<hipStream_t>(stream)),
+                           "score dump launch"))
+        return r;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// sage_device.h -- device-side definitions shared by the gfx950 kernels of
+// the quantized attention forward (quantize passes and the attention kernel).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+#include "sage_kernels.h"
+
+namespace sage {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+
+// MFMA accumulator bias: the int32 QK^T accumulators start at the bit pattern
+// of 1.5 * 2^23, so that for |S| < 2^22 the accumulated integer, read as an
+// fp32, is exactly 1.5 * 2^23 + S (no int -> float conversion needed).
+// |S| <= 128 * 127 * 127 = 2064512 < 2^22 for head_dim <= 128.
+constexpr int kAccBiasBits = 0x4B400000;
+constexpr float kAccBias = 12582912.0f;
+constexpr int kNegInfBits = (int)0xFF800000u;   // -inf; smallest signed int32 of any score
+
+__device__ __forceinline__ float bits_f(int x) { return __int_as_float(x); }
+
+// fp16/bf16 element helpers -------------------------------------------------
+// (conversions from fp32 round to nearest even)
+template <bool BF16> struct Half;
+template <> struct Half<false> {
+    __device__ static float to_f(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+    __device__ static uint16_t from_f(float x) { return __builtin_bit_cast(uint16_t, (_Float16)x); }
+};
+template <> struct Half<true> {
+    __device__ static float to_f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+    __device__ static uint16_t from_f(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+};
+
+// Order of keys inside an aligned block of 64 in the transposed V operand:
+// position 32*h + 16*b + 4*r + e holds key 32*b + 8*r + 4*h + e.  This is the
+// order in which a lane of the S^T = K Q^T accumulator holds its keys (lane
+// half h, accumulator block b, register i = 4*r + e), so that the softmax
+// output feeds the P.V MFMA as its B operand without any data movement.
+__device__ __forceinline__ int v_perm_pos(int key64) {
+    int b = key64 >> 5, r = (key64 >> 3) & 3, h = (key64 >> 2) & 1, e = key64 & 3;
+    return (h << 5) | (b << 4) | (r << 2) | e;
+}
+
+// LDS 16-byte-chunk swizzles (bank-conflict-free ds_read_b128 over 32 rows).
+// K tile rows hold Dp bytes; V^T tile rows hold 64 keys (64 B for FP8,
+// 128 B for fp16/bf16).
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int row, int chunk) {
+    if constexpr (ROW_BYTES >= 128) return chunk ^ (row & 7);
+    else return chunk ^ ((row >> 1) & 3);
+}
+
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+    // Workgroups are dispatched round-robin over the 8 XCDs.  Renumber them so
+    // that consecutive logical ids (query tiles of the same head) run on the
+    // same XCD and share its L2 for the K/V stream.
+    const int per = nwg / 8, rem = nwg % 8;
+    const int xcd = bid % 8, idx = bid / 8;
+    return (xcd < rem) ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+}
+
+__device__ __forceinline__ float swap_half_max(float x) {
+    // max over lanes l and l ^ 32
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_half_sum(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
+    return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+}  // namespace sage

@@ -1,0 +1,109 @@
+// sage_kernels.h -- kernel argument blocks and host launch helpers shared by
+// the C-ABI layer (sage_api.hip) and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sage {
+
+// Tile sizes.  One workgroup of 4 wavefronts covers kBQ query rows (32 per
+// wavefront: one MFMA column block); the key loop advances kBK keys per step,
+// which is also the online-softmax tile.  Quantized rows are padded to kPad.
+constexpr int kBQ = 128;
+constexpr int kBK = 64;
+constexpr int kPad = 128;
+constexpr int kThreads = 256;
+
+// Per-channel statistics pass over K or V (exact sums; min/max for V).
+struct StatsArgs {
+    const void* x;
+    int64_t sb, sh, sn;          // element strides (batch, head, token)
+    const int32_t* cu;           // varlen offsets or nullptr
+    int B, H, N, d, dp;          // N: dense length or max length
+    int chunks;                  // token chunks per (b, h)
+    int want_minmax;
+    void* part_sum;              // [B][H][chunks][dp] int64 (fp16) or double (bf16)
+    float* part_min;             // [B][H][chunks][dp]
+    float* part_max;
+};
+
+// Reduce the partial statistics into means (and V scales).
+struct FinalizeArgs {
+    const void* part_sum;
+    const float* part_min;
+    const float* part_max;
+    const int32_t* cu;
+    int B, H, N, dp, chunks;
+    int mode;                    // 0: mean only; 1: FP8 V scale (+ mean if smooth)
+    int smooth;                  // V: subtract the mean before the amax
+    float* mean;                 // [B][H][dp] (may be null when !smooth)
+    float* v_scale;              // [B][H][dp]
+    float* v_inv;                // [B][H][dp] 448 / amax, for the quantize pass
+};
+
+// INT8 quantization of Q or K rows.
+struct QuantRowsArgs {
+    const void* x;
+    int64_t sb, sh, sn;
+    const int32_t* cu;
+    int B, H, N, npad, d;
+    int group_shift;             // log2(rows per scale group)
+    const float* mean;           // [B][H][dp] or nullptr
+    int8_t* out;                 // [B][H][npad][dp]
+    float* scale;                // [B][H][npad >> group_shift]
+};
+
+// Transposed V operand (FP8 codes or fp16/bf16).
+struct QuantVArgs {
+    const void* v;
+    int64_t sb, sh, sn;
+    const int32_t* cu;
+    int B, H, N, npad, d;
+    const float* mean;           // smooth_v mean or nullptr
+    const float* inv;            // FP8: 448 / amax per channel
+    void* vt;                    // [B][H][dp][npad]
+};
+
+struct AttnArgs {
+    const int8_t* q8;
+    const float* qs;
+    const int8_t* k8;
+    const float* ks;
+    const float* kmean;
+    const void* vt;
+    const float* vs;
+    const float* vmean;
+    void* out;
+    float* lse;
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    int B, Hq, Hkv, Nq, Nk, d;
+    int nq_pad, nk_pad;
+    int gq_shift, gk_shift;
+    int causal;
+    float sm_scale;
+    int64_t ob, oh, on;
+    int out_vec4;                // 4 consecutive channels may be stored as one 8-byte write
+    int lse_varlen;              // LSE layout [Hq][total_q] instead of [B][Hq][Nq]
+    int total_q;
+    int n_qtiles;                // query tiles per (b, h)
+    int num_wg;
+    // debug score dump (sage_debug_qk_scores)
+    void* dbg;
+    int dbg_mode;
+};
+
+// Launchers (defined in the kernel translation units).  Each returns the
+// hipError_t of the launch.
+hipError_t launch_stats(const StatsArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_quant_rows(const QuantRowsArgs& a, bool bf16, bool vec, hipStream_t s);
+hipError_t launch_quant_v(const QuantVArgs& a, bool bf16, bool fp8, bool vec, hipStream_t s);
+hipError_t launch_attn(const AttnArgs& a, int dp, int pv /*0 fp8, 1 fp16, 2 bf16*/, bool out_bf16,
+                       hipStream_t s);
+hipError_t launch_qk_scores(const AttnArgs& a, int dp, hipStream_t s);
+
+constexpr int kStatsChunk = 256;  // tokens per statistics chunk
+
+}  // namespace sage

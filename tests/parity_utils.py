@@ -1,0 +1,194 @@
+"""Shared helpers for the GPU parity tests: run the HIP path and the CPU
+oracle on the same seeded inputs and compare them.
+
+Tolerance for outputs: the GPU's fp16/bf16 output against the oracle's
+unrounded value, |diff| <= 2e-3 + one output ulp at |ref| (an fp16/bf16
+rounding flip alone can exceed 2e-3 near |ref| ~ 1), plus cosine similarity
+>= 0.9999; against exact fp64 attention, cosine similarity >= 0.999.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+import quantized_attention_smooth_amd as sage
+
+ABS_TOL = 2e-3
+COS_EMU = 0.9999
+COS_EXACT = 0.999
+LSE_TOL_EMU = 1e-3
+LSE_TOL_EXACT = 2e-2
+
+
+def out_ulp(ref: np.ndarray, dtype: str) -> np.ndarray:
+    mbits, emin = (7, -126) if dtype == "bf16" else (10, -14)
+    a = np.maximum(np.abs(ref), 2.0 ** emin)
+    e = np.floor(np.log2(a))
+    return np.exp2(np.maximum(e, emin) - mbits)
+
+
+def cosine(a: np.ndarray, b: np.ndarray) -> float:
+    a = a.astype(np.float64).ravel()
+    b = b.astype(np.float64).ravel()
+    return float(np.dot(a, b) / (np.linalg.norm(a) * np.linalg.norm(b) + 1e-300))
+
+
+def v_unpermute(vt: np.ndarray, n: int) -> np.ndarray:
+    """vt[..., Dp, Nk_pad] in the kernel's key order -> [..., n, Dp].
+    Inside each aligned block of 64 keys, key 32b + 8r + 4h + e sits at
+    position 32h + 16b + 4r + e (the layout stated in include/sage.h)."""
+    k = np.arange(n)
+    kk = k & 63
+    b, r, h, e = kk >> 5, (kk >> 3) & 3, (kk >> 2) & 1, kk & 3
+    pos = (k & ~63) | (h << 5) | (b << 4) | (r << 2) | e
+    return np.swapaxes(vt[..., pos], -1, -2)
+
+
+def sample_rows(seed: int, per: int):
+    """rows(b, n): the first and last rows, rows around 64/128-row tile edges,
+    and a seeded random sample."""
+    def f(b, n):
+        rng = np.random.default_rng(seed * 1000 + b)
+        fixed = [0, 1, 31, 32, 63, 64, 127, 128, 129, n // 2, n - 2, n - 1]
+        rnd = rng.integers(0, n, size=per)
+        r = np.unique(np.clip(np.concatenate([fixed, rnd]), 0, n - 1))
+        return r.astype(np.int32)
+    return f
+
+
+class Case:
+    """One workload evaluated on both sides."""
+
+    def __init__(self, w: workloads.Workload, inputs: dict, *, v_dtype: Optional[str] = None):
+        self.w = w
+        self.inp = inputs
+        self.v_dtype = v_dtype or w.v_dtype
+        self.cu = inputs.get("cu_seqlens")
+        self.cu_np = None if self.cu is None else self.cu.numpy()
+
+    # ---------------------------------------------------------------- GPU side
+    def run_gpu(self, return_lse: bool = False, sm_scale=None):
+        w, dev = self.w, "cuda"
+        q, k, v = (self.inp[x].to(dev) for x in ("q", "k", "v"))
+        if w.varlen:
+            cu = self.cu.to(dev)
+            ms = self.inp["max_seqlen"]
+            qk = sage.sage_quant_qk(q, k, qk_quant_gran=w.gran, smooth_k=w.smooth_k, cu_seqlens_q=cu,
+                                    cu_seqlens_k=cu, max_seqlen_q=ms, max_seqlen_k=ms)
+            qv = sage.sage_quant_v(v, v_dtype=self.v_dtype, smooth_v=w.smooth_v, cu_seqlens_k=cu, max_seqlen_k=ms)
+            res = sage.sage_attn_varlen_fwd(qk, qv, cu, cu, q.shape[0], is_causal=w.causal, sm_scale=sm_scale,
+                                            return_lse=return_lse, pv_accum_dtype=w.pv_accum)
+        else:
+            qk = sage.sage_quant_qk(q, k, tensor_layout=w.layout, qk_quant_gran=w.gran, smooth_k=w.smooth_k)
+            qv = sage.sage_quant_v(v, tensor_layout=w.layout, v_dtype=self.v_dtype, smooth_v=w.smooth_v)
+            res = sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, is_causal=w.causal, sm_scale=sm_scale,
+                                     return_lse=return_lse, pv_accum_dtype=w.pv_accum)
+        out, lse = (res if return_lse else (res, None))
+        torch.cuda.synchronize()
+        self.qk, self.qv = qk, qv
+        self.gpu_out = out.float().cpu().numpy()
+        self.gpu_lse = None if lse is None else lse.cpu().numpy()
+        return self
+
+    # ------------------------------------------------------------- oracle side
+    def run_oracle(self, rows=None, attention: bool = True, sm_scale=None, exact: bool = False):
+        w = self.w
+        q, k, v = (self.inp[x].float().numpy() for x in ("q", "k", "v"))
+        kw = dict(layout=w.layout, causal=w.causal, sm_scale=sm_scale, cu_seqlens_q=self.cu_np,
+                  cu_seqlens_k=self.cu_np, rows=rows)
+        self.ref = oracle.reference_forward(q, k, v, dtype=w.dtype, gran=w.gran, v_dtype=self.v_dtype,
+                                            smooth_k=w.smooth_k, smooth_v=w.smooth_v, attention=attention, **kw)
+        self.exact = oracle.exact_forward(q, k, v, **kw) if exact else None
+        return self
+
+    # ------------------------------------------------------------- comparisons
+    def gpu_rows(self, b: int, rows: np.ndarray) -> np.ndarray:
+        """GPU output [Hq, nrows, d] of sequence b at the given rows."""
+        o = self.gpu_out
+        if self.w.varlen:
+            return o[self.cu_np[b] + rows].transpose(1, 0, 2)
+        if self.w.layout == "HND":
+            return o[b][:, rows]
+        return o[b][rows].transpose(1, 0, 2)
+
+    def gpu_lse_rows(self, b: int, rows: np.ndarray) -> np.ndarray:
+        if self.w.varlen:
+            return self.gpu_lse[:, self.cu_np[b] + rows]
+        return self.gpu_lse[b][:, rows]
+
+    def n_seq(self):
+        return len(self.ref["q8"])
+
+    def check_quantized_bitexact(self):
+        w = self.w
+        gq, gk = oracle.Q_GROUP[w.gran], oracle.K_GROUP[w.gran]
+        q8 = self.qk.q8.cpu().numpy()
+        qs = self.qk.q_scale.cpu().numpy()
+        k8 = self.qk.k8.cpu().numpy()
+        ks = self.qk.k_scale.cpu().numpy()
+        km = None if self.qk.k_mean is None else self.qk.k_mean.cpu().numpy()
+        vt = self.qv.vt.cpu()
+        vt = (vt.numpy() if self.v_dtype == "fp8" else vt.float().numpy())
+        vs = None if self.qv.v_scale is None else self.qv.v_scale.cpu().numpy()
+        vm = None if self.qv.v_mean is None else self.qv.v_mean.cpu().numpy()
+        for b in range(self.n_seq()):
+            nq = self.ref["q8"][b].shape[1]
+            nk = self.ref["k8"][b].shape[1]
+            np.testing.assert_array_equal(q8[b][:, :nq], self.ref["q8"][b], err_msg=f"q8 seq {b}")
+            assert not q8[b][:, nq:].any(), "padding rows of q8 must be zero"
+            ngq = -(-nq // gq)
+            np.testing.assert_array_equal(qs[b][:, :ngq], self.ref["q_scale"][b], err_msg=f"q_scale seq {b}")
+            np.testing.assert_array_equal(k8[b][:, :nk], self.ref["k8"][b], err_msg=f"k8 seq {b}")
+            assert not k8[b][:, nk:].any()
+            ngk = -(-nk // gk)
+            np.testing.assert_array_equal(ks[b][:, :ngk], self.ref["k_scale"][b], err_msg=f"k_scale seq {b}")
+            if w.smooth_k:
+                np.testing.assert_array_equal(km[b], self.ref["k_mean"][b], err_msg=f"k_mean seq {b}")
+            vb = v_unpermute(vt[b], vt.shape[-1])
+            if self.v_dtype == "fp8":
+                np.testing.assert_array_equal(vb[:, :nk], self.ref["v8"][b], err_msg=f"v8 seq {b}")
+                np.testing.assert_array_equal(vs[b], self.ref["v_scale"][b], err_msg=f"v_scale seq {b}")
+            else:
+                np.testing.assert_array_equal(vb[:, :nk], self.ref["v16"][b], err_msg=f"v16 seq {b}")
+            assert not vb[:, nk:].any(), "padding keys of V must be zero"
+            if w.smooth_v:
+                np.testing.assert_array_equal(vm[b], self.ref["v_mean"][b], err_msg=f"v_mean seq {b}")
+
+    def check_outputs(self, lse: bool = False):
+        worst = 0.0
+        gs, rs, es = [], [], []
+        for b in range(self.n_seq()):
+            rows = self.ref["rows"][b]
+            g = self.gpu_rows(b, rows)
+            r = self.ref["out"][b]
+            tol = ABS_TOL + out_ulp(r, self.w.dtype)
+            err = np.abs(g - r)
+            bad = err > tol
+            assert not bad.any(), (f"seq {b}: {bad.sum()} outputs out of tolerance, max err "
+                                   f"{err.max():.3g} at {np.unravel_index(err.argmax(), err.shape)}")
+            worst = max(worst, float((err - ABS_TOL).max()))
+            gs.append(g.ravel()); rs.append(r.ravel())
+            if self.exact is not None:
+                es.append(self.exact["out"][b].ravel())
+            if lse:
+                gl = self.gpu_lse_rows(b, rows)
+                assert np.max(np.abs(gl - self.ref["lse"][b])) <= LSE_TOL_EMU
+                if self.exact is not None:
+                    assert np.max(np.abs(gl - self.exact["lse"][b])) <= LSE_TOL_EXACT
+        g, r = np.concatenate(gs), np.concatenate(rs)
+        c_emu = cosine(g, r)
+        assert c_emu >= COS_EMU, c_emu
+        c_ex = None
+        if es:
+            c_ex = cosine(g, np.concatenate(es))
+            assert c_ex >= COS_EXACT, c_ex
+        return c_emu, c_ex
+
+
+def scale_down(name: str, **kw) -> dict:
+    return workloads.make_inputs(workloads.WORKLOADS[name], scale_down=kw or None)

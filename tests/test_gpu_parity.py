@@ -1,0 +1,254 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Bit-exact: INT8 Q/K codes, their scales, K/V means, FP8 V codes and scales,
+and the int32 QK^T scores.  Within tolerance: outputs and LSE (see
+parity_utils).  Every case prints its name, shape and seed first, so that a
+failing GPU step can be identified from its last line of output.
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import quantized_attention_smooth_amd as sage
+from parity_utils import Case, cosine, sample_rows, scale_down
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------ tiny workload, everything
+def test_tiny_workload_full():
+    inp = workloads.make_inputs(workloads.WORKLOADS["tiny"])
+    _announce("tiny B1 H2 N256 d64 fp16 per_thread FP16-V seed 1")
+    c = Case(inp["workload"], inp).run_gpu(return_lse=True).run_oracle(exact=True)
+    c.check_quantized_bitexact()
+    c.check_outputs(lse=True)
+    # full int32 score dump against the oracle's exact integer scores
+    S = sage.sage_debug_qk_scores(c.qk).cpu().numpy()
+    ref = oracle.reference_forward(*(inp[x].float().numpy() for x in ("q", "k", "v")), dtype="fp16",
+                                   gran="per_thread", v_dtype="fp16", want_scores=True)
+    for h in range(2):
+        np.testing.assert_array_equal(S[0, h], ref["scores"][0][h])
+
+
+# ------------------------------------------------------------------ full-size workloads
+BIG = ["b2h8n4096d128", "gqa_prefill_n8192", "video_dit_n17550", "varlen16_h16"]
+
+
+@pytest.fixture(scope="module")
+def big_cases():
+    return {}
+
+
+def _big(name, cache):
+    if name not in cache:
+        w = workloads.WORKLOADS[name]
+        _announce(f"workload {name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} N{w.Nq} d{w.d} {w.dtype} {w.layout} "
+                  f"causal={w.causal} {w.gran} V={w.v_dtype} seed {w.seed}")
+        inp = workloads.make_inputs(w)
+        cache[name] = Case(w, inp).run_gpu(return_lse=w.return_lse)
+    return cache[name]
+
+
+@pytest.mark.parametrize("name", BIG)
+def test_workload_quantization_bitexact(name, big_cases):
+    c = _big(name, big_cases)
+    c.run_oracle(attention=False)
+    c.check_quantized_bitexact()
+
+
+@pytest.mark.parametrize("name", ["b2h8n4096d128", "gqa_prefill_n8192", "video_dit_n17550"])
+def test_workload_score_checksums(name, big_cases):
+    """Row checksums sum_j S_ij and sum_j (j+1) S_ij of the kernel's int32
+    scores against the oracle's integer codes (an fp64 GEMM of INT8 codes is
+    exact here: |S| < 2^22)."""
+    c = _big(name, big_cases)
+    if not hasattr(c, "ref"):
+        c.run_oracle(attention=False)
+    got = sage.sage_debug_qk_scores(c.qk, checksums=True).cpu().numpy().view(np.uint64)
+    w = c.w
+    grp = w.Hq // w.Hkv
+    rows = sample_rows(w.seed, 48)(0, w.Nq)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            q8 = c.ref["q8"][b][h][rows].astype(np.float64)
+            k8 = c.ref["k8"][b][h // grp].astype(np.float64)
+            S = (q8 @ k8.T).astype(np.int64)
+            s1 = S.sum(axis=1).astype(np.uint64)
+            s2 = (S * (np.arange(k8.shape[0], dtype=np.int64) + 1)[None, :]).sum(axis=1).astype(np.uint64)
+            np.testing.assert_array_equal(got[b, h, rows, 0], s1)
+            np.testing.assert_array_equal(got[b, h, rows, 1], s2)
+
+
+@pytest.mark.parametrize("name", BIG)
+def test_workload_outputs(name, big_cases):
+    c = _big(name, big_cases)
+    w = c.w
+    c.run_oracle(rows=sample_rows(w.seed, 24 if w.Hq * w.B > 64 else 48), exact=True)
+    c_emu, c_ex = c.check_outputs(lse=w.return_lse)
+    _announce(f"{name}: cos vs oracle {c_emu:.6f}, vs exact fp64 {c_ex:.6f}")
+
+
+# ------------------------------------------------------------------ edge-case matrix
+SMALL = [
+    # (Nq, Nk, d): ragged tails, Nq != Nk, padded head dims
+    (200, 200, 128),
+    (130, 300, 64),
+    (300, 70, 40),
+    (65, 129, 96),
+    (1, 1, 16),
+]
+
+
+@pytest.mark.parametrize("gran", ["per_block", "per_warp", "per_thread"])
+@pytest.mark.parametrize("v_dtype", ["fp8", "fp16"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("shape", SMALL)
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_small_matrix(gran, v_dtype, causal, shape, dtype):
+    nq, nk, d = shape
+    seed = 100 + nq + nk + d
+    _announce(f"small {dtype} Nq{nq} Nk{nk} d{d} {gran} V={v_dtype} causal={causal} seed {seed}")
+    base = workloads.WORKLOADS["b2h8n4096d128"]
+    w = dataclasses.replace(base, B=2, Hq=4, Hkv=2, Nq=nq, Nk=nk, d=d, dtype=dtype, gran=gran,
+                                      v_dtype=v_dtype, causal=causal, smooth_v=(v_dtype == "fp8"), seed=seed,
+                                      k_bias_std=1.0, v_bias_std=0.5)
+    inp = workloads.make_inputs(w)
+    c = Case(w, inp).run_gpu(return_lse=True).run_oracle(exact=True)
+    c.check_quantized_bitexact()
+    c.check_outputs(lse=True)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_small_matches_oracle(causal):
+    base = workloads.WORKLOADS["varlen16_h16"]
+    w = dataclasses.replace(base, B=5, Hq=4, Hkv=2, len_lo=1, len_hi=300, causal=causal, seed=77)
+    _announce(f"varlen small causal={causal} seed 77")
+    inp = workloads.make_inputs(w)
+    c = Case(w, inp).run_gpu(return_lse=True).run_oracle(exact=True)
+    c.check_quantized_bitexact()
+    c.check_outputs(lse=True)
+
+
+# ------------------------------------------------------------------ structural invariants (bit-exact)
+def _run(q, k, v, **kw):
+    out = sage.sageattn(q, k, v, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def test_hnd_equals_nhd():
+    _announce("HND == NHD")
+    g = torch.Generator().manual_seed(5)
+    q, k, v = (torch.randn(2, 3, 333, 128, generator=g).half().cuda() for _ in range(3))
+    a = _run(q, k, v, tensor_layout="HND", is_causal=True, qk_quant_gran="per_thread")
+    b = _run(q.transpose(1, 2).contiguous(), k.transpose(1, 2).contiguous(), v.transpose(1, 2).contiguous(),
+             tensor_layout="NHD", is_causal=True, qk_quant_gran="per_thread")
+    assert torch.equal(a, b.transpose(1, 2))
+    # non-contiguous NHD views of the HND tensors give the same result too
+    c = _run(q.transpose(1, 2), k.transpose(1, 2), v.transpose(1, 2), tensor_layout="NHD", is_causal=True,
+             qk_quant_gran="per_thread")
+    assert torch.equal(a, c.transpose(1, 2))
+
+
+def test_gqa_equals_repeated_kv():
+    _announce("GQA == repeat_interleave")
+    g = torch.Generator().manual_seed(6)
+    q = torch.randn(1, 8, 300, 64, generator=g).bfloat16().cuda()
+    k = torch.randn(1, 2, 300, 64, generator=g).bfloat16().cuda()
+    v = torch.randn(1, 2, 300, 64, generator=g).bfloat16().cuda()
+    a, la = _run(q, k, v, return_lse=True)
+    b, lb = _run(q, k.repeat_interleave(4, dim=1), v.repeat_interleave(4, dim=1), return_lse=True)
+    assert torch.equal(a, b) and torch.equal(la, lb)
+
+
+def test_head_dim_padding_equals_explicit_zero_pad():
+    _announce("d=96 == zero-padded 128")
+    g = torch.Generator().manual_seed(7)
+    q, k, v = (torch.randn(1, 2, 257, 96, generator=g).half().cuda() for _ in range(3))
+    a = _run(q, k, v)
+    pad = lambda x: torch.nn.functional.pad(x, (0, 32))
+    b = _run(pad(q), pad(k), pad(v), sm_scale=1 / math.sqrt(96))
+    assert torch.equal(a, b[..., :96])
+    assert not b[..., 96:].any()
+
+
+def test_varlen_equals_per_sequence_dense():
+    _announce("varlen == per-sequence dense")
+    g = torch.Generator().manual_seed(8)
+    lens = [1, 77, 128, 300, 64]
+    cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int32)
+    T = int(cu[-1])
+    q, k, v = (torch.randn(T, 4, 128, generator=g).half().cuda() for _ in range(3))
+    out, lse = sage.sageattn_varlen(q, k, v, cu.cuda(), cu.cuda(), max(lens), max(lens), is_causal=True,
+                                    return_lse=True, smooth_v=True)
+    for b, n in enumerate(lens):
+        s, e = int(cu[b]), int(cu[b + 1])
+        qb, kb, vb = (x[s:e].transpose(0, 1).unsqueeze(0).contiguous() for x in (q, k, v))
+        ob, lb = _run(qb, kb, vb, is_causal=True, return_lse=True, smooth_v=True)
+        assert torch.equal(out[s:e], ob[0].transpose(0, 1)), b
+        assert torch.equal(lse[:, s:e], lb[0]), b
+
+
+def test_deterministic():
+    _announce("run-to-run determinism")
+    g = torch.Generator().manual_seed(9)
+    q, k, v = (torch.randn(2, 4, 1000, 128, generator=g).half().cuda() for _ in range(3))
+    a = _run(q, k, v, qk_quant_gran="per_warp", smooth_v=True)
+    for _ in range(3):
+        assert torch.equal(a, _run(q, k, v, qk_quant_gran="per_warp", smooth_v=True))
+
+
+# ------------------------------------------------------------------ degenerate inputs
+def test_all_zero_k_gives_uniform_attention():
+    """K = 0 makes every score 0: the output is the mean of V over visible keys."""
+    _announce("all-zero K")
+    g = torch.Generator().manual_seed(10)
+    q = torch.randn(1, 2, 150, 64, generator=g).half().cuda()
+    k = torch.zeros(1, 2, 150, 64).half().cuda()
+    v = torch.randn(1, 2, 150, 64, generator=g).half().cuda()
+    out = _run(q, k, v, v_dtype="fp16").float().cpu()
+    ref = v.float().cpu().mean(dim=2, keepdim=True).expand_as(out)
+    assert torch.max(torch.abs(out - ref)) < 2e-3
+    outc = _run(q, k, v, v_dtype="fp16", is_causal=True).float().cpu()
+    refc = v.float().cpu().cumsum(dim=2) / torch.arange(1, 151).view(1, 1, 150, 1)
+    assert torch.max(torch.abs(outc - refc)) < 2e-3
+
+
+def test_single_key_returns_its_value():
+    _announce("one key")
+    g = torch.Generator().manual_seed(11)
+    q = torch.randn(1, 1, 70, 32, generator=g).half().cuda()
+    k = torch.randn(1, 1, 1, 32, generator=g).half().cuda()
+    v = torch.randn(1, 1, 1, 32, generator=g).half().cuda()
+    out = _run(q, k, v, v_dtype="fp16")
+    assert torch.equal(out, v.expand(1, 1, 70, 32))
+
+
+def test_page_shape_examples():
+    """The shape/dtype examples the pages print (tests/golden/page_shapes.txt)."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "page_shapes.txt")
+    for line in open(path):
+        if line.startswith("#") or not line.strip():
+            continue
+        src, shape, layout, causal, dtype, out_shape = [t.strip() for t in line.split("|")]
+        shape = tuple(int(x) for x in shape.split(","))
+        _announce(f"page example {shape} {layout} causal={causal}")
+        g = torch.Generator().manual_seed(42)
+        q, k, v = (torch.randn(*shape, generator=g).half().cuda() for _ in range(3))
+        out = _run(q, k, v, tensor_layout=layout, is_causal=bool(int(causal)))
+        assert tuple(out.shape) == tuple(int(x) for x in out_shape.split(",")), src
+        assert out.dtype == torch.float16
+        # loose sanity bound from the AMD page's test (mean abs diff vs SDPA around 1e-2)
+        ref = torch.nn.functional.scaled_dot_product_attention(q.float(), k.float(), v.float(),
+                                                               is_causal=bool(int(causal)))
+        assert (out.float() - ref).abs().mean().item() < 1e-2
