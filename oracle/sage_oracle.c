@@ -64,10 +64,10 @@ static double e4m3_value(double x) {               /* x already in [-448, 448] *
 }
 
 /* Code byte of an E4M3FN value v that is exactly representable.  The sign bit
- * is set for strictly negative inputs (a negative value that rounds to zero
- * keeps its sign; -0.0 itself encodes as 0x00).                              */
+ * is the sign bit of the input, as for any IEEE-style conversion: negative
+ * values that round to zero, and -0.0 itself, encode as 0x80.                */
 static uint8_t e4m3_code_of(double x_before_rounding, double v) {
-    uint8_t sign = x_before_rounding < 0 ? 0x80 : 0x00;
+    uint8_t sign = signbit(x_before_rounding) ? 0x80 : 0x00;
     double av = fabs(v);
     if (av == 0.0) return sign;
     int e2;
@@ -189,22 +189,25 @@ void oracle_quant_v_fp8(const float* v, int n, int dp, uint8_t* codes, float* sc
  * following the method's steps in order:
  *   scores  S_ij = sum_c q8_ic k8_jc in exact integer arithmetic
  *           ([guide] sec. 1: QK^T by 8-bit integer multiplication);
- *   dequant s_ij = fl32(S_ij * f_ij), f_ij = fl32(c_i * kscale_j),
- *           c_i = fl32(fl32(qscale_i * sm_scale) * log2(e))  (log2 domain);
+ *   dequant f_ij = fl32(c_i * kscale_j), c_i = fl32(fl32(qscale_i * sm_scale)
+ *           * log2(e)), s_ij = fl32(S_ij * f_ij)  (log2 domain);
  *   online softmax over key tiles of `bk` keys in ascending order
  *           ([amd-9070] sec. 2: blockwise like FlashAttention): the reference
  *           maximum m moves to the tile maximum when that exceeds m + tau
  *           (tau = 0 is the textbook update), and the running sums are
  *           rescaled by 2^(m_old - m_new);
- *   P       p_ij = fl32(2^(s_ij - m)); on the FP8 path the product operand is
- *           E4M3FN(fl32(min(p, 2^tau) * 448 / 2^tau)), on the FP16 path it is
- *           p rounded to fp16 (bf16 for bf16 inputs) ([guide] sec. 1: V in
- *           FP8 or FP16);
+ *   P       the exponent is formed in fp32 as x_ij = fl32(S_ij f_ij + nb_i)
+ *           with one rounding (a fused multiply-add), nb_i = fl32(L - m_i);
+ *           p_ij = fl32(2^x_ij).  On the FP8 path L = fl32(log2 448) - tau,
+ *           so p already carries P's static scale 448 / 2^tau, and the P.V
+ *           operand is E4M3FN(min(p, 448)); on the FP16 path L = 0 and the
+ *           operand is p rounded to fp16 (bf16 for bf16 inputs) ([guide]
+ *           sec. 1: V in FP8 or FP16);
  *   sums    l = sum_j p_ij (unquantized), acc_c = sum_j P_ij * V_jc, both fp64;
- *   output  out_ic = acc_c * vscale_c / (P_scale * l) + vmean_c (FP8 path) or
- *           acc_c / l + vmean_c (FP16 path) ([guide] sec. 4.2: smooth_v adds
- *           back the mean that was subtracted);
- *   lse     (m + log2 l) ln 2, plus sm_scale * sum_c q8_ic qscale_i kmean_c
+ *   output  out_ic = acc_c * vscale_c / l + vmean_c (FP8 path; P's scale
+ *           cancels between acc and l) or acc_c / l + vmean_c (FP16 path)
+ *           ([guide] sec. 4.2: smooth_v adds back the mean it subtracted);
+ *   lse     (m - L + log2 l) ln 2, plus sm_scale * sum_c q8_ic qscale_i kmean_c
  *           when K was smoothed, so that it is the log-sum-exp of the
  *           unsmoothed scores ([guide] sec. 4.1: return_lse).
  *
@@ -212,13 +215,25 @@ void oracle_quant_v_fp8(const float* v, int n, int dp, uint8_t* codes, float* sc
  * shift is 0); keys j >= nk do not exist.  Tiles with no visible key are
  * skipped.
  *
+ * Rounding fragility: 2^x is evaluated here to the correctly rounded fp32
+ * value; an implementation whose exp2 is accurate to 1 ulp may return a p up
+ * to 2 ulps away, and that can move P across an FP8/fp16 rounding midpoint.
+ * For every P whose code would change within p (1 -+ 2^-22), `allow` (if not
+ * NULL) accumulates |code change| * |V| (rescaled like acc and normalised like
+ * out), an upper bound on what such a flip can move each output.
+ *
  * q8: nq x dp; qscale: nq (per row, expanded from its group); k8: nk x dp;
  * kscale: nk (per key, expanded); vval: nk x dp values of the PV operand
  * (decoded E4M3 codes on the FP8 path, fp16/bf16 values on the FP16 path);
  * vscale: dp (FP8 path) or NULL; vmean, kmean: dp or NULL.
  * p_mode: 0 FP8, 1 fp16, 2 bf16.
  * rows: nrows query indices to compute; out: nrows x dp; lse: nrows or NULL;
- * sdump: nrows x nk int32 scores or NULL.                                    */
+ * sdump: nrows x nk int32 scores or NULL; allow: nrows x dp or NULL.         */
+static double p_operand(double p, int p_mode) {
+    if (p_mode == 0) return e4m3_value(p < E4M3_MAX ? p : E4M3_MAX);
+    return fmt_rne(p, p_mode == 2 ? 7 : 10, p_mode == 2 ? -126 : -14);
+}
+
 int oracle_attn_rows(int nq, int nk, int dp,
                      const int8_t* q8, const float* qscale,
                      const int8_t* k8, const float* kscale,
@@ -226,18 +241,20 @@ int oracle_attn_rows(int nq, int nk, int dp,
                      const float* kmean, float sm_scale, int causal, int causal_shift,
                      int bk, int tau, int p_mode,
                      int nrows, const int32_t* rows,
-                     double* out, double* lse, int32_t* sdump) {
+                     double* out, double* lse, int32_t* sdump, double* allow) {
     if (bk <= 0 || dp <= 0 || nk <= 0) return -1;
     const float LOG2E = 1.4426950408889634f;
-    const double p_scale = E4M3_MAX / ldexp(1.0, tau);
+    const float L = p_mode == 0 ? (float)log2(E4M3_MAX) - (float)tau : 0.0f;
     int err = 0;
 #pragma omp parallel for schedule(dynamic, 4)
     for (int ri = 0; ri < nrows; ++ri) {
         int i = rows[ri];
         if (i < 0 || i >= nq) { err = -2; continue; }
         int32_t* S = (int32_t*)malloc(sizeof(int32_t) * (size_t)nk);
+        float* f = (float*)malloc(sizeof(float) * (size_t)nk);
         float* s = (float*)malloc(sizeof(float) * (size_t)nk);
         double* acc = (double*)calloc((size_t)dp, sizeof(double));
+        double* alw = (double*)calloc((size_t)dp, sizeof(double));
         const int8_t* qi = q8 + (size_t)i * dp;
         for (int j = 0; j < nk; ++j) {
             int64_t dot = 0;
@@ -249,8 +266,9 @@ int oracle_attn_rows(int nq, int nk, int dp,
         volatile float ci = qscale[i] * sm_scale;
         volatile float ci2 = ci * LOG2E;
         for (int j = 0; j < nk; ++j) {
-            volatile float f = ci2 * kscale[j];
-            volatile float sj = (float)S[j] * f;
+            volatile float fj = ci2 * kscale[j];
+            volatile float sj = (float)S[j] * fj;
+            f[j] = fj;
             s[j] = sj;
         }
         int last = nk - 1;
@@ -269,32 +287,32 @@ int oracle_attn_rows(int nq, int nk, int dp,
                 if (m != -INFINITY) {
                     float alpha = (float)exp2((double)m - (double)mt);
                     l *= alpha;
-                    for (int c = 0; c < dp; ++c) acc[c] *= alpha;
+                    for (int c = 0; c < dp; ++c) { acc[c] *= alpha; alw[c] *= alpha; }
                 }
                 m = mt;
             }
+            volatile float nb = L - m;
             for (int j = t0; j <= t1; ++j) {
-                float p = (float)exp2((double)s[j] - (double)m);
+                float x = fmaf((float)S[j], f[j], nb);      /* one rounding */
+                float p = (float)exp2((double)x);
                 l += p;
-                double pq;
-                if (p_mode == 0) {
-                    double cap = ldexp(1.0, tau);
-                    double pc = p < cap ? p : cap;
-                    volatile float scaled = (float)(pc * p_scale);
-                    pq = e4m3_value(scaled);
-                } else {
-                    pq = fmt_rne(p, p_mode == 2 ? 7 : 10, p_mode == 2 ? -126 : -14);
-                }
+                double pq = p_operand(p, p_mode);
+                double lo = p_operand((double)p * (1.0 - 0x1p-22), p_mode);
+                double hi = p_operand((double)p * (1.0 + 0x1p-22), p_mode);
+                double flip = fabs(hi - lo);
                 const float* vj = vval + (size_t)j * dp;
-                for (int c = 0; c < dp; ++c) acc[c] += pq * (double)vj[c];
+                for (int c = 0; c < dp; ++c) {
+                    acc[c] += pq * (double)vj[c];
+                    if (flip > 0.0) alw[c] += flip * fabs((double)vj[c]);
+                }
             }
         }
         for (int c = 0; c < dp; ++c) {
-            double o;
-            if (p_mode == 0) o = acc[c] * (double)vscale[c] / (p_scale * l);
-            else o = acc[c] / l;
+            double sc = p_mode == 0 ? (double)vscale[c] / l : 1.0 / l;
+            double o = acc[c] * sc;
             if (vmean) o += vmean[c];
             out[(size_t)ri * dp + c] = o;
+            if (allow) allow[(size_t)ri * dp + c] = alw[c] * sc;
         }
         if (lse) {
             double corr = 0.0;
@@ -302,9 +320,9 @@ int oracle_attn_rows(int nq, int nk, int dp,
                 for (int c = 0; c < dp; ++c) corr += (double)qi[c] * (double)qscale[i] * (double)kmean[c];
                 corr *= (double)sm_scale;
             }
-            lse[ri] = ((double)m + log2(l)) * M_LN2 + corr;
+            lse[ri] = ((double)m - (double)L + log2(l)) * M_LN2 + corr;
         }
-        free(S); free(s); free(acc);
+        free(S); free(f); free(s); free(acc); free(alw);
     }
     return err;
 }

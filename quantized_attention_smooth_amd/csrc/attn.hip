@@ -223,18 +223,20 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
                     for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
             }
-            // ---- P = 2^(s - m) (times 448 on the FP8 path)
+            // ---- P = 2^(s - m) (times 448 on the FP8 path).  The exponent is
+            // fl32(S * f + fl32(L - m)) with a single rounding: S is recovered
+            // exactly from the biased accumulator (both terms lie in
+            // [2^23, 2^24)), so the only inexact step after it is the FMA.
             const float m_use = (m_ref == -INFINITY) ? 0.f : m_ref;
-            float nb[4];
-#pragma unroll
-            for (int g = 0; g < 4; ++g) nb[g] = p_log2_scale - (kAccBias * f[g] + m_use);
+            const float nb = p_log2_scale - m_use;
             float p[2][16];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int g = 2 * kb + (i >> 3);
-                    p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(bits_f(acc[kb][i]), f[g], nb[g]));
+                    const float sf = bits_f(acc[kb][i]) - kAccBias;
+                    p[kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sf, f[g], nb));
                     lsum += p[kb][i];
                 }
             const uint8_t* vs = stage + C::KT_BYTES;

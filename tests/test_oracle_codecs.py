@@ -23,10 +23,9 @@ def test_e4m3_encode_exhaustive_over_fp16():
     xc = np.clip(x, -448.0, 448.0).astype(np.float32)
     ours = oracle.e4m3_encode(xc)
     ref = torch.from_numpy(xc).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    # -0.0 encodes as +0 (both decode to zero); everything else must agree bit for bit
-    neg_zero = (xc == 0) & np.signbit(xc)
-    assert np.array_equal(ours[~neg_zero], ref[~neg_zero])
-    assert np.all(ours[neg_zero] == 0)
+    # every code agrees bit for bit, including the sign of zero (-0.0 -> 0x80)
+    assert np.array_equal(ours, ref)
+    assert ours[np.nonzero((xc == 0) & np.signbit(xc))[0][0]] == 0x80
 
 
 def test_e4m3_encode_clamps_out_of_range():

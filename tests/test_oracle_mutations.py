@@ -16,16 +16,17 @@ PINS = ["tests/test_oracle_codecs.py", "tests/test_oracle_quant.py", "tests/test
 
 MUTATIONS = {
     "online softmax: running sum not rescaled": ("l *= alpha;", ""),
-    "online softmax: accumulator not rescaled": ("for (int c = 0; c < dp; ++c) acc[c] *= alpha;", ""),
-    "dequant: wrong key-group scale": ("volatile float f = ci2 * kscale[j];",
-                                       "volatile float f = ci2 * kscale[j + 1 < nk ? j + 1 : j];"),
-    "P scale 256 instead of 448": ("const double p_scale = E4M3_MAX / ldexp(1.0, tau);",
-                                   "const double p_scale = 256.0 / ldexp(1.0, tau);"),
-    "lse: smoothing correction sign": ("lse[ri] = ((double)m + log2(l)) * M_LN2 + corr;",
-                                       "lse[ri] = ((double)m + log2(l)) * M_LN2 - corr;"),
+    "online softmax: accumulator not rescaled": ("{ acc[c] *= alpha; alw[c] *= alpha; }", "{ alw[c] *= alpha; }"),
+    "dequant: wrong key-group scale": ("volatile float fj = ci2 * kscale[j];",
+                                       "volatile float fj = ci2 * kscale[j + 1 < nk ? j + 1 : j];"),
+    "P scale 256 instead of 448": ("const float L = p_mode == 0 ? (float)log2(E4M3_MAX) - (float)tau : 0.0f;",
+                                   "const float L = p_mode == 0 ? (float)log2(256.0) - (float)tau : 0.0f;"),
+    "lse: smoothing correction sign": ("lse[ri] = ((double)m - (double)L + log2(l)) * M_LN2 + corr;",
+                                       "lse[ri] = ((double)m - (double)L + log2(l)) * M_LN2 - corr;"),
     "causal: diagonal masked": ("long lim = (long)i + causal_shift;\n            if (lim < last) last = (int)lim;\n        }\n        float m",
                                 "long lim = (long)i + causal_shift - 1;\n            if (lim < last) last = (int)lim;\n        }\n        float m"),
-    "epilogue: V scale dropped": ("o = acc[c] * (double)vscale[c] / (p_scale * l);", "o = acc[c] / (p_scale * l);"),
+    "epilogue: V scale dropped": ("double sc = p_mode == 0 ? (double)vscale[c] / l : 1.0 / l;",
+                                  "double sc = p_mode == 0 ? 1.0 / (448.0 * l) : 1.0 / l;"),
     "epilogue: V mean not added back": ("if (vmean) o += vmean[c];", ""),
     "INT8: truncation instead of rounding": ("float q = nearbyintf(t);", "float q = truncf(t);"),
     "INT8: scale amax/128": ("volatile float scale = amax / 127.0f;", "volatile float scale = amax / 128.0f;"),
