@@ -45,7 +45,7 @@ K_GROUP = {"per_block": 64, "per_warp": 64, "per_thread": 16}
 # key tile of the online softmax and the lazy-rescale threshold used by the
 # HIP kernel's schedule (see oracle_attn_rows in sage_oracle.c)
 DEFAULT_BK = 64
-DEFAULT_TAU = 0
+DEFAULT_TAU = 3
 
 
 def build(force: bool = False) -> str:
@@ -85,7 +85,7 @@ def lib():
         L.oracle_quant_v_fp8.argtypes = [P, i, i, P, P]
         L.oracle_quant_v_fp8.restype = None
         L.oracle_attn_rows.argtypes = [i, i, i, P, P, P, P, P, P, P, P, ctypes.c_float, i, i, i, i, i,
-                                       i, P, P, P, P, P]
+                                       i, P, P, P, P, P, P]
         L.oracle_attn_rows.restype = i
         L.oracle_attn_exact.argtypes = [i, i, i, P, P, P, ctypes.c_double, i, i, i, P, P, P]
         L.oracle_attn_exact.restype = i
@@ -202,7 +202,8 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
       rows[b], out[b] (Hq, nrows, d) float64, lse[b] (Hq, nrows), scores[b]
       (Hq, nrows, Nk_b) int32 if want_scores, allow[b] (Hq, nrows, d): bound on
       how far a 2-ulp difference in an exp2 evaluation can move each output
-      through P's rounding (see oracle_attn_rows).
+      through P's rounding (see oracle_attn_rows), lse_pq[b] (Hq, nrows): the
+      share of lse due to rounding P to its operand format.
     """
     varlen = cu_seqlens_q is not None
     if varlen and cu_seqlens_k is None:
@@ -221,7 +222,7 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
         raise ValueError("Hq must be divisible by Hkv")
     grp = hq // hkv
     res = {k_: [] for k_ in ("q8", "q_scale", "k8", "k_scale", "k_mean", "v8", "v16", "v_scale", "v_mean",
-                             "rows", "out", "lse", "scores", "allow")}
+                             "rows", "out", "lse", "scores", "allow", "lse_pq")}
     L = lib()
     for (b, qb), (_, kb), (_, vb) in zip(qp, kp, vp):
         nq, nk = qb.shape[1], kb.shape[1]
@@ -264,7 +265,7 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
             continue
         r = np.arange(nq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows(b, nq), dtype=np.int32)
         res["rows"].append(r)
-        outs, lses, scs, alws = [], [], [], []
+        outs, lses, scs, alws, lpqs = [], [], [], [], []
         p_mode = 0 if v_dtype == "fp8" else (2 if dtype == "bf16" else 1)
         for h in range(hq):
             hk = h // grp
@@ -274,18 +275,20 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
             ls = np.zeros(len(r), dtype=np.float64)
             sd = np.zeros((len(r), nk), dtype=np.int32) if want_scores else None
             al = np.zeros((len(r), dp), dtype=np.float64)
+            lpq = np.zeros(len(r), dtype=np.float64)
             vsc = vss[hk] if v_dtype == "fp8" else None
             rc = L.oracle_attn_rows(nq, nk, dp, _p(q8s[h]), _p(qs_row), _p(k8s[hk]), _p(ks_key),
                                     _p(np.ascontiguousarray(vvals[hk], dtype=np.float32)), _p(vsc),
                                     _p(vms[hk] if smooth_v else None), _p(kms[hk] if smooth_k else None),
                                     sm32, int(causal), 0, bk, tau, p_mode, len(r), _p(r), _p(o), _p(ls), _p(sd),
-                                    _p(al))
+                                    _p(al), _p(lpq))
             if rc != 0:
                 raise RuntimeError(f"oracle_attn_rows failed ({rc})")
-            outs.append(o[:, :d]); lses.append(ls); alws.append(al[:, :d])
+            outs.append(o[:, :d]); lses.append(ls); alws.append(al[:, :d]); lpqs.append(lpq)
             if want_scores:
                 scs.append(sd)
         res["out"].append(np.stack(outs)); res["lse"].append(np.stack(lses)); res["allow"].append(np.stack(alws))
+        res["lse_pq"].append(np.stack(lpqs))
         if want_scores:
             res["scores"].append(np.stack(scs))
     return res

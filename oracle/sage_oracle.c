@@ -196,14 +196,17 @@ void oracle_quant_v_fp8(const float* v, int n, int dp, uint8_t* codes, float* sc
  *           maximum m moves to the tile maximum when that exceeds m + tau
  *           (tau = 0 is the textbook update), and the running sums are
  *           rescaled by 2^(m_old - m_new);
- *   P       the exponent is formed in fp32 as x_ij = fl32(S_ij f_ij + nb_i)
- *           with one rounding (a fused multiply-add), nb_i = fl32(L - m_i);
+ *   P       the exponent is formed in fp32, in the order the GPU kernel uses:
+ *           with B = 1.5 * 2^23 (so that B + S_ij is exact in fp32),
+ *           c_ij = fl32(nb_i - B f_ij) and x_ij = fl32((B + S_ij) f_ij + c_ij),
+ *           each with one rounding (fused multiply-adds), nb_i = fl32(L - m_i);
  *           p_ij = fl32(2^x_ij).  On the FP8 path L = fl32(log2 448) - tau,
  *           so p already carries P's static scale 448 / 2^tau, and the P.V
- *           operand is E4M3FN(min(p, 448)); on the FP16 path L = 0 and the
- *           operand is p rounded to fp16 (bf16 for bf16 inputs) ([guide]
- *           sec. 1: V in FP8 or FP16);
- *   sums    l = sum_j p_ij (unquantized), acc_c = sum_j P_ij * V_jc, both fp64;
+ *           operand is P_ij = E4M3FN(min(p, 448)); on the FP16 path L = 0 and
+ *           P_ij is p rounded to fp16 (bf16 for bf16 inputs) ([guide] sec. 1:
+ *           V in FP8 or FP16);
+ *   sums    l = sum_j P_ij and acc_c = sum_j P_ij * V_jc, both over the same
+ *           rounded P and in fp64, so the weights P_ij / l sum to one;
  *   output  out_ic = acc_c * vscale_c / l + vmean_c (FP8 path; P's scale
  *           cancels between acc and l) or acc_c / l + vmean_c (FP16 path)
  *           ([guide] sec. 4.2: smooth_v adds back the mean it subtracted);
@@ -218,9 +221,10 @@ void oracle_quant_v_fp8(const float* v, int n, int dp, uint8_t* codes, float* sc
  * Rounding fragility: 2^x is evaluated here to the correctly rounded fp32
  * value; an implementation whose exp2 is accurate to 1 ulp may return a p up
  * to 2 ulps away, and that can move P across an FP8/fp16 rounding midpoint.
- * For every P whose code would change within p (1 -+ 2^-22), `allow` (if not
- * NULL) accumulates |code change| * |V| (rescaled like acc and normalised like
- * out), an upper bound on what such a flip can move each output.
+ * A change d of one P_ij moves out_i by d (V_jc - out_ic) / l, at most
+ * |d| (|V_jc| + max_k |V_kc|) / l.  For every P whose code would change within
+ * p (1 -+ 2^-22), `allow` (if not NULL) accumulates that bound (rescaled like
+ * acc and normalised like out).
  *
  * q8: nq x dp; qscale: nq (per row, expanded from its group); k8: nk x dp;
  * kscale: nk (per key, expanded); vval: nk x dp values of the PV operand
@@ -228,7 +232,9 @@ void oracle_quant_v_fp8(const float* v, int n, int dp, uint8_t* codes, float* sc
  * vscale: dp (FP8 path) or NULL; vmean, kmean: dp or NULL.
  * p_mode: 0 FP8, 1 fp16, 2 bf16.
  * rows: nrows query indices to compute; out: nrows x dp; lse: nrows or NULL;
- * sdump: nrows x nk int32 scores or NULL; allow: nrows x dp or NULL.         */
+ * sdump: nrows x nk int32 scores or NULL; allow: nrows x dp or NULL;
+ * lse_pq: nrows or NULL, the part of lse that comes from rounding P to its
+ * operand format: |ln(sum of rounded P) - ln(sum of unrounded P)|.          */
 static double p_operand(double p, int p_mode) {
     if (p_mode == 0) return e4m3_value(p < E4M3_MAX ? p : E4M3_MAX);
     return fmt_rne(p, p_mode == 2 ? 7 : 10, p_mode == 2 ? -126 : -14);
@@ -241,7 +247,7 @@ int oracle_attn_rows(int nq, int nk, int dp,
                      const float* kmean, float sm_scale, int causal, int causal_shift,
                      int bk, int tau, int p_mode,
                      int nrows, const int32_t* rows,
-                     double* out, double* lse, int32_t* sdump, double* allow) {
+                     double* out, double* lse, int32_t* sdump, double* allow, double* lse_pq) {
     if (bk <= 0 || dp <= 0 || nk <= 0) return -1;
     const float LOG2E = 1.4426950408889634f;
     const float L = p_mode == 0 ? (float)log2(E4M3_MAX) - (float)tau : 0.0f;
@@ -255,6 +261,7 @@ int oracle_attn_rows(int nq, int nk, int dp,
         float* s = (float*)malloc(sizeof(float) * (size_t)nk);
         double* acc = (double*)calloc((size_t)dp, sizeof(double));
         double* alw = (double*)calloc((size_t)dp, sizeof(double));
+        double* vmax = (double*)calloc((size_t)dp, sizeof(double));
         const int8_t* qi = q8 + (size_t)i * dp;
         for (int j = 0; j < nk; ++j) {
             int64_t dot = 0;
@@ -276,34 +283,46 @@ int oracle_attn_rows(int nq, int nk, int dp,
             long lim = (long)i + causal_shift;
             if (lim < last) last = (int)lim;
         }
+        /* largest |V| per channel, for the fragility bound */
+        for (int c = 0; c < dp; ++c) vmax[c] = 0.0;
+        for (int j = 0; j < nk; ++j)
+            for (int c = 0; c < dp; ++c) {
+                double a = fabs((double)vval[(size_t)j * dp + c]);
+                if (a > vmax[c]) vmax[c] = a;
+            }
         float m = -INFINITY;
-        double l = 0.0;
+        double l = 0.0, lu = 0.0;                          /* sums of rounded / unrounded P */
         for (int t0 = 0; t0 <= last; t0 += bk) {
             int t1 = t0 + bk - 1;
             if (t1 > last) t1 = last;
             float mt = -INFINITY;
             for (int j = t0; j <= t1; ++j) if (s[j] > mt) mt = s[j];
-            if (m == -INFINITY || (double)mt > (double)m + tau) {
+            volatile float thresh = m + (float)tau;     /* the decision is taken in fp32 */
+            if (m == -INFINITY || mt > thresh) {
                 if (m != -INFINITY) {
                     float alpha = (float)exp2((double)m - (double)mt);
                     l *= alpha;
+                    lu *= alpha;
                     for (int c = 0; c < dp; ++c) { acc[c] *= alpha; alw[c] *= alpha; }
                 }
                 m = mt;
             }
             volatile float nb = L - m;
+            const float B = 12582912.0f;                  /* 1.5 * 2^23 */
             for (int j = t0; j <= t1; ++j) {
-                float x = fmaf((float)S[j], f[j], nb);      /* one rounding */
+                float cj = fmaf(-B, f[j], nb);                   /* one rounding */
+                float x = fmaf(B + (float)S[j], f[j], cj);       /* B + S exact; one rounding */
                 float p = (float)exp2((double)x);
-                l += p;
                 double pq = p_operand(p, p_mode);
+                l += pq;
+                lu += (double)p;
                 double lo = p_operand((double)p * (1.0 - 0x1p-22), p_mode);
                 double hi = p_operand((double)p * (1.0 + 0x1p-22), p_mode);
                 double flip = fabs(hi - lo);
                 const float* vj = vval + (size_t)j * dp;
                 for (int c = 0; c < dp; ++c) {
                     acc[c] += pq * (double)vj[c];
-                    if (flip > 0.0) alw[c] += flip * fabs((double)vj[c]);
+                    if (flip > 0.0) alw[c] += flip * (fabs((double)vj[c]) + vmax[c]);
                 }
             }
         }
@@ -322,7 +341,8 @@ int oracle_attn_rows(int nq, int nk, int dp,
             }
             lse[ri] = ((double)m - (double)L + log2(l)) * M_LN2 + corr;
         }
-        free(S); free(f); free(s); free(acc); free(alw);
+        if (lse_pq) lse_pq[ri] = l > 0.0 ? fabs(log(l) - log(lu)) : 0.0;
+        free(S); free(f); free(s); free(acc); free(alw); free(vmax);
     }
     return err;
 }

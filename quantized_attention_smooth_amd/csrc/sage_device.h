@@ -50,13 +50,14 @@ __device__ __forceinline__ int v_perm_pos(int key64) {
     return (h << 5) | (b << 4) | (r << 2) | e;
 }
 
-// LDS 16-byte-chunk swizzles (bank-conflict-free ds_read_b128 over 32 rows).
-// K tile rows hold Dp bytes; V^T tile rows hold 64 keys (64 B for FP8,
-// 128 B for fp16/bf16).
+// LDS 16-byte-chunk swizzles for ds_read_b128 of 32 consecutive rows at one
+// logical chunk: rows that fall into the same 256-byte bank window must hit
+// different chunks.  K tile rows hold Dp bytes; V^T tile rows hold 64 keys
+// (64 B for FP8, 128 B for fp16/bf16).
 template <int ROW_BYTES>
 __device__ __forceinline__ int swz(int row, int chunk) {
-    if constexpr (ROW_BYTES >= 128) return chunk ^ (row & 7);
-    else return chunk ^ ((row >> 1) & 3);
+    if constexpr (ROW_BYTES >= 128) return chunk ^ ((row >> 1) & 7);
+    else return chunk ^ ((row >> 2) & 3);
 }
 
 __device__ __forceinline__ int xcd_remap(int bid, int nwg) {

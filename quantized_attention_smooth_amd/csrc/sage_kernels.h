@@ -7,10 +7,11 @@
 
 namespace sage {
 
-// Tile sizes.  One workgroup of 4 wavefronts covers kBQ query rows (32 per
-// wavefront: one MFMA column block); the key loop advances kBK keys per step,
-// which is also the online-softmax tile.  Quantized rows are padded to kPad.
-constexpr int kBQ = 128;
+// Tile sizes.  One attention workgroup of 4 wavefronts covers kBQ query rows
+// (64 per wavefront: two MFMA column blocks); the key loop advances kBK keys
+// per step, which is also the online-softmax tile.  Quantized rows are padded
+// to kPad.
+constexpr int kBQ = 256;
 constexpr int kBK = 64;
 constexpr int kPad = 128;
 constexpr int kThreads = 256;

@@ -241,7 +241,9 @@ class Case:
                 gl = self.gpu_lse_rows(b, rows)
                 assert np.max(np.abs(gl - self.ref["lse"][b])) <= LSE_TOL_EMU
                 if self.exact is not None and self.w.smooth_k:
-                    bound = self.lse_exact_bound(b, rows, sm) + 1e-3
+                    # score error of the INT8 Q/K, plus what rounding P to its
+                    # operand format moved the row sum, plus the emulation slack
+                    bound = self.lse_exact_bound(b, rows, sm) + self.ref["lse_pq"][b] + LSE_TOL_EMU + 1e-4
                     assert np.all(np.abs(gl - self.exact["lse"][b]) <= bound)
         g, r = np.concatenate(gs), np.concatenate(rs)
         c_emu = cosine(g, r)

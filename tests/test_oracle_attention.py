@@ -93,9 +93,11 @@ def _dequantized(r, b, h, hk, gran, v_dtype, dtype):
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp16_path_matches_exact_on_dequantized(gran, causal):
     """With P rounded to fp16 the emulation differs from exact attention on its
-    own dequantized operands only by that rounding: |P~ - p| <= 2^-11 p for
-    normal p plus 2^-25 absolute (fp16 subnormal half-step), so
-    |out - out_exact| <= 2^-11 max|v| + n_k 2^-25 max|v| / l with l >= 1."""
+    own dequantized operands only by that rounding: P = p (1 + d) with
+    |d| <= 2^-11 for normal p (plus 2^-25 absolute below the fp16 normal
+    range), and the weights P_j / sum P differ from p_j / sum p by at most a
+    factor (1 +- 2^-11) / (1 -+ 2^-11), so
+    |out - out_exact| <= (2^-10 + n_k 2^-24) max|v| (l >= 1)."""
     rng = np.random.default_rng(21)
     nq, nk, d = 150, 200, 48
     q = _half((1, 3, nq, d), rng)
@@ -108,7 +110,7 @@ def test_fp16_path_matches_exact_on_dequantized(gran, causal):
         vfull = vh + vm[None, :]
         ex = oracle.exact_forward(qh[None, None], kh[None, None], vfull[None, None], causal=causal,
                                   sm_scale=1 / math.sqrt(d))
-        bound = (2.0 ** -11 + nk * 2.0 ** -25) * np.abs(vh).max() + 1e-6
+        bound = (2.0 ** -10 * (1 + 2.0 ** -10) + nk * 2.0 ** -24) * np.abs(vh).max() + 1e-6
         err = np.abs(r["out"][0][h] - ex["out"][0][0][:, :d]).max()
         assert err <= bound, (err, bound)
 
@@ -116,8 +118,8 @@ def test_fp16_path_matches_exact_on_dequantized(gran, causal):
 @pytest.mark.parametrize("tau", [0, 3])
 def test_fp8_single_tile_closed_form(tau):
     """One key tile: P8 = E4M3(fl32(p * 448 / 2^tau)) with p = 2^(s - max),
-    out = sum_j dec(P8_j) v_j vscale / (448/2^tau * sum_j p_j); the FP8 cast
-    here is torch's."""
+    out = sum_j dec(P8_j) v_j vscale / sum_j dec(P8_j); the FP8 cast here is
+    torch's."""
     rng = np.random.default_rng(22)
     nq, nk, d = 40, 100, 64
     q, k, v = _half((1, 1, nq, d), rng), _half((1, 1, nk, d), rng), _half((1, 1, nk, d), rng)
@@ -128,10 +130,14 @@ def test_fp8_single_tile_closed_form(tau):
     pscale = 448.0 / 2 ** tau
     scaled = (p.astype(np.float64) * pscale).astype(np.float32)
     p8 = torch.from_numpy(scaled).to(torch.float8_e4m3fn).to(torch.float64).numpy()
-    ref = (p8 @ vh) / (pscale * p.astype(np.float64).sum(axis=1, keepdims=True))
+    ref = (p8 @ vh) / p8.sum(axis=1, keepdims=True)
     diff = np.abs(r["out"][0][0] - ref)
-    # s is formed in fp32 by the oracle and in fp64 here: a rare P8 tie may flip
-    assert np.mean(diff > 1e-6) < 0.01
+    # the oracle forms the exponent in fp32 (within ~1e-4 of the fp64 value
+    # used here), so a few P8 codes per hundred rows sit on the other side of a
+    # rounding midpoint; every other row must agree to fp64 rounding
+    rows_off = np.mean(diff.max(axis=1) > 1e-6)
+    assert rows_off < 0.3, rows_off
+    assert np.median(diff) < 1e-9
     assert diff.max() < 2e-3
 
 
@@ -161,9 +167,10 @@ def test_fp8_schedule_without_max_updates_equals_single_tile():
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_path_within_bound_and_scores_exact(causal):
-    """E4M3 rounding of P (scaled to 448) has relative error <= 2^-4 for normal
-    values and absolute error <= 2^-10/448 below 2^-6/448, giving
-    |out - out_exact| <= (2^-4 + n_k 2^-10 / 448) max|v_hat|."""
+    """E4M3 rounding of P (scaled to 448 / 2^tau) has relative error <= 2^-4
+    for normal values and absolute error <= 2^-10 below 2^-6; normalising by
+    the sum of the rounded P gives
+    |out - out_exact| <= (2^-3 / (1 - 2^-4) + n_k 2^-9 2^tau / 448) max|v_hat|."""
     rng = np.random.default_rng(24)
     nq, nk, d = 130, 190, 128
     q, k, v = _half((2, 2, nq, d), rng), _half((2, 2, nk, d), rng, bias=0.5), _half((2, 2, nk, d), rng)
@@ -176,7 +183,7 @@ def test_fp8_path_within_bound_and_scores_exact(causal):
             qh, kh, vh, vm = _dequantized(r, b, h, h, "per_thread", "fp8", "fp16")
             ex = oracle.exact_forward(qh[None, None], kh[None, None], (vh + vm[None, :])[None, None],
                                       causal=causal, sm_scale=1 / math.sqrt(d))
-            bound = (2.0 ** -4 + nk * 2.0 ** -10 / 448) * np.abs(vh).max()
+            bound = (2.0 ** -3 / (1 - 2.0 ** -4) + nk * 2.0 ** -9 * 8 / 448) * np.abs(vh).max()
             err = np.abs(r["out"][b][h] - ex["out"][0][0]).max()
             assert err <= bound, (err, bound)
             # typical error is far below the worst-case bound
@@ -184,21 +191,23 @@ def test_fp8_path_within_bound_and_scores_exact(causal):
 
 
 def test_lse_closed_form_with_smoothing():
-    """lse is the log-sum-exp of the unsmoothed dequantized scores:
-    ln sum_j exp(sm_scale q_hat_i.(k_hat'_j + mean_k))."""
+    """lse is the log-sum-exp of the unsmoothed dequantized scores,
+    ln sum_j exp(sm_scale q_hat_i.(k_hat'_j + mean_k)), up to the rounding of
+    the P values that l sums: within ln(1 + 2^-11) on the fp16 path."""
     rng = np.random.default_rng(25)
     nq, nk, d = 64, 150, 64
     q, k, v = _half((1, 2, nq, d), rng), _half((1, 2, nk, d), rng, bias=1.5), _half((1, 2, nk, d), rng)
     for causal in (False, True):
-        r = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_warp", smooth_k=True, causal=causal)
+        r = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_warp", smooth_k=True, causal=causal,
+                                     v_dtype="fp16")
         for h in range(2):
-            qh, kh, _, _ = _dequantized(r, 0, h, h, "per_warp", "fp8", "fp16")
+            qh, kh, _, _ = _dequantized(r, 0, h, h, "per_warp", "fp16", "fp16")
             km = r["k_mean"][0][h].astype(np.float64)
             s = (qh @ (kh + km[None, :]).T) / math.sqrt(d)
             if causal:
                 s = np.where(np.arange(nk)[None, :] <= np.arange(nq)[:, None], s, -np.inf)
             ref = sps.logsumexp(s, axis=1)
-            assert np.max(np.abs(r["lse"][0][h] - ref)) < 2e-5
+            assert np.max(np.abs(r["lse"][0][h] - ref)) < 2.0 ** -10
 
 
 def test_gqa_and_varlen_slicing():
@@ -220,3 +229,22 @@ def test_gqa_and_varlen_slicing():
         assert np.array_equal(r["out"][b], rb["out"][0])
         assert np.array_equal(r["q8"][b], rb["q8"][0])
         assert np.array_equal(r["k8"][b], rb["k8"][0][::2])
+
+
+def test_lse_pq_share_of_p_rounding():
+    """lse_pq is |ln sum(rounded P) - ln sum(P)|: 0 when every P is exactly
+    representable, and within the format's relative rounding bound
+    (2^-4 for E4M3 normals, 2^-11 for fp16) otherwise."""
+    rng = np.random.default_rng(31)
+    k = _half((1, 1, 150, 64), rng)
+    v = _half((1, 1, 150, 64), rng)
+    # Q = 0: every score is 0, so every P is 2^(log2(448) - tau) = 56, an E4M3 value
+    r0 = oracle.reference_forward(np.zeros((1, 1, 40, 64), np.float32), k, v, dtype="fp16", gran="per_thread")
+    assert np.all(r0["lse_pq"][0] == 0.0)
+    q = _half((1, 1, 40, 64), rng, scale=2.0)
+    r8 = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_thread")
+    pq8 = r8["lse_pq"][0]
+    assert np.all(pq8 > 0) and np.all(pq8 <= -math.log1p(-2.0 ** -4))
+    r16 = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_thread", v_dtype="fp16")
+    pq16 = r16["lse_pq"][0]
+    assert np.all(pq16 <= -math.log1p(-2.0 ** -11)) and pq16.max() < pq8.max()

@@ -23,8 +23,8 @@ MUTATIONS = {
                                    "const float L = p_mode == 0 ? (float)log2(256.0) - (float)tau : 0.0f;"),
     "lse: smoothing correction sign": ("lse[ri] = ((double)m - (double)L + log2(l)) * M_LN2 + corr;",
                                        "lse[ri] = ((double)m - (double)L + log2(l)) * M_LN2 - corr;"),
-    "causal: diagonal masked": ("long lim = (long)i + causal_shift;\n            if (lim < last) last = (int)lim;\n        }\n        float m",
-                                "long lim = (long)i + causal_shift - 1;\n            if (lim < last) last = (int)lim;\n        }\n        float m"),
+    "causal: diagonal masked": ("long lim = (long)i + causal_shift;\n            if (lim < last) last = (int)lim;",
+                                "long lim = (long)i + causal_shift - 1;\n            if (lim < last) last = (int)lim;"),
     "epilogue: V scale dropped": ("double sc = p_mode == 0 ? (double)vscale[c] / l : 1.0 / l;",
                                   "double sc = p_mode == 0 ? 1.0 / (448.0 * l) : 1.0 / l;"),
     "epilogue: V mean not added back": ("if (vmean) o += vmean[c];", ""),
