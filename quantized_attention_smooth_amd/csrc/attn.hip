@@ -37,6 +37,8 @@
 //    lets one wavefront keep the MFMA pipe and the VALU busy together.
 //  * O^T (fp32) is rescaled only when some row of the wavefront raised its
 //    running maximum (lazy rescaling with threshold kTau).
+#include <type_traits>
+
 #include "sage_device.h"
 
 namespace sage {
@@ -50,6 +52,15 @@ constexpr float kLog2_448 = 8.807354922057604f;   // log2 of the FP8 P scale (44
 constexpr int kTau = 3;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = I .. N-1.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 template <int DP, int PV>
@@ -59,48 +70,61 @@ struct AttnCfg {
     static constexpr int VE = PV == 0 ? 1 : 2;          // V element bytes
     static constexpr int VROW = kBK * VE;               // V^T tile row (one channel) bytes
     static constexpr int VT_BYTES = DP * VROW;
-    static constexpr int SC_OFF = KT_BYTES + VT_BYTES;  // the tile's K scales, one 16-byte slot per wavefront
-    static constexpr int STAGE = KT_BYTES + VT_BYTES + 64;
+    static constexpr int SC_OFF = KT_BYTES + VT_BYTES;  // the tile's K scales, one 256-byte slot per wavefront
+    static constexpr int STAGE = KT_BYTES + VT_BYTES + 4 * 256;
     static constexpr int NI = (KT_BYTES + VT_BYTES) / (16 * kThreads);   // 1 KB DMA instructions per wavefront
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
-// Direct global -> LDS copy of one key tile into one stage of the ring.
-// Instruction i of wavefront w fills the 1 KB of granules [(4i + w) * 64, +64);
-// lane L writes granule (4i + w) * 64 + L.  The granule at (row, physical
-// chunk c) receives logical chunk swz(row, c) (the swizzle is an involution),
-// so readers address logical chunk c at swz(row, c).  Lanes 0-3 of every
-// wavefront then copy the tile's K scales (4 groups of 16 keys, or the one
-// group of 64 four times) into the wavefront's own 16-byte slot, so that the
-// softmax reads them from LDS instead of issuing global loads behind the
-// in-flight copies.  Every wavefront issues NI + 1 copies per tile.
+// Direct global -> LDS copy of one key tile into one stage of the ring, as
+// NI + 1 instructions per wavefront that the key loop can place one by one.
+// Instruction i < NI of wavefront w fills the 1 KB of granules
+// [(4i + w) * 64, +64); lane L writes granule (4i + w) * 64 + L.  The granule
+// at (row, physical chunk c) receives logical chunk swz(row, c) (the swizzle
+// is an involution), so readers address logical chunk c at swz(row, c).
+// Instruction NI copies the tile's K scales into the wavefront's own 256-byte
+// slot, 4 bytes per lane: lane L holds group L % 4 (4 groups of 16 keys), or
+// the one group of 64 keys; the softmax reads the first 16 bytes.  All lanes
+// take part so that no branch splits the loop body.  (The K tile is a whole
+// number of 256-granule rounds, so whether instruction i copies K or V is
+// known at compile time.)
 template <int DP, int PV>
-__device__ __forceinline__ void dma_tile(uint8_t* stage, const int8_t* kbase, const uint8_t* vbase,
-                                         int64_t vrow_stride, const float* ksbase, bool ks16, int t, int wave,
-                                         int lane) {
-    using C = AttnCfg<DP, PV>;
-    constexpr int KG = C::KT_BYTES / 16, KCPR = DP / 16, VCPR = C::VROW / 16;
-#pragma unroll
-    for (int i = 0; i < C::NI; ++i) {
-        const int gbase = (4 * i + wave) * 64;           // wave-uniform
-        const int g = gbase + lane;
-        const uint8_t* src;
-        if (gbase < KG) {
-            const int row = g / KCPR, ch = swz<DP>(row, g % KCPR);
-            src = reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t * C::KT_BYTES + row * DP + ch * 16;
+struct TileCopy {
+    const int8_t* kbase;
+    const uint8_t* vbase;
+    int64_t vrow_stride;
+    const float* ksbase;
+    bool ks16;
+    int wave, lane;                                     // wave is wave-uniform (an SGPR)
+
+    template <int I>
+    __device__ __forceinline__ void issue(uint8_t* stage, int t) const {
+        using C = AttnCfg<DP, PV>;
+        constexpr int KG = C::KT_BYTES / 16, KCPR = DP / 16, VCPR = C::VROW / 16;
+        static_assert(KG % 256 == 0, "K tile must fill whole copy rounds");
+        if constexpr (I < C::NI) {
+            const int gbase = (4 * I + wave) * 64;
+            const int g = gbase + lane;
+            const uint8_t* src;
+            if constexpr (I < KG / 256) {
+                const int row = g / KCPR, ch = swz<DP>(row, g % KCPR);
+                src = reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t * C::KT_BYTES + row * DP + ch * 16;
+            } else {
+                const int gv = g - KG, row = gv / VCPR, ch = swz<C::VROW>(row, gv % VCPR);
+                src = vbase + row * vrow_stride + (int64_t)t * C::VROW + ch * 16;
+            }
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + gbase * 16), 16, 0, 0);
         } else {
-            const int gv = g - KG, row = gv / VCPR, ch = swz<C::VROW>(row, gv % VCPR);
-            src = vbase + row * vrow_stride + (int64_t)t * C::VROW + ch * 16;
+            const float* src = ks16 ? ksbase + 4 * t + (lane & 3) : ksbase + t;
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + C::SC_OFF + wave * 256), 4, 0, 0);
         }
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + gbase * 16), 16, 0, 0);
     }
-    if (lane < 4) {
-        const float* src = ks16 ? ksbase + 4 * t + lane : ksbase + t;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + C::SC_OFF + wave * 16), 4, 0, 0);
+    __device__ __forceinline__ void issue_all(uint8_t* stage, int t) const {
+        static_for<0, AttnCfg<DP, PV>::NI + 1>([&](auto i) { issue<decltype(i)::value>(stage, t); });
     }
-}
+};
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
@@ -156,24 +180,27 @@ __device__ __forceinline__ void qk_half(const v4i (&kf)[2][DP / 32], const v4i (
             S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[cb], cb == 0 ? biasv : S[kb], 0, 0, 0);
 }
 
-// V^T fragments of one tile (A operand of P.V: channel row cb*32 + n, the keys
-// of lane half hh).
-template <int DP, int PV>
-struct VFrag {
-    // FP8: 32 bytes per 32-channel block; fp16/bf16: 4 x 16 bytes per block
-    v4i f[DP / 32][PV == 0 ? 2 : 4];
-};
+// V^T operand of P.V for one tile.  FP8: a[cb] = the 32 bytes of channel row cb*32 + n for the keys of
+// lane half hh; fp16/bf16: a[cb][u] = 8 of those keys (u-th 16-byte chunk).
+template <int DP, int PV> struct VA;
+template <int DP> struct VA<DP, 0> { v8i a[DP / 32]; };
+template <int DP> struct VA<DP, 1> { v4i a[DP / 32][4]; };
+template <int DP> struct VA<DP, 2> { v4i a[DP / 32][4]; };
 
 template <int DP, int PV>
-__device__ __forceinline__ void load_vfrag(const uint8_t* vs, int n, int hh, VFrag<DP, PV>& vf) {
+__device__ __forceinline__ void load_va(const uint8_t* vs, int n, int hh, VA<DP, PV>& va) {
     using C = AttnCfg<DP, PV>;
 #pragma unroll
     for (int cb = 0; cb < DP / 32; ++cb) {
         const int row = cb * 32 + n;
+        const uint8_t* r = vs + row * C::VROW;
+        if constexpr (PV == 0) {
+            const v4i lo = *reinterpret_cast<const v4i*>(r + swz<C::VROW>(row, 2 * hh) * 16);
+            const v4i hi = *reinterpret_cast<const v4i*>(r + swz<C::VROW>(row, 2 * hh + 1) * 16);
+            va.a[cb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        } else {
 #pragma unroll
-        for (int u = 0; u < (PV == 0 ? 2 : 4); ++u) {
-            const int ch = (PV == 0 ? 2 : 4) * hh + u;
-            vf.f[cb][u] = *reinterpret_cast<const v4i*>(vs + row * C::VROW + swz<C::VROW>(row, ch) * 16);
+            for (int u = 0; u < 4; ++u) va.a[cb][u] = *reinterpret_cast<const v4i*>(r + swz<C::VROW>(row, 4 * hh + u) * 16);
         }
     }
 }
@@ -205,7 +232,7 @@ __device__ __forceinline__ void phalf_zero(PHalf<PV>& P) {
 // next tile, past the rescale branch).
 template <int PV>
 __device__ __forceinline__ void keep_here(const PHalf<PV>& P) {
-#if __HIP_DEVICE_COMPILE__                              // VGPR constraints exist only for the gfx950 pass
+#if __HIP_DEVICE_COMPILE__                              // register constraints exist only for the gfx950 pass
     if constexpr (PV == 0) {
         asm volatile("" ::"v"(P.w));
     } else {
@@ -231,39 +258,91 @@ __device__ __forceinline__ void make_ones(Ones<PV>& o, bool par) {
     }
 }
 
-// O^T += V^T P^T and l += rowsum(P) for one row block.
-template <int DP, int PV>
-__device__ __forceinline__ void pv_half(const VFrag<DP, PV>& vf, const PHalf<PV>& P, const Ones<PV>& ones,
-                                        v16f (&o)[DP / 32], v4f& ls) {
-    if constexpr (PV == 0) {
-#pragma unroll
-        for (int cb = 0; cb < DP / 32; ++cb) {
-            const v4i lo = vf.f[cb][0], hi = vf.f[cb][1];
-            const v8i va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            o[cb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, P.w, o[cb], 0, 0, 0, 0, 0, 0);
-        }
-        ls = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones.v, P.w, ls, 0, 0, 0, 0, 0, 0);
-    } else {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int cb = 0; cb < DP / 32; ++cb) {
-                if constexpr (PV == 1)
-                    o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, vf.f[cb][u]), P.h[u],
-                                                                   o[cb], 0, 0, 0);
-                else
-                    o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, vf.f[cb][u]), P.h[u],
-                                                                    o[cb], 0, 0, 0);
-            }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if constexpr (PV == 1) ls = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones.v, P.h[u], ls, 0, 0, 0);
-            else ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones.v, P.h[u], ls, 0, 0, 0);
-        }
-    }
+// ---- P.V on the matrix cores with O^T in AGPRs.
+// The library is built with MFMA results in VGPRs, so that the softmax reads
+// the score accumulators directly; the output accumulators, which only the
+// matrix cores touch, live in AGPRs instead, through these MFMAs written as
+// inline assembly.  The compiler does not see them as MFMAs, so every place
+// where compiled code reads or writes O passes o_guard() first and after:
+// an MFMA result may be read by the VALU only 18 wait states after a 16-pass
+// MFMA, and a VALU write must precede the MFMA that reads it by a few.
+template <int DP>
+__device__ __forceinline__ void o_guard(v16f (&o)[DP / 32]) {
+#if __HIP_DEVICE_COMPILE__
+    if constexpr (DP == 128)
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]), "+a"(o[2]), "+a"(o[3]));
+    else
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+a"(o[0]), "+a"(o[1]));
+#endif
 }
 
-// Online softmax of one tile for one row block (rows row0 + n).
+// Keeps the P.V operands (V^T and P) alive and untouched
+// until a safe distance after the last MFMA that reads them: an MFMA may
+// still be waiting behind the previous one on the matrix core when the
+// compiler, which sees only inline assembly, would reuse those registers.
+template <int DP, int PV>
+__device__ __forceinline__ void operands_guard(VA<DP, PV>& va, PHalf<PV>& p0, PHalf<PV>& p1) {
+#if __HIP_DEVICE_COMPILE__
+    if constexpr (PV == 0) {
+#pragma unroll
+        for (int cb = 0; cb < DP / 32; ++cb) asm volatile("" : "+v"(va.a[cb]));
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(p0.w), "+v"(p1.w));
+#pragma unroll
+        for (int cb = 0; cb < DP / 32; ++cb) asm volatile("" : "+v"(va.a[cb]));
+    } else {
+#pragma unroll
+        for (int cb = 0; cb < DP / 32; ++cb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(va.a[cb][u]));
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(p0.h[0]), "+v"(p0.h[1]), "+v"(p0.h[2]), "+v"(p0.h[3]),
+                     "+v"(p1.h[0]), "+v"(p1.h[1]), "+v"(p1.h[2]), "+v"(p1.h[3]));
+#pragma unroll
+        for (int cb = 0; cb < DP / 32; ++cb)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) asm volatile("" : "+v"(va.a[cb][u]));
+    }
+#endif
+}
+
+// One P.V MFMA: O^T[cb] += V^T[cb] P^T (FP8: all 64 keys; fp16/bf16: the
+// 16-key slice u).  The V^T operand comes from LDS loads whose lgkmcnt wait
+// the compiler places right before this instruction, or from VALU writes it
+// cannot see as hazards here; the matrix core needs a few more wait states
+// before it reads such registers (without them the first MFMA after the wait
+// was seen to read stale values), hence the s_nop inside the statement.
+template <int DP, int PV, int CB, int U>
+__device__ __forceinline__ void pv_job(const VA<DP, PV>& va, const PHalf<PV>& P, v16f (&o)[DP / 32]) {
+#if __HIP_DEVICE_COMPILE__
+    if constexpr (PV == 0)
+        asm("s_nop 4\n\tv_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(o[CB]) : "v"(va.a[CB]), "v"(P.w));
+    else if constexpr (PV == 1)
+        asm("s_nop 4\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(o[CB]) : "v"(va.a[CB][U]), "v"(P.h[U]));
+    else
+        asm("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o[CB]) : "v"(va.a[CB][U]), "v"(P.h[U]));
+#endif
+}
+
+// Row sums: l += rowsum(P) (slice U on the fp16/bf16 path).
+template <int PV, int U>
+__device__ __forceinline__ void rs_job(const PHalf<PV>& P, const Ones<PV>& ones, v4f& ls) {
+    if constexpr (PV == 0) ls = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones.v, P.w, ls, 0, 0, 0, 0, 0, 0);
+    else if constexpr (PV == 1) ls = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones.v, P.h[U], ls, 0, 0, 0);
+    else ls = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones.v, P.h[U], ls, 0, 0, 0);
+}
+
+// The whole P.V and row-sum step of one row block (outside the pipeline).
+template <int DP, int PV>
+__device__ __forceinline__ void pv_all(const VA<DP, PV>& va, const PHalf<PV>& P, const Ones<PV>& ones,
+                                       v16f (&o)[DP / 32], v4f& ls) {
+    static_for<0, DP / 32>([&](auto cb) {
+        if constexpr (PV == 0) pv_job<DP, PV, decltype(cb)::value, 0>(va, P, o);
+        else static_for<0, 4>([&](auto u) { pv_job<DP, PV, decltype(cb)::value, decltype(u)::value>(va, P, o); });
+    });
+    if constexpr (PV == 0) rs_job<PV, 0>(P, ones, ls);
+    else static_for<0, 4>([&](auto u) { rs_job<PV, decltype(u)::value>(P, ones, ls); });
+}
+
+// Online softmax of one tile for one row block (rows row + n).
 //   f = (q_scale * sm_scale * log2 e) * k_scale per key-scale group g
 //   (g = 2*kb + i/8 covers keys 16g .. 16g+15; a 64-key group fills all four),
 //   tile max  mt = max over keys of fl32(S * f),
@@ -273,7 +352,8 @@ __device__ __forceinline__ void pv_half(const VFrag<DP, PV>& vf, const PHalf<PV>
 // exactly as the oracle orders these roundings.  MASKED hides the keys a
 // row may not see (past the sequence end, or after the row when causal).
 // Returns, per lane, whether its row raised its maximum; m_prev then holds
-// the maximum before this tile.
+// the maximum before this tile.  (Used by the masked tiles; the pipelined
+// loop runs the same steps in pieces, see SoftmaxPieces.)
 template <int PV, bool MASKED>
 __device__ __forceinline__ bool softmax_half(const v16i (&S)[2], const float (&ksv)[4], float cq, float& m_ref,
                                              float& m_prev, PHalf<PV>& P, int k0, int Lk, bool causal, int row,
@@ -348,7 +428,93 @@ __device__ __forceinline__ bool softmax_half(const v16i (&S)[2], const float (&k
     return raise;
 }
 
-// Rescale O and l of a row whose maximum moved (m_prev -> m_ref).
+// The unmasked softmax of one row block cut into pieces that the pipelined
+// loop interleaves with MFMAs: head<0..3>() compute the scale factors and the
+// tile maximum and take the raise decision (the same steps and roundings as
+// softmax_half), piece<E>() turns the lane's 32 keys into P two at a time.
+template <int PV>
+struct SoftmaxPieces {
+    static constexpr float p_log2_scale = PV == 0 ? kLog2_448 - (float)kTau : 0.f;
+    float f[4], cg[4], smax;
+    int mi[4];
+    int word[8];                                        // FP8: bytes 0-1 of word w between its two chunks
+    bool raise;
+
+    template <int H>
+    __device__ __forceinline__ void head(const v16i (&S)[2], const float (&ksv)[4], float cq, float& m_ref,
+                                         float& m_prev) {
+        if constexpr (H == 0) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) f[g] = ksv[g] * cq;
+            group_max(S, 0);
+        } else if constexpr (H == 1) {
+            group_max(S, 1);
+            group_max(S, 2);
+        } else if constexpr (H == 2) {
+            group_max(S, 3);
+            smax = -INFINITY;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) smax = fmaxf(smax, (bits_f(mi[g]) - kAccBias) * f[g]);
+        } else {
+            smax = swap_half_max(smax);
+            m_prev = m_ref;
+            raise = smax > m_ref + (float)kTau;
+            m_ref = raise ? smax : m_ref;
+            const float nb = p_log2_scale - m_ref;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) cg[g] = __builtin_fmaf(-kAccBias, f[g], nb);
+        }
+    }
+    // Keys 2E and 2E+1 of the lane's 32 become P in three stages, which the
+    // loop skews over consecutive pieces (piece e: products of chunk e, exp2
+    // of chunk e-1, conversion of chunk e-2), so that no instruction waits
+    // for the one just before it.
+    static constexpr int NPIECE = 18;
+    float xv[32], pv[32];
+
+    template <int E>
+    __device__ __forceinline__ void piece(const v16i (&S)[2], PHalf<PV>& P) {
+        if constexpr (E < 16) {
+            constexpr int kb = E >> 3, i0 = (2 * E) & 15, g = 2 * kb + (i0 >> 3);
+            xv[2 * E] = __builtin_fmaf(bits_f(S[kb][i0]), f[g], cg[g]);
+            xv[2 * E + 1] = __builtin_fmaf(bits_f(S[kb][i0 + 1]), f[g], cg[g]);
+        }
+        if constexpr (E >= 1 && E - 1 < 16) {
+            pv[2 * E - 2] = __builtin_amdgcn_exp2f(xv[2 * E - 2]);
+            pv[2 * E - 1] = __builtin_amdgcn_exp2f(xv[2 * E - 1]);
+        }
+        if constexpr (E >= 2) convert<E - 2>(P);
+    }
+
+    template <int C>
+    __device__ __forceinline__ void convert(PHalf<PV>& P) {
+        constexpr int kb = C >> 3, i0 = (2 * C) & 15, g = 2 * kb + (i0 >> 3);
+        const float p0 = pv[2 * C], p1 = pv[2 * C + 1];
+        if constexpr (PV == 0) {
+            constexpr int w = C >> 1;
+            if constexpr ((C & 1) == 0) word[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
+            else P.w[w] = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, word[w], true);
+        } else if constexpr (PV == 1) {
+            P.h[g][i0 & 7] = (_Float16)p0;
+            P.h[g][(i0 & 7) + 1] = (_Float16)p1;
+        } else {
+            P.h[g][i0 & 7] = (__bf16)p0;
+            P.h[g][(i0 & 7) + 1] = (__bf16)p1;
+        }
+    }
+
+  private:
+    __device__ __forceinline__ void group_max(const v16i (&S)[2], int g) {
+        const int kb = g >> 1, i0 = (g & 1) * 8;
+        int m = S[kb][i0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) m = max(m, S[kb][i0 + i]);
+        mi[g] = m;
+    }
+};
+
+// Rescale O and l of a row whose maximum moved (m_prev -> m_ref).  O must be
+// guarded (o_guard) around this.
 template <int DP>
 __device__ __forceinline__ void rescale_half(float m_ref, float m_prev, v16f (&o)[DP / 32], v4f& ls) {
     // 0 when the row had no maximum yet (its O and l are 0)
@@ -361,30 +527,22 @@ __device__ __forceinline__ void rescale_half(float m_ref, float m_prev, v16f (&o
     for (int i = 0; i < 4; ++i) ls[i] *= alpha;
 }
 
-// Instruction order of one pipelined tile (two phases).  Each phase: its K
-// fragment reads, then its MFMAs spread evenly through the softmax VALU
-// stream of the other row block.  The V fragments are read at the start.
-template <int DP, int PV>
-__device__ __forceinline__ void interleave_hint() {
-    constexpr int NCB = DP / 32;
-    constexpr int N_K = 2 * NCB;                                // K fragment reads per phase
-    constexpr int N_V = NCB * (PV == 0 ? 2 : 4);                // V fragment reads per tile
-    constexpr int N_MFMA = 2 * NCB + (PV == 0 ? NCB + 1 : 4 * NCB + 4);   // per phase
-    constexpr int N_VALU = 160;                                 // per phase, approximate
-    constexpr int PER = (N_VALU + N_MFMA - 1) / N_MFMA;
-    __builtin_amdgcn_sched_group_barrier(0x100, N_K + N_V + 1, 0);   // DS reads: K scales, V, K of phase A
-    __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
-#pragma unroll
-    for (int i = 0; i < N_MFMA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, PER, 0); // VALU
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, N_K, 0);     // DS reads: K of phase B
-#pragma unroll
-    for (int i = 0; i < N_MFMA; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, PER, 0);
-    }
+// ---- instruction interleave of the pipelined loop
+// A region pairs NJ matrix-core jobs (MFMAs) with NV VALU pieces: after job k
+// come pieces k*NV/NJ .. (k+1)*NV/NJ - 1, and a scheduling fence keeps the
+// compiler from regrouping them, so that one wavefront keeps both the VALU
+// and the matrix cores busy.  job(k) and piece(e) take
+// std::integral_constant indices.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+template <int NJ, int NV, class J, class V>
+__device__ __forceinline__ void interleave(J&& job, V&& piece) {
+    static_for<0, NJ>([&](auto kc) {
+        constexpr int k = decltype(kc)::value;
+        job(kc);
+        static_for<k * NV / NJ, (k + 1) * NV / NJ>(piece);
+        sched_fence();
+    });
 }
 
 template <int DP, int PV, bool OUT_BF16>
@@ -398,7 +556,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     constexpr int LPT = C::NI + 1;                      // DMA instructions per wavefront per tile
     __shared__ __attribute__((aligned(16))) uint8_t smem[NST * C::STAGE];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
     const int n = lane & 31, hh = lane >> 5;
 
     // ---- work item
@@ -468,13 +627,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 
     auto stage_of = [&](int t) { return smem + (t % NST) * C::STAGE; };
     auto ks_of = [&](const uint8_t* st, float (&ksv)[4]) {
-        const v4f k4 = *reinterpret_cast<const v4f*>(st + C::SC_OFF + wave * 16);
+        const v4f k4 = *reinterpret_cast<const v4f*>(st + C::SC_OFF + wave * 256);
 #pragma unroll
         for (int g = 0; g < 4; ++g) ksv[g] = k4[g];
     };
+    const TileCopy<DP, PV> copier{kbase, vbase, vrow_stride, ksbase, ks16, wave, lane};
     auto issue = [&](int t) {
-        if (t < ntiles)
-            dma_tile<DP, PV>(stage_of(t), kbase, vbase, vrow_stride, ksbase, ks16, t, wave, lane);
+        if (t < ntiles) copier.issue_all(stage_of(t), t);
     };
     // end of step t: tile t+2 (read in step t+1) has landed in every wavefront
     auto step_end = [&](int t) {
@@ -492,77 +651,124 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 
     // ---- pipelined main loop over the unmasked tiles.  The two row blocks
     // of the wavefront alternate, so that the VALU and the matrix cores always
-    // have independent work.  Tile t is one straight-line block:
-    //   phase A: softmax of block 0 (tile t)
-    //            || QK^T of block 1 (tile t), P.V of block 0 (tile t-1)
-    //   phase B: softmax of block 1 (tile t)
-    //            || QK^T of block 0 (tile t+1), P.V of block 1 (tile t-1)
-    // then, rarely, the rescale of O and l for rows whose maximum moved.  All
-    // P.V products issued in tile t use P of tile t-1, computed with the
-    // maxima before tile t, so the rescale after them is exact bookkeeping.
+    // have independent work.  Tile t is four regions (VALU || matrix cores):
+    //   H0: maximum of block 0 (tile t)   || P.V of block 1 (tile t-1)
+    //   E0: P of block 0 (tile t)         || QK^T of block 1 (tile t)
+    //   H1: maximum of block 1 (tile t)   || P.V of block 0 (tile t)
+    //   E1: P of block 1 (tile t)         || QK^T of block 0 (tile t+1)
+    // A block's O and l are rescaled (rarely) right after its H region: its
+    // last P.V was issued in the previous region with P from before the move.
+    // Carried from tile to tile: S of block 0 (tile t+1), P of block 1
+    // (tile t), V^T of tile t, K fragments and K scales of tile t+1.  The copy
+    // of tile t+AHEAD is spread over the E regions; past the last tile it
+    // copies the last tile again into the free stage, which keeps the
+    // wait counts uniform.
+    using C2 = AttnCfg<DP, PV>;
+    constexpr int NQK = 2 * NCB;                        // QK^T MFMAs per block and tile
+    constexpr int NPV = PV == 0 ? NCB : 4 * NCB;        // P.V MFMAs
+    constexpr int NRS = PV == 0 ? 1 : 4;                // row-sum MFMAs
+    constexpr int NDMA = C2::NI + 1;
     v16i S[2][2];
     PHalf<PV> P[2];
-    phalf_zero<PV>(P[0]);                               // P.V of "tile -1" adds exact zeros
-    phalf_zero<PV>(P[1]);
+    phalf_zero<PV>(P[1]);                               // P.V of block 1 for "tile -1" adds exact zeros
+    v4i kf[2][NCB];
+    float ksv[4];
+    VA<DP, PV> va;
     if (n_main > 0 && live) {
-        v4i kf[2][NCB];
         load_kfrag<DP>(stage_of(0), n, hh, kf);
+        ks_of(stage_of(0), ksv);
+        load_va<DP, PV>(stage_of(0) + C::KT_BYTES, n, hh, va);
         qk_half<DP>(kf, qf[0], biasv, S[0]);
     }
+    auto pv_region_job = [&](auto kc, const PHalf<PV>& Pj, v16f (&oj)[NCB], v4f& lsj) {
+        constexpr int k = decltype(kc)::value;
+        if constexpr (k < NPV) {
+            if constexpr (PV == 0) pv_job<DP, PV, k, 0>(va, Pj, oj);
+            else pv_job<DP, PV, k % NCB, k / NCB>(va, Pj, oj);
+        } else {
+            rs_job<PV, k - NPV>(Pj, ones, lsj);
+        }
+    };
     for (int t = 0; t < n_main; ++t) {
-        issue(t + AHEAD);
+        const int tc = min(t + AHEAD, ntiles - 1);      // tile copied in this step (clamped)
+        uint8_t* st_copy = stage_of(t + AHEAD);
         if (live) {
             const uint8_t* st = stage_of(t);
-            float ksv[4];
-            ks_of(st, ksv);
-            VFrag<DP, PV> vf;                           // V of tile t-1 (tile 0 for t = 0: times zero P)
-            load_vfrag<DP, PV>(stage_of(t == 0 ? 0 : t - 1) + C::KT_BYTES, n, hh, vf);
-            const PHalf<PV> P0 = P[0], P1 = P[1];
-            bool raised;
-            {   // phase A
-                v4i kf[2][NCB];
-                load_kfrag<DP>(st, n, hh, kf);
-                raised = softmax_half<PV, false>(S[0], ksv, cq[0], m_ref[0], m_prev[0], P[0], 0, 0, false, 0, hh);
-                qk_half<DP>(kf, qf[1], biasv, S[1]);
-                pv_half<DP, PV>(vf, P0, ones, o[0], ls[0]);
-            }
-            {   // phase B
-                v4i kf[2][NCB];
-                load_kfrag<DP>(stage_of(t + 1), n, hh, kf);
-                raised |= softmax_half<PV, false>(S[1], ksv, cq[1], m_ref[1], m_prev[1], P[1], 0, 0, false, 0, hh);
-                qk_half<DP>(kf, qf[0], biasv, S[0]);
-                pv_half<DP, PV>(vf, P1, ones, o[1], ls[1]);
-            }
-            interleave_hint<DP, PV>();
-            keep_here<PV>(P[0]);
-            keep_here<PV>(P[1]);
-            if (__any(raised)) {
+            const uint8_t* st_next = stage_of(t + 1);
+            // H0
+            SoftmaxPieces<PV> s0;
+            interleave<NPV + NRS, 4>([&](auto kc) { pv_region_job(kc, P[1], o[1], ls[1]); },
+                                     [&](auto hc) { s0.template head<decltype(hc)::value>(S[0], ksv, cq[0], m_ref[0],
+                                                                                           m_prev[0]); });
+            if (__any(s0.raise)) {
+                o_guard<DP>(o[0]);
                 rescale_half<DP>(m_ref[0], m_prev[0], o[0], ls[0]);
-                rescale_half<DP>(m_ref[1], m_prev[1], o[1], ls[1]);
+                o_guard<DP>(o[0]);
             }
+            // E0
+            interleave<NQK, SoftmaxPieces<PV>::NPIECE>(
+                [&](auto kc) {
+                    constexpr int k = decltype(kc)::value;
+                    constexpr int cb = k >> 1, kb = k & 1;
+                    S[1][kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[1][cb], cb == 0 ? biasv : S[1][kb],
+                                                                     0, 0, 0);
+                    if constexpr (k == 0) load_va<DP, PV>(st + C::KT_BYTES, n, hh, va);   // V of tile t
+                    if constexpr (k >= 1 && k - 1 < NDMA / 2) copier.template issue<k - 1>(st_copy, tc);
+                },
+                [&](auto ec) { s0.template piece<decltype(ec)::value>(S[0], P[0]); });
+            // H1
+            SoftmaxPieces<PV> s1;
+            interleave<NPV + NRS, 4>(
+                [&](auto kc) {
+                    pv_region_job(kc, P[0], o[0], ls[0]);
+                    if constexpr (decltype(kc)::value == 0) load_kfrag<DP>(st_next, n, hh, kf);   // K of tile t+1
+                },
+                [&](auto hc) { s1.template head<decltype(hc)::value>(S[1], ksv, cq[1], m_ref[1], m_prev[1]); });
+            if (__any(s1.raise)) {
+                o_guard<DP>(o[1]);
+                rescale_half<DP>(m_ref[1], m_prev[1], o[1], ls[1]);
+                o_guard<DP>(o[1]);
+            }
+            // E1
+            interleave<NQK, SoftmaxPieces<PV>::NPIECE>(
+                [&](auto kc) {
+                    constexpr int k = decltype(kc)::value;
+                    constexpr int cb = k >> 1, kb = k & 1;
+                    S[0][kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[0][cb], cb == 0 ? biasv : S[0][kb],
+                                                                     0, 0, 0);
+                    if constexpr (k >= 1 && k - 1 < NDMA - NDMA / 2) copier.template issue<NDMA / 2 + k - 1>(st_copy, tc);
+                    if constexpr (k == NQK - 1) ks_of(st_next, ksv);                     // K scales of tile t+1
+                },
+                [&](auto ec) { s1.template piece<decltype(ec)::value>(S[1], P[1]); });
+            keep_here<PV>(P[1]);
+        } else {
+            copier.issue_all(st_copy, tc);
         }
-        step_end(t);
+        wait_vmcnt<LPT * (AHEAD - 2)>();                // tile t+2 has landed
+        block_sync();
     }
-    if (live && n_main > 0) {                           // P.V of the last pipelined tile
-        VFrag<DP, PV> vf;
-        load_vfrag<DP, PV>(stage_of(n_main - 1) + C::KT_BYTES, n, hh, vf);
-        pv_half<DP, PV>(vf, P[0], ones, o[0], ls[0]);
-        pv_half<DP, PV>(vf, P[1], ones, o[1], ls[1]);
+    if (live && n_main > 0) {                           // P.V of block 1, last pipelined tile (V is in va)
+        o_guard<DP>(o[1]);                              // spaces the MFMAs from the VALU writes of P
+        pv_all<DP, PV>(va, P[1], ones, o[1], ls[1]);
     }
+    // the newest copy of the loop may still be in flight; the masked tiles
+    // below count their own copies from zero, and the workgroup must not end
+    // with a copy into its LDS outstanding
+    wait_vmcnt<0>();
+    int t = n_main;
 
     // ---- remaining tiles (a ragged end, the causal diagonal): one at a time
-    for (int t = n_main; t < ntiles; ++t) {
+    for (; t < ntiles; ++t) {
         issue(t + AHEAD);
         const int k0 = t * kBK;
         if (live && (!a.causal || k0 <= wq0 + 63)) {
             const uint8_t* st = stage_of(t);
-            float ksv[4];
             ks_of(st, ksv);
-            v4i kf[2][NCB];
             load_kfrag<DP>(st, n, hh, kf);
             qk_half<DP>(kf, qf[0], biasv, S[0]);
             qk_half<DP>(kf, qf[1], biasv, S[1]);
             const bool need_mask = (k0 + kBK > Lk) || (a.causal && k0 + kBK - 1 > wq0);
+            PHalf<PV> P[2];
             bool raised[2];
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -573,18 +779,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                     raised[j] = softmax_half<PV, false>(S[j], ksv, cq[j], m_ref[j], m_prev[j], P[j], k0, Lk,
                                                         a.causal, wq0 + 32 * j + n, hh);
             }
+            o_guard<DP>(o[0]);
+            o_guard<DP>(o[1]);
             if (__any(raised[0] || raised[1])) {
                 rescale_half<DP>(m_ref[0], m_prev[0], o[0], ls[0]);
                 rescale_half<DP>(m_ref[1], m_prev[1], o[1], ls[1]);
+                o_guard<DP>(o[0]);
+                o_guard<DP>(o[1]);
             }
-            VFrag<DP, PV> vf;
-            load_vfrag<DP, PV>(st + C::KT_BYTES, n, hh, vf);
-            pv_half<DP, PV>(vf, P[0], ones, o[0], ls[0]);
-            pv_half<DP, PV>(vf, P[1], ones, o[1], ls[1]);
+            VA<DP, PV> va;
+            load_va<DP, PV>(st + C::KT_BYTES, n, hh, va);
+            pv_all<DP, PV>(va, P[0], ones, o[0], ls[0]);
+            pv_all<DP, PV>(va, P[1], ones, o[1], ls[1]);
         }
         step_end(t);
     }
     if (!live) return;
+    o_guard<DP>(o[0]);                                  // the last P.V MFMAs wrote O
+    o_guard<DP>(o[1]);
 
     // ---- epilogue: normalise, add back V's mean, write in the caller's layout
     const float* vsc = PV == 0 ? a.vs + khead * DP : nullptr;
