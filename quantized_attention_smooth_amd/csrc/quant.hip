@@ -1,15 +1,19 @@
 // quant.hip -- HBM-bound quantize passes for the quantized attention forward
 // (gfx950).
 //
-//   stats_kernel     exact per-channel sums of K or V along the sequence
+//   statistics       exact per-channel sums of K or V along the sequence
 //                    (plus min/max for FP8 V), one workgroup per 256-token
-//                    chunk of one (sequence, head);
-//   finalize_kernel  chunk partials -> mean, and for FP8 V the per-channel
-//                    scale amax/448 and its reciprocal;
-//   quant_rows_kernel  Q or K rows -> INT8 codes + one fp32 scale per group
-//                    of rows (per_block / per_warp / per_thread);
-//   quant_v_kernel   V -> transposed FP8 E4M3FN codes (or fp16/bf16), keys
+//                    chunk of one (sequence, head), written as partials;
+//   row quantization Q or K rows -> INT8 codes + one fp32 scale per group of
+//                    rows (per_block / per_warp / per_thread);
+//   V quantization   V -> transposed FP8 E4M3FN codes (or fp16/bf16), keys
 //                    reordered inside each 64-key block for the P.V MFMA.
+// Four launches in all: [Q rows + K statistics], [K rows], [V statistics],
+// [V].  Every workgroup of the K / V pass reduces the (at most kMaxChunks)
+// chunk partials of its (sequence, head) itself -- they sit in L2 -- after
+// issuing its own loads, so no separate finalize pass (and no cross-workgroup
+// synchronisation, whose device-scope fences write back and invalidate the
+// per-XCD L2) is needed.
 //
 // Method ("SageAttention deployment guide", pwwt.cn): sec. 1 first bullet
 // (Q, K -> INT8 with per-block / per-thread scale factors), second bullet
@@ -17,8 +21,9 @@
 // sequence; smooth_v subtracts V's mean).
 //
 // Bit-exactness: a mean is fl32(fl64(exact sum) / N).  fp16 inputs are
-// summed as int64 multiples of 2^-24 (every fp16 value is one; exact for
-// N < 2^23).  bf16 inputs are summed in fp64, which is exact -- and therefore
+// summed as multiples of 2^-24 (every fp16 value is one): each thread adds
+// its 16 values in fp64, which is exact (|sum| < 2^44 units), and the
+// threads' and chunks' sums are combined as int64 (exact for N < 2^23).  bf16 inputs are summed in fp64, which is exact -- and therefore
 // independent of the summation order -- when a column's values span fewer
 // than 53 bits including log2(N).  The quantizer's fp32 operations are single
 // IEEE operations (no contraction), so codes and scales are reproducible.
@@ -67,31 +72,78 @@ __device__ __forceinline__ const uint16_t* row_ptr(const void* base, int64_t sb,
 }
 
 // ---------------------------------------------------------------------------
+// The statistics of one (sequence, head), reduced from its chunk partials by
+// the threads tid < DP of a workgroup (one channel each): the mean
+// fl32(fl64(exact sum) / N) and, with want_minmax, the FP8 V scale amax / 448
+// and its reciprocal (amax over |v - mean| if smooth, else over |v|).
+template <bool BF16>
+__device__ __forceinline__ void channel_stats(const StatsArgs& a, int h, int b, int c, bool smooth, float& mean,
+                                              float& scale, float& inv) {
+    using Acc = typename std::conditional<BF16, double, long long>::type;
+    int n0, N;
+    seq_range(a.cu, b, a.N, n0, N);
+    const int64_t base = ((int64_t)b * a.H + h) * a.chunks * a.dp + c;
+    Acc s = 0;
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll 8
+    for (int k = 0; k < a.chunks; ++k) {                // chunks <= kMaxChunks
+        s += reinterpret_cast<const Acc*>(a.part_sum)[base + (int64_t)k * a.dp];
+        if (a.want_minmax) {
+            lo = fminf(lo, a.part_min[base + (int64_t)k * a.dp]);
+            hi = fmaxf(hi, a.part_max[base + (int64_t)k * a.dp]);
+        }
+    }
+    mean = 0.f;
+    if (N > 0) {
+        double s64;
+        if constexpr (BF16) s64 = s;
+        else s64 = (double)s * 0x1p-24;
+        mean = (float)(s64 / (double)N);
+    }
+    scale = 0.f;
+    inv = 0.f;
+    if (a.want_minmax && N > 0) {
+        // rounding is monotonic, so max_n |fl(v_n - mean)| is reached at the
+        // column's max or min
+        const float amax = smooth ? fmaxf(hi - mean, mean - lo) : fmaxf(hi, -lo);
+        if (amax > 0.f) {
+            scale = amax / 448.0f;
+            inv = 448.0f / amax;
+        }
+    }
+}
+
+// Statistics of one kStatsChunk-token chunk of one (sequence, head): per-channel sum
+// (exact, see above) and, for FP8 V, min and max.
 template <bool BF16, int DP, bool VEC>
-__global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
+__device__ __forceinline__ void stats_body(const StatsArgs& a, int chunk, int h, int b) {
     constexpr int TPR = DP / 8;
     constexpr int RPP = kThreads / TPR;
+    constexpr int ITER = kStatsChunk / RPP;
     using Acc = typename std::conditional<BF16, double, long long>::type;
-    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     int n0, N;
     seq_range(a.cu, b, a.N, n0, N);
     const int tid = threadIdx.x, cg = tid % TPR, rr = tid / TPR;
-    const int t0 = chunk * kStatsChunk;
-    Acc sum[8];
+    const int t_lo = chunk * a.chunk_len, t_hi = min(N, t_lo + a.chunk_len);
+    double sum[8];
     float mn[8], mx[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) { sum[j] = 0; mn[j] = INFINITY; mx[j] = -INFINITY; }
-    for (int r = rr; r < kStatsChunk; r += RPP) {
-        const int n = t0 + r;
-        if (n >= N) break;
-        float v[8];
-        load8<BF16, VEC>(row_ptr(a.x, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d, v);
+    for (int j = 0; j < 8; ++j) { sum[j] = 0.0; mn[j] = INFINITY; mx[j] = -INFINITY; }
+    for (int t0 = t_lo; t0 < t_hi; t0 += kStatsChunk) {
+        // the ITER loads of a step are independent: unrolled, they are in flight together
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if constexpr (BF16) sum[j] += (double)v[j];
-            else sum[j] += (long long)(v[j] * 16777216.0f);   // exact: v * 2^24 is an integer
-            mn[j] = fminf(mn[j], v[j]);
-            mx[j] = fmaxf(mx[j], v[j]);
+        for (int it = 0; it < ITER; ++it) {
+            const int n = t0 + it * RPP + rr;
+            if (n < t_hi) {
+                float v[8];
+                load8<BF16, VEC>(row_ptr(a.x, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d, v);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    sum[j] += (double)v[j];
+                    mn[j] = fminf(mn[j], v[j]);
+                    mx[j] = fmaxf(mx[j], v[j]);
+                }
+            }
         }
     }
     // reduce over the RPP threads that share a channel group, in a fixed order
@@ -99,7 +151,8 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     __shared__ float s_mn[RPP][DP], s_mx[RPP][DP];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        s_sum[rr][cg * 8 + j] = sum[j];
+        if constexpr (BF16) s_sum[rr][cg * 8 + j] = sum[j];
+        else s_sum[rr][cg * 8 + j] = (long long)(sum[j] * 16777216.0);   // an integer below 2^53: exact
         s_mn[rr][cg * 8 + j] = mn[j];
         s_mx[rr][cg * 8 + j] = mx[j];
     }
@@ -121,75 +174,66 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     }
 }
 
-template <bool BF16>
-__global__ void finalize_kernel(FinalizeArgs a) {
-    using Acc = typename std::conditional<BF16, double, long long>::type;
-    const int h = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
-    if (c >= a.dp) return;
-    int n0, N;
-    seq_range(a.cu, b, a.N, n0, N);
-    const int64_t base = ((int64_t)b * a.H + h) * a.chunks * a.dp + c;
-    Acc s = 0;
-    float lo = INFINITY, hi = -INFINITY;
-    for (int k = 0; k < a.chunks; ++k) {
-        s += reinterpret_cast<const Acc*>(a.part_sum)[base + (int64_t)k * a.dp];
-        if (a.mode == 1) {
-            lo = fminf(lo, a.part_min[base + (int64_t)k * a.dp]);
-            hi = fmaxf(hi, a.part_max[base + (int64_t)k * a.dp]);
+// Channel statistics of one (sequence, head) for a tile workgroup: threads
+// tid < DP reduce their channel's partials (channel_stats), tile 0 stores the
+// caller's outputs, and mean / inverse scale land in LDS for all threads.
+template <bool BF16, int DP>
+__device__ __forceinline__ void tile_stats(const StatsArgs& a, int tile, int h, int b, float* s_mu, float* s_inv) {
+    const int tid = threadIdx.x;
+    if (tid < DP) {
+        float mean, sc, iv;
+        channel_stats<BF16>(a, h, b, tid, a.smooth, mean, sc, iv);
+        const int64_t o = ((int64_t)b * a.H + h) * DP + tid;
+        if (tile == 0) {
+            if (a.out_mean) a.out_mean[o] = mean;
+            if (a.out_scale) a.out_scale[o] = sc;
         }
+        s_mu[tid] = mean;
+        if (s_inv) s_inv[tid] = iv;
     }
-    float mean = 0.f;
-    if (N > 0) {
-        double s64;
-        if constexpr (BF16) s64 = s;
-        else s64 = (double)s * 0x1p-24;
-        mean = (float)(s64 / (double)N);
-    }
-    const int64_t o = ((int64_t)b * a.H + h) * a.dp + c;
-    if (a.mean) a.mean[o] = mean;
-    if (a.mode == 1) {
-        float amax = 0.f;
-        if (N > 0) {
-            // rounding is monotonic, so max_n |fl(v_n - mean)| is reached at
-            // the column's max or min
-            if (a.smooth) amax = fmaxf(hi - mean, mean - lo);
-            else amax = fmaxf(hi, -lo);
-        }
-        a.v_scale[o] = amax > 0.f ? amax / 448.0f : 0.f;
-        a.v_inv[o] = amax > 0.f ? 448.0f / amax : 0.f;
-    }
+    __syncthreads();
 }
 
 // ---------------------------------------------------------------------------
+// INT8 quantization of one 128-row tile of Q or K.  With ks (K with
+// smoothing) the workgroup subtracts the channel means, which it reduces
+// from the statistics partials while its row loads are in flight.
 template <bool BF16, int DP, bool VEC>
-__global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantRowsArgs a) {
+__device__ __forceinline__ void quant_rows_body(const QuantRowsArgs& a, int tile, int h, int b, const StatsArgs* ks) {
     constexpr int TPR = DP / 8;
     constexpr int RPP = kThreads / TPR;
     constexpr int PASSES = kPad / RPP;
-    const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     int n0, N;
     seq_range(a.cu, b, a.N, n0, N);
     const int tid = threadIdx.x, cg = tid % TPR, rr = tid / TPR;
     const int row0 = tile * kPad;
     __shared__ float rmax[kPad];
+    float vals[PASSES][8];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int n = row0 + p * RPP + rr;
+        if (n < N) {
+            load8<BF16, VEC>(row_ptr(a.x, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d, vals[p]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vals[p][j] = 0.f;
+        }
+    }
+    __shared__ float s_mu[DP];
+    if (ks) tile_stats<BF16, DP>(*ks, tile, h, b, s_mu, nullptr);
     float mu[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) mu[j] = a.mean ? a.mean[((int64_t)b * a.H + h) * DP + cg * 8 + j] : 0.f;
-    float vals[PASSES][8];
+    for (int j = 0; j < 8; ++j) mu[j] = ks ? s_mu[cg * 8 + j] : 0.f;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const int r = p * RPP + rr, n = row0 + r;
         float m = 0.f;
         if (n < N) {
-            load8<BF16, VEC>(row_ptr(a.x, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d, vals[p]);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 vals[p][j] = vals[p][j] - mu[j];
                 m = fmaxf(m, fabsf(vals[p][j]));
             }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) vals[p][j] = 0.f;
         }
 #pragma unroll
         for (int off = 1; off < TPR; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -222,40 +266,85 @@ __global__ __launch_bounds__(kThreads) void quant_rows_kernel(QuantRowsArgs a) {
     }
 }
 
+// Pass 1 of the Q/K quantization: workgroups [0, nq_blocks) quantize Q
+// tiles; the others collect K statistics (smooth_k) or quantize K tiles.
+template <bool BF16, int DP, bool VEC>
+__global__ __launch_bounds__(kThreads) void qk_pass1_kernel(QuantRowsArgs q, QuantRowsArgs k, StatsArgs ks,
+                                                            int nq_blocks, int smooth) {
+    int bid = blockIdx.x;
+    if (bid < nq_blocks) {
+        const int tiles = q.npad / kPad;
+        quant_rows_body<BF16, DP, VEC>(q, bid % tiles, (bid / tiles) % q.H, bid / tiles / q.H, nullptr);
+        return;
+    }
+    bid -= nq_blocks;
+    if (smooth) {
+        stats_body<BF16, DP, VEC>(ks, bid % ks.chunks, (bid / ks.chunks) % ks.H, bid / ks.chunks / ks.H);
+    } else {
+        const int tiles = k.npad / kPad;
+        quant_rows_body<BF16, DP, VEC>(k, bid % tiles, (bid / tiles) % k.H, bid / tiles / k.H, nullptr);
+    }
+}
+
+// Pass 2 (smooth_k): K tiles, minus the mean of their (sequence, head);
+// tile 0 stores k_mean.
+template <bool BF16, int DP, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_pass2_kernel(QuantRowsArgs k, StatsArgs ks) {
+    const int tiles = k.npad / kPad;
+    const int tile = blockIdx.x % tiles, h = (blockIdx.x / tiles) % k.H, b = blockIdx.x / tiles / k.H;
+    quant_rows_body<BF16, DP, VEC>(k, tile, h, b, &ks);
+}
+
 // ---------------------------------------------------------------------------
+template <bool BF16, int DP, bool VEC>
+__global__ __launch_bounds__(kThreads) void v_stats_kernel(StatsArgs vs) {
+    const int bid = blockIdx.x;
+    stats_body<BF16, DP, VEC>(vs, bid % vs.chunks, (bid / vs.chunks) % vs.H, bid / vs.chunks / vs.H);
+}
+
+// V -> V^T codes for one 128-key tile.  With statistics, the workgroup
+// reduces the channel means / FP8 scales of its (sequence, head) while its
+// loads are in flight (tile 0 stores v_scale and v_mean).
 template <bool BF16, int DP, bool FP8, bool VEC>
-__global__ __launch_bounds__(kThreads) void quant_v_kernel(QuantVArgs a) {
+__global__ __launch_bounds__(kThreads) void quant_v_kernel(QuantVArgs a, StatsArgs vs, int have_stats) {
     constexpr int TPR = DP / 8;
     constexpr int RPP = kThreads / TPR;
     constexpr int PASSES = kPad / RPP;
     constexpr int E = FP8 ? 1 : 2;                      // bytes per element
-    const int tile = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tiles = a.npad / kPad;
+    const int tile = blockIdx.x % tiles, h = (blockIdx.x / tiles) % a.H, b = blockIdx.x / tiles / a.H;
     int n0, N;
     seq_range(a.cu, b, a.N, n0, N);
     const int tid = threadIdx.x, cg = tid % TPR, rr = tid / TPR;
     const int row0 = tile * kPad;
     __shared__ __attribute__((aligned(16))) uint8_t sv[DP * kPad * E];
     const int64_t hb = ((int64_t)b * a.H + h) * DP;
+    float v[PASSES][8];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int n = row0 + p * RPP + rr;
+        if (n < N) {
+            load8<BF16, VEC>(row_ptr(a.v, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d, v[p]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[p][j] = 0.f;
+        }
+    }
+    __shared__ float s_mu[DP], s_inv[DP];
+    if (have_stats) tile_stats<BF16, DP>(vs, tile, h, b, s_mu, s_inv);
     float mu[8], inv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        mu[j] = a.mean ? a.mean[hb + cg * 8 + j] : 0.f;
-        inv[j] = FP8 ? a.inv[hb + cg * 8 + j] : 1.f;
+        mu[j] = (have_stats && vs.smooth) ? s_mu[cg * 8 + j] : 0.f;
+        inv[j] = (have_stats && FP8) ? s_inv[cg * 8 + j] : 1.f;
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const int r = p * RPP + rr, n = row0 + r;
-        float v[8];
-        if (n < N) {
-            load8<BF16, VEC>(row_ptr(a.v, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d, v);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = 0.f;
-        }
         const int pos = (r & ~63) | v_perm_pos(r & 63);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float x = v[j] - mu[j];
+            const float x = v[p][j] - mu[j];
             const int c = cg * 8 + j;
             if constexpr (FP8) {
                 float t = x * inv[j];
@@ -281,71 +370,57 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(QuantVArgs a) {
 
 // ---------------------------------------------------------------------------
 // launchers
-template <bool BF16>
-static hipError_t stats_dispatch(const StatsArgs& a, bool vec, hipStream_t s) {
-    dim3 grid(a.chunks, a.H, a.B);
-    if (a.dp == 128) {
-        if (vec) stats_kernel<BF16, 128, true><<<grid, kThreads, 0, s>>>(a);
-        else stats_kernel<BF16, 128, false><<<grid, kThreads, 0, s>>>(a);
-    } else {
-        if (vec) stats_kernel<BF16, 64, true><<<grid, kThreads, 0, s>>>(a);
-        else stats_kernel<BF16, 64, false><<<grid, kThreads, 0, s>>>(a);
+template <bool BF16, int DP, bool VEC>
+static hipError_t quant_qk_dispatch(const QuantRowsArgs& q, const QuantRowsArgs& k, const StatsArgs& ks, bool smooth,
+                                    hipStream_t s) {
+    const int nq = (q.npad / kPad) * q.H * q.B;
+    const int n2 = smooth ? ks.chunks * ks.H * ks.B : (k.npad / kPad) * k.H * k.B;
+    qk_pass1_kernel<BF16, DP, VEC><<<nq + n2, kThreads, 0, s>>>(q, k, ks, nq, smooth ? 1 : 0);
+    if (smooth) {
+        if (hipError_t e = hipGetLastError()) return e;
+        k_pass2_kernel<BF16, DP, VEC><<<(k.npad / kPad) * k.H * k.B, kThreads, 0, s>>>(k, ks);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_stats(const StatsArgs& a, bool bf16, hipStream_t s) {
-    // vector loads need 16-byte aligned rows
-    const bool vec = (reinterpret_cast<uintptr_t>(a.x) % 16 == 0) && a.d % 8 == 0 && a.sb % 8 == 0 &&
-                     a.sh % 8 == 0 && a.sn % 8 == 0;
-    return bf16 ? stats_dispatch<true>(a, vec, s) : stats_dispatch<false>(a, vec, s);
-}
-
-hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t s) {
-    dim3 grid(a.H, a.B);
-    if (bf16) finalize_kernel<true><<<grid, 128, 0, s>>>(a);
-    else finalize_kernel<false><<<grid, 128, 0, s>>>(a);
-    return hipGetLastError();
-}
-
-template <bool BF16, int DP>
-static void quant_rows_dispatch(const QuantRowsArgs& a, bool vec, hipStream_t s) {
-    dim3 grid(a.npad / kPad, a.H, a.B);
-    if (vec) quant_rows_kernel<BF16, DP, true><<<grid, kThreads, 0, s>>>(a);
-    else quant_rows_kernel<BF16, DP, false><<<grid, kThreads, 0, s>>>(a);
-}
-
-hipError_t launch_quant_rows(const QuantRowsArgs& a, bool bf16, bool vec, hipStream_t s) {
-    const int dp = a.d <= 64 ? 64 : 128;
+hipError_t launch_quant_qk(const QuantRowsArgs& q, const QuantRowsArgs& k, const StatsArgs& ks, bool smooth,
+                           bool bf16, bool vec, hipStream_t s) {
+    const int dp = q.d <= 64 ? 64 : 128;
+#define SAGE_QK(BF, D, V) return quant_qk_dispatch<BF, D, V>(q, k, ks, smooth, s)
     if (bf16) {
-        if (dp == 128) quant_rows_dispatch<true, 128>(a, vec, s);
-        else quant_rows_dispatch<true, 64>(a, vec, s);
+        if (dp == 128) { if (vec) SAGE_QK(true, 128, true); else SAGE_QK(true, 128, false); }
+        else { if (vec) SAGE_QK(true, 64, true); else SAGE_QK(true, 64, false); }
     } else {
-        if (dp == 128) quant_rows_dispatch<false, 128>(a, vec, s);
-        else quant_rows_dispatch<false, 64>(a, vec, s);
+        if (dp == 128) { if (vec) SAGE_QK(false, 128, true); else SAGE_QK(false, 128, false); }
+        else { if (vec) SAGE_QK(false, 64, true); else SAGE_QK(false, 64, false); }
     }
+#undef SAGE_QK
+}
+
+template <bool BF16, int DP, bool FP8, bool VEC>
+static hipError_t quant_v_dispatch(const QuantVArgs& a, const StatsArgs& vs, bool stats, bool smooth, hipStream_t s) {
+    if (stats) {
+        v_stats_kernel<BF16, DP, VEC><<<vs.chunks * vs.H * vs.B, kThreads, 0, s>>>(vs);
+        if (hipError_t e = hipGetLastError()) return e;
+    }
+    quant_v_kernel<BF16, DP, FP8, VEC><<<(a.npad / kPad) * a.H * a.B, kThreads, 0, s>>>(a, vs, stats ? 1 : 0);
     return hipGetLastError();
 }
 
-template <bool BF16, int DP, bool FP8>
-static void quant_v_dispatch(const QuantVArgs& a, bool vec, hipStream_t s) {
-    dim3 grid(a.npad / kPad, a.H, a.B);
-    if (vec) quant_v_kernel<BF16, DP, FP8, true><<<grid, kThreads, 0, s>>>(a);
-    else quant_v_kernel<BF16, DP, FP8, false><<<grid, kThreads, 0, s>>>(a);
-}
-
-hipError_t launch_quant_v(const QuantVArgs& a, bool bf16, bool fp8, bool vec, hipStream_t s) {
+hipError_t launch_quant_v(const QuantVArgs& a, const StatsArgs& vs, bool stats, bool smooth, bool bf16, bool fp8,
+                          bool vec, hipStream_t s) {
     const int dp = a.d <= 64 ? 64 : 128;
-#define SAGE_QV(BF, D, F) quant_v_dispatch<BF, D, F>(a, vec, s)
+#define SAGE_QV(BF, D, F, V) return quant_v_dispatch<BF, D, F, V>(a, vs, stats, smooth, s)
+#define SAGE_QV2(BF, D, F) { if (vec) SAGE_QV(BF, D, F, true); else SAGE_QV(BF, D, F, false); }
     if (bf16) {
-        if (dp == 128) { if (fp8) SAGE_QV(true, 128, true); else SAGE_QV(true, 128, false); }
-        else { if (fp8) SAGE_QV(true, 64, true); else SAGE_QV(true, 64, false); }
+        if (dp == 128) { if (fp8) SAGE_QV2(true, 128, true) else SAGE_QV2(true, 128, false) }
+        else { if (fp8) SAGE_QV2(true, 64, true) else SAGE_QV2(true, 64, false) }
     } else {
-        if (dp == 128) { if (fp8) SAGE_QV(false, 128, true); else SAGE_QV(false, 128, false); }
-        else { if (fp8) SAGE_QV(false, 64, true); else SAGE_QV(false, 64, false); }
+        if (dp == 128) { if (fp8) SAGE_QV2(false, 128, true) else SAGE_QV2(false, 128, false) }
+        else { if (fp8) SAGE_QV2(false, 64, true) else SAGE_QV2(false, 64, false) }
     }
+#undef SAGE_QV2
 #undef SAGE_QV
-    return hipGetLastError();
 }
 
 }  // namespace sage

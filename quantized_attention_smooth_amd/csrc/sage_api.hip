@@ -52,21 +52,24 @@ int check_sizes(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
 }
 
 struct WsLayout {
-    size_t sum_off, min_off, max_off, inv_off, total;
+    size_t sum_off, min_off, max_off, total;
+    int chunk_len;
     int chunks;
 };
 
 WsLayout ws_layout(int B, int H, int N, int d) {
     WsLayout w{};
     const int dp = dp_of(d);
-    w.chunks = (int)((N + sage::kStatsChunk - 1) / sage::kStatsChunk);
+    // kStatsChunk tokens per chunk, longer (a multiple of it) beyond kMaxChunks chunks
+    const int64_t per = (N + sage::kMaxChunks - 1) / sage::kMaxChunks;
+    w.chunk_len = (int)std::max<int64_t>(sage::kStatsChunk, round_up(per, sage::kStatsChunk));
+    w.chunks = (int)((N + w.chunk_len - 1) / w.chunk_len);
     const size_t cells = (size_t)B * H * w.chunks * dp;
     auto al = [](size_t x) { return (x + 255) / 256 * 256; };
     w.sum_off = 0;
     w.min_off = al(cells * 8);
     w.max_off = w.min_off + al(cells * 4);
-    w.inv_off = w.max_off + al(cells * 4);
-    w.total = w.inv_off + al((size_t)B * H * dp * 4);
+    w.total = w.max_off + al(cells * 4);
     return w;
 }
 
@@ -116,17 +119,13 @@ int sage_quant_qk(const sage_quant_qk_params* p, void* stream) {
     const int dp = dp_of(p->d);
     const int nq_pad = (int)round_up(p->Nq, sage::kPad), nk_pad = (int)round_up(p->Nk, sage::kPad);
     uint8_t* wsb = reinterpret_cast<uint8_t*>(p->workspace);
+    sage::StatsArgs st{};
+    st.x = p->k; st.sb = p->k_stride_b; st.sh = p->k_stride_h; st.sn = p->k_stride_n;
+    st.cu = p->cu_seqlens_k; st.B = p->B; st.H = p->Hkv; st.N = p->Nk; st.d = p->d; st.dp = dp;
+    st.chunks = ws.chunks; st.chunk_len = ws.chunk_len; st.want_minmax = 0;
     if (p->smooth_k) {
-        sage::StatsArgs st{};
-        st.x = p->k; st.sb = p->k_stride_b; st.sh = p->k_stride_h; st.sn = p->k_stride_n;
-        st.cu = p->cu_seqlens_k; st.B = p->B; st.H = p->Hkv; st.N = p->Nk; st.d = p->d; st.dp = dp;
-        st.chunks = ws.chunks; st.want_minmax = 0;
-        st.part_sum = wsb + ws.sum_off; st.part_min = nullptr; st.part_max = nullptr;
-        if (int r = hip_status(sage::launch_stats(st, bf16, s), "K statistics launch")) return r;
-        sage::FinalizeArgs fa{};
-        fa.part_sum = st.part_sum; fa.cu = p->cu_seqlens_k; fa.B = p->B; fa.H = p->Hkv; fa.N = p->Nk;
-        fa.dp = dp; fa.chunks = ws.chunks; fa.mode = 0; fa.mean = p->k_mean;
-        if (int r = hip_status(sage::launch_finalize(fa, bf16, s), "K mean launch")) return r;
+        st.part_sum = wsb + ws.sum_off;
+        st.out_mean = p->k_mean;
     }
     auto vec_ok = [&](const void* x, int64_t sb, int64_t sh, int64_t sn) {
         return aligned(x, 16) && p->d % 8 == 0 && sb % 8 == 0 && sh % 8 == 0 && sn % 8 == 0;
@@ -134,17 +133,15 @@ int sage_quant_qk(const sage_quant_qk_params* p, void* stream) {
     sage::QuantRowsArgs qa{};
     qa.x = p->q; qa.sb = p->q_stride_b; qa.sh = p->q_stride_h; qa.sn = p->q_stride_n; qa.cu = p->cu_seqlens_q;
     qa.B = p->B; qa.H = p->Hq; qa.N = p->Nq; qa.npad = nq_pad; qa.d = p->d;
-    qa.group_shift = q_group_shift(p->gran); qa.mean = nullptr; qa.out = p->q8; qa.scale = p->q_scale;
-    if (int r = hip_status(sage::launch_quant_rows(qa, bf16, vec_ok(p->q, p->q_stride_b, p->q_stride_h, p->q_stride_n), s),
-                           "Q quantize launch"))
-        return r;
+    qa.group_shift = q_group_shift(p->gran); qa.out = p->q8; qa.scale = p->q_scale;
     sage::QuantRowsArgs ka{};
     ka.x = p->k; ka.sb = p->k_stride_b; ka.sh = p->k_stride_h; ka.sn = p->k_stride_n; ka.cu = p->cu_seqlens_k;
     ka.B = p->B; ka.H = p->Hkv; ka.N = p->Nk; ka.npad = nk_pad; ka.d = p->d;
-    ka.group_shift = k_group_shift(p->gran); ka.mean = p->smooth_k ? p->k_mean : nullptr;
-    ka.out = p->k8; ka.scale = p->k_scale;
-    if (int r = hip_status(sage::launch_quant_rows(ka, bf16, vec_ok(p->k, p->k_stride_b, p->k_stride_h, p->k_stride_n), s),
-                           "K quantize launch"))
+    ka.group_shift = k_group_shift(p->gran); ka.out = p->k8; ka.scale = p->k_scale;
+    const bool vec = vec_ok(p->q, p->q_stride_b, p->q_stride_h, p->q_stride_n) &&
+                     vec_ok(p->k, p->k_stride_b, p->k_stride_h, p->k_stride_n);
+    if (int r = hip_status(sage::launch_quant_qk(qa, ka, st, p->smooth_k, bf16, vec, s),
+                           "Q/K quantize launch"))
         return r;
     return ok();
 }
@@ -177,30 +174,26 @@ int sage_quant_v(const sage_quant_v_params* p, void* stream) {
     const int dp = dp_of(p->d);
     const int nk_pad = (int)round_up(p->Nk, sage::kPad);
     uint8_t* wsb = reinterpret_cast<uint8_t*>(p->workspace);
-    float* v_inv = need_stats ? reinterpret_cast<float*>(wsb + ws.inv_off) : nullptr;
+    sage::StatsArgs st{};
+    st.x = p->v; st.sb = p->v_stride_b; st.sh = p->v_stride_h; st.sn = p->v_stride_n;
+    st.cu = p->cu_seqlens_k; st.B = p->B; st.H = p->Hkv; st.N = p->Nk; st.d = p->d; st.dp = dp;
+    st.chunks = ws.chunks; st.chunk_len = ws.chunk_len; st.want_minmax = fp8 ? 1 : 0;
     if (need_stats) {
-        sage::StatsArgs st{};
-        st.x = p->v; st.sb = p->v_stride_b; st.sh = p->v_stride_h; st.sn = p->v_stride_n;
-        st.cu = p->cu_seqlens_k; st.B = p->B; st.H = p->Hkv; st.N = p->Nk; st.d = p->d; st.dp = dp;
-        st.chunks = ws.chunks; st.want_minmax = fp8 ? 1 : 0;
         st.part_sum = wsb + ws.sum_off;
         st.part_min = reinterpret_cast<float*>(wsb + ws.min_off);
         st.part_max = reinterpret_cast<float*>(wsb + ws.max_off);
-        if (int r = hip_status(sage::launch_stats(st, bf16, s), "V statistics launch")) return r;
-        sage::FinalizeArgs fa{};
-        fa.part_sum = st.part_sum; fa.part_min = st.part_min; fa.part_max = st.part_max;
-        fa.cu = p->cu_seqlens_k; fa.B = p->B; fa.H = p->Hkv; fa.N = p->Nk; fa.dp = dp; fa.chunks = ws.chunks;
-        fa.mode = fp8 ? 1 : 0; fa.smooth = p->smooth_v; fa.mean = p->smooth_v ? p->v_mean : nullptr;
-        fa.v_scale = p->v_scale; fa.v_inv = v_inv;
-        if (int r = hip_status(sage::launch_finalize(fa, bf16, s), "V statistics finalize launch")) return r;
+        st.smooth = p->smooth_v ? 1 : 0;
+        st.out_mean = p->smooth_v ? p->v_mean : nullptr;
+        st.out_scale = fp8 ? p->v_scale : nullptr;
     }
     sage::QuantVArgs va{};
     va.v = p->v; va.sb = p->v_stride_b; va.sh = p->v_stride_h; va.sn = p->v_stride_n; va.cu = p->cu_seqlens_k;
-    va.B = p->B; va.H = p->Hkv; va.N = p->Nk; va.npad = nk_pad; va.d = p->d;
-    va.mean = p->smooth_v ? p->v_mean : nullptr; va.inv = v_inv; va.vt = p->vt;
+    va.B = p->B; va.H = p->Hkv; va.N = p->Nk; va.npad = nk_pad; va.d = p->d; va.vt = p->vt;
     const bool vec = aligned(p->v, 16) && p->d % 8 == 0 && p->v_stride_b % 8 == 0 && p->v_stride_h % 8 == 0 &&
                      p->v_stride_n % 8 == 0;
-    if (int r = hip_status(sage::launch_quant_v(va, bf16, fp8, vec, s), "V quantize launch")) return r;
+    if (int r = hip_status(sage::launch_quant_v(va, st, need_stats, p->smooth_v, bf16, fp8, vec, s),
+                           "V quantize launch"))
+        return r;
     return ok();
 }
 

@@ -23,24 +23,14 @@ struct StatsArgs {
     const int32_t* cu;           // varlen offsets or nullptr
     int B, H, N, d, dp;          // N: dense length or max length
     int chunks;                  // token chunks per (b, h)
+    int chunk_len;               // tokens per chunk (a multiple of kStatsChunk)
     int want_minmax;
     void* part_sum;              // [B][H][chunks][dp] int64 (fp16) or double (bf16)
     float* part_min;             // [B][H][chunks][dp]
     float* part_max;
-};
-
-// Reduce the partial statistics into means (and V scales).
-struct FinalizeArgs {
-    const void* part_sum;
-    const float* part_min;
-    const float* part_max;
-    const int32_t* cu;
-    int B, H, N, dp, chunks;
-    int mode;                    // 0: mean only; 1: FP8 V scale (+ mean if smooth)
-    int smooth;                  // V: subtract the mean before the amax
-    float* mean;                 // [B][H][dp] (may be null when !smooth)
-    float* v_scale;              // [B][H][dp]
-    float* v_inv;                // [B][H][dp] 448 / amax, for the quantize pass
+    int smooth;                  // V: amax over |v - mean| (else over |v|)
+    float* out_mean;             // caller's k_mean / v_mean, or nullptr
+    float* out_scale;            // caller's v_scale, or nullptr
 };
 
 // INT8 quantization of Q or K rows.
@@ -50,7 +40,6 @@ struct QuantRowsArgs {
     const int32_t* cu;
     int B, H, N, npad, d;
     int group_shift;             // log2(rows per scale group)
-    const float* mean;           // [B][H][dp] or nullptr
     int8_t* out;                 // [B][H][npad][dp]
     float* scale;                // [B][H][npad >> group_shift]
 };
@@ -61,8 +50,6 @@ struct QuantVArgs {
     int64_t sb, sh, sn;
     const int32_t* cu;
     int B, H, N, npad, d;
-    const float* mean;           // smooth_v mean or nullptr
-    const float* inv;            // FP8: 448 / amax per channel
     void* vt;                    // [B][H][dp][npad]
 };
 
@@ -97,14 +84,21 @@ struct AttnArgs {
 
 // Launchers (defined in the kernel translation units).  Each returns the
 // hipError_t of the launch.
-hipError_t launch_stats(const StatsArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_finalize(const FinalizeArgs& a, bool bf16, hipStream_t s);
-hipError_t launch_quant_rows(const QuantRowsArgs& a, bool bf16, bool vec, hipStream_t s);
-hipError_t launch_quant_v(const QuantVArgs& a, bool bf16, bool fp8, bool vec, hipStream_t s);
+// Q and K: Q tiles and the K statistics (smooth) in one launch, then the K
+// tiles; without smoothing, one launch for both.
+hipError_t launch_quant_qk(const QuantRowsArgs& q, const QuantRowsArgs& k, const StatsArgs& ks, bool smooth,
+                           bool bf16, bool vec, hipStream_t s);
+// V: statistics (when stats), then the tiles.
+hipError_t launch_quant_v(const QuantVArgs& a, const StatsArgs& vs, bool stats, bool smooth, bool bf16, bool fp8,
+                          bool vec, hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int dp, int pv /*0 fp8, 1 fp16, 2 bf16*/, bool out_bf16,
                        hipStream_t s);
 hipError_t launch_qk_scores(const AttnArgs& a, int dp, hipStream_t s);
 
-constexpr int kStatsChunk = 256;  // tokens per statistics chunk
+// Statistics chunks: kStatsChunk tokens, or longer for long sequences so
+// that a (b, h) has at most kMaxChunks partials (every tile workgroup of the
+// quantize pass reduces all partials of its (b, h)).
+constexpr int kStatsChunk = 128;
+constexpr int kMaxChunks = 32;
 
 }  // namespace sage
