@@ -60,12 +60,14 @@ def cpu_baseline(w, inp, seconds: float) -> dict:
     q, k, v = (inp[x].float().numpy() for x in ("q", "k", "v"))
     ops, heads, t_total = 0.0, 0, 0.0
     grp = w.Hq // w.Hkv
-    for h in range(w.Hq):
+    problems = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    while t_total < seconds:
+        b, h = problems[heads % len(problems)]
         hk = h // grp
         if w.layout == "HND":
-            qs, ks, vs = q[:1, h:h + 1], k[:1, hk:hk + 1], v[:1, hk:hk + 1]
+            qs, ks, vs = q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1]
         else:
-            qs, ks, vs = q[:1, :, h:h + 1], k[:1, :, hk:hk + 1], v[:1, :, hk:hk + 1]
+            qs, ks, vs = q[b:b + 1, :, h:h + 1], k[b:b + 1, :, hk:hk + 1], v[b:b + 1, :, hk:hk + 1]
         t0 = time.perf_counter()
         oracle.reference_forward(np.ascontiguousarray(qs), np.ascontiguousarray(ks), np.ascontiguousarray(vs),
                                  dtype=w.dtype, layout=w.layout, causal=w.causal, gran=w.gran,
@@ -74,10 +76,9 @@ def cpu_baseline(w, inp, seconds: float) -> dict:
         heads += 1
         per = 4.0 * w.Nq * w.Nk * w.d
         ops += per / 2 if w.causal else per
-        if t_total >= seconds:
-            break
     return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} of {w.B * w.Hq} (batch, head) problems of {w.name}, all {w.Nq} query rows, "
+            "sample": f"{heads} (batch, head) problems of {w.name} (of {w.B * w.Hq} per step, taken in order, "
+                      f"repeating if needed), all {w.Nq} query rows, "
                       f"quantization included; {t_total:.1f} s"}
 
 
@@ -89,6 +90,10 @@ def main() -> int:
     ap.add_argument("--workload", default="b2h8n4096d128")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-calibration", action="store_true",
+                    help="before the steps, run a plain 1 GiB -> 1 GiB fp32 elementwise copy three times, so "
+                         "that hardware byte counters of the attention kernel can be scaled by what the same "
+                         "counters read for a kernel of known traffic")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -123,6 +128,14 @@ def main() -> int:
         if ev is not None:
             ev[2].record(stream)
         return out
+
+    if args.traffic_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)            # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -168,7 +181,7 @@ def main() -> int:
         "attn_pct_of_peak": round(100.0 * attn_tops / peak, 2),
         "quant_ms": round(quant_ms, 5),
         "quant_gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": peak, "unit": "TOPS",
+        "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tops / peak, 4), "traffic": measured_traffic(w.name)},
     }
     if not args.no_cpu_baseline:
