@@ -63,7 +63,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int DP, int PV>
+template <int DP, int PV, int NW = 4>
 struct AttnCfg {
     static constexpr int NCB = DP / 32;                 // 32-channel blocks
     static constexpr int KT_BYTES = kBK * DP;           // K tile: 64 keys x Dp int8
@@ -71,8 +71,9 @@ struct AttnCfg {
     static constexpr int VROW = kBK * VE;               // V^T tile row (one channel) bytes
     static constexpr int VT_BYTES = DP * VROW;
     static constexpr int SC_OFF = KT_BYTES + VT_BYTES;  // the tile's K scales, one 256-byte slot per wavefront
-    static constexpr int STAGE = KT_BYTES + VT_BYTES + 4 * 256;
-    static constexpr int NI = (KT_BYTES + VT_BYTES) / (16 * kThreads);   // 1 KB DMA instructions per wavefront
+    static constexpr int STAGE = KT_BYTES + VT_BYTES + NW * 256;
+    static constexpr int NI = (KT_BYTES + VT_BYTES) / (16 * 64 * NW);   // DMA instructions per wavefront
+    static_assert(NI * 16 * 64 * NW == KT_BYTES + VT_BYTES, "tile must fill whole copy rounds");
 };
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -80,17 +81,17 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 // Direct global -> LDS copy of one key tile into one stage of the ring, as
 // NI + 1 instructions per wavefront that the key loop can place one by one.
-// Instruction i < NI of wavefront w fills the 1 KB of granules
-// [(4i + w) * 64, +64); lane L writes granule (4i + w) * 64 + L.  The granule
-// at (row, physical chunk c) receives logical chunk swz(row, c) (the swizzle
-// is an involution), so readers address logical chunk c at swz(row, c).
-// Instruction NI copies the tile's K scales into the wavefront's own 256-byte
-// slot, 4 bytes per lane: lane L holds group L % 4 (4 groups of 16 keys), or
-// the one group of 64 keys; the softmax reads the first 16 bytes.  All lanes
-// take part so that no branch splits the loop body.  (The K tile is a whole
-// number of 256-granule rounds, so whether instruction i copies K or V is
-// known at compile time.)
-template <int DP, int PV>
+// Instruction i < NI of wavefront w (of NW) fills the 1 KB of granules
+// [(NW*i + w) * 64, +64); lane L writes granule (NW*i + w) * 64 + L.  The
+// granule at (row, physical chunk c) receives logical chunk swz(row, c) (the
+// swizzle is an involution), so readers address logical chunk c at
+// swz(row, c).  Instruction NI copies the tile's K scales into the
+// wavefront's own 256-byte slot, 4 bytes per lane: lane L holds group L % 4
+// (4 groups of 16 keys), or the one group of 64 keys; the softmax reads the
+// first 16 bytes.  All lanes take part so that no branch splits the loop
+// body.  Whether a wavefront's granules belong to K or to V^T depends only on
+// the instruction and the wavefront, so the choice is wave-uniform.
+template <int DP, int PV, int NW = 4>
 struct TileCopy {
     const int8_t* kbase;
     const uint8_t* vbase;
@@ -101,20 +102,24 @@ struct TileCopy {
 
     template <int I>
     __device__ __forceinline__ void issue(uint8_t* stage, int t) const {
-        using C = AttnCfg<DP, PV>;
+        using C = AttnCfg<DP, PV, NW>;
         constexpr int KG = C::KT_BYTES / 16, KCPR = DP / 16, VCPR = C::VROW / 16;
-        static_assert(KG % 256 == 0, "K tile must fill whole copy rounds");
+        static_assert(KG % 64 == 0, "K tile must fill whole wavefront chunks");
         if constexpr (I < C::NI) {
-            const int gbase = (4 * I + wave) * 64;
+            const int gbase = (NW * I + wave) * 64;
             const int g = gbase + lane;
-            const uint8_t* src;
-            if constexpr (I < KG / 256) {
+            auto k_src = [&]() {
                 const int row = g / KCPR, ch = swz<DP>(row, g % KCPR);
-                src = reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t * C::KT_BYTES + row * DP + ch * 16;
-            } else {
+                return reinterpret_cast<const uint8_t*>(kbase) + (int64_t)t * C::KT_BYTES + row * DP + ch * 16;
+            };
+            auto v_src = [&]() {
                 const int gv = g - KG, row = gv / VCPR, ch = swz<C::VROW>(row, gv % VCPR);
-                src = vbase + row * vrow_stride + (int64_t)t * C::VROW + ch * 16;
-            }
+                return vbase + row * vrow_stride + (int64_t)t * C::VROW + ch * 16;
+            };
+            const uint8_t* src;
+            if constexpr ((I + 1) * NW * 64 <= KG) src = k_src();
+            else if constexpr (I * NW * 64 >= KG) src = v_src();
+            else src = gbase < KG ? k_src() : v_src();
             __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + gbase * 16), 16, 0, 0);
         } else {
             const float* src = ks16 ? ksbase + 4 * t + (lane & 3) : ksbase + t;
@@ -122,7 +127,7 @@ struct TileCopy {
         }
     }
     __device__ __forceinline__ void issue_all(uint8_t* stage, int t) const {
-        static_for<0, AttnCfg<DP, PV>::NI + 1>([&](auto i) { issue<decltype(i)::value>(stage, t); });
+        static_for<0, AttnCfg<DP, PV, NW>::NI + 1>([&](auto i) { issue<decltype(i)::value>(stage, t); });
     }
 };
 
@@ -167,6 +172,16 @@ __device__ __forceinline__ void load_kfrag(const uint8_t* ks, int n, int hh, v4i
     }
 }
 
+// The K fragments of one 32-channel block (both 32-key halves).
+template <int DP>
+__device__ __forceinline__ void load_kfrag_cb(const uint8_t* ks, int n, int hh, int cb, v4i (&kf)[2][DP / 32]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        const int row = kb * 32 + n;
+        kf[kb][cb] = *reinterpret_cast<const v4i*>(ks + row * DP + swz<DP>(row, cb * 2 + hh) * 16);
+    }
+}
+
 // S^T of one row block: S[kb][i] = bias + S(query n of the block,
 // key 32*kb + 8*(i/4) + 4*hh + i%4).  Two accumulation chains over the
 // channel blocks; the first MFMA of each takes the bias vector as input.
@@ -203,6 +218,17 @@ __device__ __forceinline__ void load_va(const uint8_t* vs, int n, int hh, VA<DP,
             for (int u = 0; u < 4; ++u) va.a[cb][u] = *reinterpret_cast<const v4i*>(r + swz<C::VROW>(row, 4 * hh + u) * 16);
         }
     }
+}
+
+// The FP8 V^T operand of one 32-channel block.
+template <int DP>
+__device__ __forceinline__ void load_va_cb(const uint8_t* vs, int n, int hh, int cb, VA<DP, 0>& va) {
+    constexpr int VROW = kBK;
+    const int row = cb * 32 + n;
+    const uint8_t* r = vs + row * VROW;
+    const v4i lo = *reinterpret_cast<const v4i*>(r + swz<VROW>(row, 2 * hh) * 16);
+    const v4i hi = *reinterpret_cast<const v4i*>(r + swz<VROW>(row, 2 * hh + 1) * 16);
+    va.a[cb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // P of one tile for one row block, as the P.V B operand.  FP8: w holds the
@@ -863,6 +889,296 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// FP8 P.V with two wavefronts per SIMD.  One workgroup of 8 wavefronts (two
+// per SIMD) covers kBQ query rows, 32 per wavefront.  A single wavefront can
+// issue a VALU instruction only every few cycles, so the softmax of one
+// wavefront cannot keep pace with its own MFMAs; with two wavefronts per SIMD
+// the VALU work of both runs side by side while the matrix core serves
+// whichever has an MFMA ready, and each hides the other's latencies.
+// Per wavefront the loop is the same software pipeline as above with one row
+// block: tile t is two regions,
+//   H: maximum of tile t             || P.V of tile t-1 (+ row sums)
+//   E: P of tile t                   || QK^T of tile t+1
+// and O is rescaled (rarely) after H.
+// P.V of the 8-wavefront kernel: O^T stays in VGPRs and the MFMAs are
+// compiler builtins, so the compiler sees every operand and places the wait
+// states itself.
+template <int DP, int CB>
+__device__ __forceinline__ void pv8_job(const VA<DP, 0>& va, const PHalf<0>& P, v16f (&o)[DP / 32]) {
+    o[CB] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va.a[CB], P.w, o[CB], 0, 0, 0, 0, 0, 0);
+}
+template <int DP>
+__device__ __forceinline__ void pv8_all(const VA<DP, 0>& va, const PHalf<0>& P, const Ones<0>& ones,
+                                        v16f (&o)[DP / 32], v4f& ls) {
+    static_for<0, DP / 32>([&](auto cb) { pv8_job<DP, decltype(cb)::value>(va, P, o); });
+    rs_job<0, 0>(P, ones, ls);
+}
+
+constexpr int kWaves8 = 8;
+constexpr int kThreads8 = 64 * kWaves8;
+
+template <int DP, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
+    constexpr int PV = 0, NW = kWaves8;
+    using C = AttnCfg<DP, PV, NW>;
+    constexpr int NCB = C::NCB;
+    constexpr int AHEAD = 3;
+    constexpr int NST = AHEAD + 2;
+    constexpr int LPT = C::NI + 1;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NST * C::STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, hh = lane >> 5;
+
+    const int wg = xcd_remap(blockIdx.x, a.num_wg);
+    int qt = wg % a.n_qtiles;
+    const int bh = wg / a.n_qtiles, h = bh % a.Hq, b = bh / a.Hq;
+    if (a.causal) qt = a.n_qtiles - 1 - qt;
+    int Lq = a.Nq, Lk = a.Nk, qoff = 0;
+    if (a.cu_q) {
+        qoff = a.cu_q[b];
+        Lq = a.cu_q[b + 1] - qoff;
+        Lk = a.cu_k[b + 1] - a.cu_k[b];
+    }
+    const int q0 = qt * kBQ;
+    if (q0 >= Lq) return;
+    const int hk = h / (a.Hq / a.Hkv);
+    const int kend = a.causal ? min(Lk, q0 + kBQ) : Lk;
+    const int ntiles = (kend + kBK - 1) / kBK;
+    const int n_main = (a.causal ? min(q0, Lk) : Lk) / kBK;
+
+    // ---- per-lane query state: row wq0 + n
+    const int wq0 = q0 + wave * 32;
+    const bool live = wq0 < Lq;
+    const int64_t qhead = (int64_t)b * a.Hq + h;
+    const int qrow = wq0 + n;
+    v4i qf[NCB];
+    float qscale = 0.f;
+    if (live) {
+        const int8_t* q8row = a.q8 + (qhead * a.nq_pad + qrow) * DP;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) qf[cb] = *reinterpret_cast<const v4i*>(q8row + cb * 32 + hh * 16);
+        qscale = a.qs[qhead * (a.nq_pad >> a.gq_shift) + (qrow >> a.gq_shift)];
+    } else {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) qf[cb] = v4i{0, 0, 0, 0};
+    }
+    const float cq = (qscale * a.sm_scale) * kLog2e;
+
+    const int64_t khead = (int64_t)b * a.Hkv + hk;
+    const int8_t* kbase = a.k8 + khead * a.nk_pad * DP;
+    const float* ksbase = a.ks + khead * (a.nk_pad >> a.gk_shift);
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vt) + khead * DP * a.nk_pad;
+    const int64_t vrow_stride = a.nk_pad;
+    const bool ks16 = a.gk_shift == 4;
+
+    v16f o[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[cb][i] = 0.f;
+    v4f ls = v4f{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY, m_prev;
+    v16i biasv;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) biasv[i] = kAccBiasBits;
+    Ones<PV> ones;
+    make_ones<PV>(ones, rowsum_parity(lane));
+
+    auto stage_of = [&](int t) { return smem + (t % NST) * C::STAGE; };
+    auto ks_of = [&](const uint8_t* st, float (&ksv)[4]) {
+        const v4f k4 = *reinterpret_cast<const v4f*>(st + C::SC_OFF + wave * 256);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) ksv[g] = k4[g];
+    };
+    const TileCopy<DP, PV, NW> copier{kbase, vbase, vrow_stride, ksbase, ks16, wave, lane};
+    auto issue = [&](int t) {
+        if (t < ntiles) copier.issue_all(stage_of(t), t);
+    };
+    auto step_end = [&](int t) {
+        if (t + AHEAD < ntiles) wait_vmcnt<LPT * (AHEAD - 2)>();
+        else wait_vmcnt<0>();
+        block_sync();
+    };
+
+#pragma unroll
+    for (int u = 0; u < AHEAD; ++u) issue(u);
+    if (ntiles >= AHEAD) wait_vmcnt<LPT * (AHEAD - 2)>();
+    else wait_vmcnt<0>();
+    block_sync();
+
+    constexpr int NQK = 2 * NCB;
+    constexpr int NPV = NCB;
+    constexpr int NRS = 1;
+    constexpr int NDMA = C::NI + 1;
+    v16i S[2][2];
+    PHalf<PV> P;
+    phalf_zero<PV>(P);                                  // P.V for "tile -1" adds exact zeros
+    v4i kf[2][NCB];
+    float ksv[4];
+    VA<DP, PV> va;
+    if (n_main > 0 && live) {
+        load_kfrag<DP>(stage_of(0), n, hh, kf);
+        ks_of(stage_of(0), ksv);
+        load_va<DP, PV>(stage_of(0) + C::KT_BYTES, n, hh, va);
+        qk_half<DP>(kf, qf, biasv, S[0]);
+    }
+    // The loop body is written for an even/odd pair of tiles so that the two
+    // score buffers keep fixed registers.
+    auto step = [&](int t, v16i (&Sc)[2], v16i (&Sn)[2]) {
+        const int tc = min(t + AHEAD, ntiles - 1);
+        uint8_t* st_copy = stage_of(t + AHEAD);
+        if (live) {
+            const uint8_t* st = stage_of(t);
+            const uint8_t* st_next = stage_of(t + 1);
+            const uint8_t* st_prev = stage_of(t > 0 ? t - 1 : 0);
+            // H
+            SoftmaxPieces<PV> sp;
+            interleave<NPV + NRS, 4>(
+                [&](auto kc) {
+                    constexpr int k = decltype(kc)::value;
+                    if constexpr (k < NPV) pv8_job<DP, k>(va, P, o);
+                    else rs_job<PV, 0>(P, ones, ls);
+                    // K of tile t+1, channel blocks 0-1 (the rest follow in E); with
+                    // Dp = 128 the upper half of V^T (tile t-1) arrives here too
+                    if constexpr (k == 0) {
+                        load_kfrag_cb<DP>(st_next, n, hh, 0, kf);
+                        load_kfrag_cb<DP>(st_next, n, hh, 1, kf);
+                    }
+                    if constexpr (NCB == 4 && k == 1) {
+                        load_va_cb<DP>(st_prev + C::KT_BYTES, n, hh, 2, va);
+                        load_va_cb<DP>(st_prev + C::KT_BYTES, n, hh, 3, va);
+                    }
+                },
+                [&](auto hc) { sp.template head<decltype(hc)::value>(Sc, ksv, cq, m_ref, m_prev); });
+            if (__any(sp.raise)) rescale_half<DP>(m_ref, m_prev, o, ls);
+            // E
+            interleave<NQK, SoftmaxPieces<PV>::NPIECE>(
+                [&](auto kc) {
+                    constexpr int k = decltype(kc)::value;
+                    constexpr int cb = k >> 1, kb = k & 1;
+                    Sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[cb], cb == 0 ? biasv : Sn[kb], 0, 0,
+                                                                   0);
+                    if constexpr (k == 0) {                                            // V of tile t
+                        load_va_cb<DP>(st + C::KT_BYTES, n, hh, 0, va);
+                        load_va_cb<DP>(st + C::KT_BYTES, n, hh, 1, va);
+                    }
+                    if constexpr (NCB == 4 && (k == 2 || k == 4)) load_kfrag_cb<DP>(st_next, n, hh, k / 2 + 1, kf);
+                    if constexpr (k >= 1 && k - 1 < NDMA) copier.template issue<k - 1>(st_copy, tc);
+                    if constexpr (k == NQK - 1) ks_of(st_next, ksv);                     // K scales of tile t+1
+                },
+                [&](auto ec) { sp.template piece<decltype(ec)::value>(Sc, P); });
+            keep_here<PV>(P);
+        } else {
+            copier.issue_all(st_copy, tc);
+        }
+        wait_vmcnt<LPT * (AHEAD - 2)>();
+        block_sync();
+    };
+    int t = 0;
+    for (; t + 1 < n_main; t += 2) {
+        step(t, S[0], S[1]);
+        step(t + 1, S[1], S[0]);
+    }
+    if (t < n_main) {
+        step(t, S[0], S[1]);
+        ++t;
+    }
+    if (live && n_main > 0) {                           // P.V of the last pipelined tile
+        if constexpr (NCB == 4) {                       // the upper half of its V^T is loaded in H, which has no next step
+            load_va_cb<DP>(stage_of(n_main - 1) + C::KT_BYTES, n, hh, 2, va);
+            load_va_cb<DP>(stage_of(n_main - 1) + C::KT_BYTES, n, hh, 3, va);
+        }
+        pv8_all<DP>(va, P, ones, o, ls);
+    }
+    wait_vmcnt<0>();
+
+    // ---- remaining tiles (a ragged end, the causal diagonal): one at a time
+    for (; t < ntiles; ++t) {
+        issue(t + AHEAD);
+        const int k0 = t * kBK;
+        if (live && (!a.causal || k0 <= wq0 + 31)) {
+            const uint8_t* st = stage_of(t);
+            ks_of(st, ksv);
+            load_kfrag<DP>(st, n, hh, kf);
+            v16i Sm[2];
+                qk_half<DP>(kf, qf, biasv, Sm);
+            const bool need_mask = (k0 + kBK > Lk) || (a.causal && k0 + kBK - 1 > wq0);
+            PHalf<PV> Pm;
+            bool raised;
+            if (need_mask)
+                raised = softmax_half<PV, true>(Sm, ksv, cq, m_ref, m_prev, Pm, k0, Lk, a.causal, qrow, hh);
+            else
+                raised = softmax_half<PV, false>(Sm, ksv, cq, m_ref, m_prev, Pm, k0, Lk, a.causal, qrow, hh);
+            if (__any(raised)) rescale_half<DP>(m_ref, m_prev, o, ls);
+            VA<DP, PV> vam;
+            load_va<DP, PV>(st + C::KT_BYTES, n, hh, vam);
+            pv8_all<DP>(vam, Pm, ones, o, ls);
+        }
+        step_end(t);
+    }
+    if (!live) return;
+
+    // ---- epilogue: normalise, add back V's mean, write in the caller's layout
+    const float* vsc = a.vs + khead * DP;
+    const float* vmu = a.vmean ? a.vmean + khead * DP : nullptr;
+    const float l_tot = ls[0];
+    const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (qrow < Lq) {
+        uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) +
+                         (a.cu_q ? (int64_t)(qoff + qrow) * a.on + (int64_t)h * a.oh
+                                 : (int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)qrow * a.on);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int c0 = cb * 32 + 8 * r4 + 4 * hh;
+                if (c0 >= a.d) continue;
+                uint16_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int c = c0 + e;
+                    float val = o[cb][4 * r4 + e] * (vsc[c] * inv_l);
+                    if (vmu) val += vmu[c];
+                    hv[e] = Half<OUT_BF16>::from_f(val);
+                }
+                if (a.out_vec4 && c0 + 3 < a.d) {
+                    uint2 w;
+                    w.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+                    w.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+                    *reinterpret_cast<uint2*>(orow + c0) = w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (c0 + e < a.d) orow[c0 + e] = hv[e];
+                }
+            }
+    }
+    if (a.lse) {
+        constexpr float p_log2_scale = kLog2_448 - (float)kTau;
+        float part = 0.f;
+        if (a.kmean) {
+            const float* km = a.kmean + khead * DP;
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int code = (int)(int8_t)((qf[cb][e >> 2] >> (8 * (e & 3))) & 0xff);
+                    part += (float)code * km[cb * 32 + hh * 16 + e];
+                }
+        }
+        const float dot = swap_half_sum(part);
+        if (hh == 0 && qrow < Lq) {
+            const float corr = a.kmean ? a.sm_scale * qscale * dot : 0.f;
+            const float lse = (m_ref + __log2f(l_tot) - p_log2_scale) * kLn2 + corr;
+            const int64_t li = a.lse_varlen ? (int64_t)h * a.total_q + qoff + qrow : qhead * a.Nq + qrow;
+            a.lse[li] = lse;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Exact int32 scores from the same K staging and QK^T fragment code, for
 // tests.  One workgroup covers kDbgBQ query rows (32 per wavefront).
 constexpr int kDbgBQ = 128;
@@ -938,8 +1254,13 @@ __global__ __launch_bounds__(kThreads) void qk_scores_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 template <int DP, int PV>
 static void attn_dispatch_out(const AttnArgs& a, bool out_bf16, hipStream_t s) {
-    if (out_bf16) attn_fwd_kernel<DP, PV, true><<<a.num_wg, kThreads, 0, s>>>(a);
-    else attn_fwd_kernel<DP, PV, false><<<a.num_wg, kThreads, 0, s>>>(a);
+    if constexpr (PV == 0) {
+        if (out_bf16) attn8_fwd_kernel<DP, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+        else attn8_fwd_kernel<DP, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+    } else {
+        if (out_bf16) attn_fwd_kernel<DP, PV, true><<<a.num_wg, kThreads, 0, s>>>(a);
+        else attn_fwd_kernel<DP, PV, false><<<a.num_wg, kThreads, 0, s>>>(a);
+    }
 }
 
 hipError_t launch_attn(const AttnArgs& a_in, int dp, int pv, bool out_bf16, hipStream_t s) {
