@@ -63,16 +63,17 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int DP, int PV, int NW = 4>
+template <int DP, int PV, int NW = 4, int NR = NW>
 struct AttnCfg {
     static constexpr int NCB = DP / 32;                 // 32-channel blocks
     static constexpr int KT_BYTES = kBK * DP;           // K tile: 64 keys x Dp int8
     static constexpr int VE = PV == 0 ? 1 : 2;          // V element bytes
     static constexpr int VROW = kBK * VE;               // V^T tile row (one channel) bytes
     static constexpr int VT_BYTES = DP * VROW;
-    static constexpr int SC_OFF = KT_BYTES + VT_BYTES;  // the tile's K scales, one 256-byte slot per wavefront
-    static constexpr int STAGE = KT_BYTES + VT_BYTES + NW * 256;
-    static constexpr int NI = (KT_BYTES + VT_BYTES) / (16 * 64 * NW);   // DMA instructions per wavefront
+    static constexpr int SC_OFF = KT_BYTES + VT_BYTES;  // the tile's K scales, one 256-byte slot per reading wavefront
+    static constexpr int STAGE = KT_BYTES + VT_BYTES + NR * 256;
+    static constexpr int NI = (KT_BYTES + VT_BYTES) / (16 * 64 * NW);   // tile DMA instructions per copying wavefront
+    static constexpr int NSC = NR / NW;                 // scale copies per copying wavefront
     static_assert(NI * 16 * 64 * NW == KT_BYTES + VT_BYTES, "tile must fill whole copy rounds");
 };
 
@@ -80,18 +81,18 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 // Direct global -> LDS copy of one key tile into one stage of the ring, as
-// NI + 1 instructions per wavefront that the key loop can place one by one.
-// Instruction i < NI of wavefront w (of NW) fills the 1 KB of granules
-// [(NW*i + w) * 64, +64); lane L writes granule (NW*i + w) * 64 + L.  The
-// granule at (row, physical chunk c) receives logical chunk swz(row, c) (the
-// swizzle is an involution), so readers address logical chunk c at
-// swz(row, c).  Instruction NI copies the tile's K scales into the
-// wavefront's own 256-byte slot, 4 bytes per lane: lane L holds group L % 4
-// (4 groups of 16 keys), or the one group of 64 keys; the softmax reads the
-// first 16 bytes.  All lanes take part so that no branch splits the loop
+// NI + NSC instructions per copying wavefront that the key loop can place one
+// by one.  Instruction i < NI of copying wavefront w (of NW) fills the 1 KB of
+// granules [(NW*i + w) * 64, +64); lane L writes granule (NW*i + w) * 64 + L.
+// The granule at (row, physical chunk c) receives logical chunk swz(row, c)
+// (the swizzle is an involution), so readers address logical chunk c at
+// swz(row, c).  Instruction NI + j copies the tile's K scales into the 256-byte
+// slot of reading wavefront w + NW*j, 4 bytes per lane: lane L holds group
+// L % 4 (4 groups of 16 keys), or the one group of 64 keys; the softmax reads
+// the first 16 bytes.  All lanes take part so that no branch splits the loop
 // body.  Whether a wavefront's granules belong to K or to V^T depends only on
 // the instruction and the wavefront, so the choice is wave-uniform.
-template <int DP, int PV, int NW = 4>
+template <int DP, int PV, int NW = 4, int NR = NW>
 struct TileCopy {
     const int8_t* kbase;
     const uint8_t* vbase;
@@ -102,7 +103,7 @@ struct TileCopy {
 
     template <int I>
     __device__ __forceinline__ void issue(uint8_t* stage, int t) const {
-        using C = AttnCfg<DP, PV, NW>;
+        using C = AttnCfg<DP, PV, NW, NR>;
         constexpr int KG = C::KT_BYTES / 16, KCPR = DP / 16, VCPR = C::VROW / 16;
         static_assert(KG % 64 == 0, "K tile must fill whole wavefront chunks");
         if constexpr (I < C::NI) {
@@ -123,13 +124,87 @@ struct TileCopy {
             __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + gbase * 16), 16, 0, 0);
         } else {
             const float* src = ks16 ? ksbase + 4 * t + (lane & 3) : ksbase + t;
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + C::SC_OFF + wave * 256), 4, 0, 0);
+            const int slot = wave + NW * (I - C::NI);
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + C::SC_OFF + slot * 256), 4, 0, 0);
         }
     }
     __device__ __forceinline__ void issue_all(uint8_t* stage, int t) const {
-        static_for<0, AttnCfg<DP, PV, NW>::NI + 1>([&](auto i) { issue<decltype(i)::value>(stage, t); });
+        using C = AttnCfg<DP, PV, NW, NR>;
+        static_for<0, C::NI + C::NSC>([&](auto i) { issue<decltype(i)::value>(stage, t); });
     }
 };
+
+// The same copy through buffer resources: every source address is a 32-bit
+// per-lane offset (one VGPR per instruction, fixed for the whole key loop)
+// plus a wave-uniform offset for the tile, and the hardware clamps each load
+// to its resource (bytes past the end read as zero).
+#if __HIP_DEVICE_COMPILE__
+template <int DP, int PV, int NW, int NR>
+struct TileCopyBuf {
+    using C = AttnCfg<DP, PV, NW, NR>;
+    __amdgpu_buffer_rsrc_t rk, rv, rs;
+    uint32_t voff[C::NI + 1];
+    int wave;
+    bool ks16;
+
+    __device__ __forceinline__ TileCopyBuf(const int8_t* kbase, const uint8_t* vbase, uint32_t vrow_stride,
+                                           const float* ksbase, uint32_t k_bytes, uint32_t v_bytes,
+                                           uint32_t s_bytes, bool ks16_, int wave_, int lane)
+        : wave(wave_), ks16(ks16_) {
+        constexpr int KG = C::KT_BYTES / 16, KCPR = DP / 16, VCPR = C::VROW / 16;
+        rk = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, (int)k_bytes, 0x00020000);
+        rv = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, (int)v_bytes, 0x00020000);
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)ksbase, (short)0, (int)s_bytes, 0x00020000);
+#pragma unroll
+        for (int i = 0; i < C::NI; ++i) {
+            const int g = (NW * i + wave) * 64 + lane;
+            if (g < KG) {
+                const int row = g / KCPR, ch = swz<DP>(row, g % KCPR);
+                voff[i] = (uint32_t)(row * DP + ch * 16);
+            } else {
+                const int gv = g - KG, row = gv / VCPR, ch = swz<C::VROW>(row, gv % VCPR);
+                voff[i] = (uint32_t)row * vrow_stride + (uint32_t)(ch * 16);
+            }
+        }
+        voff[C::NI] = ks16 ? (uint32_t)(lane & 3) * 4u : 0u;
+    }
+
+    template <int I>
+    __device__ __forceinline__ void issue(uint8_t* stage, int t) const {
+        constexpr int KG = C::KT_BYTES / 16;
+        if constexpr (I < C::NI) {
+            const int gbase = (NW * I + wave) * 64;
+            lds_ptr_t dst = (lds_ptr_t)(stage + gbase * 16);
+            if constexpr ((I + 1) * NW * 64 <= KG) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, voff[I], (uint32_t)t * C::KT_BYTES, 0, 0);
+            } else if constexpr (I * NW * 64 >= KG) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, voff[I], (uint32_t)t * C::VROW, 0, 0);
+            } else {
+                if (gbase < KG) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, voff[I], (uint32_t)t * C::KT_BYTES, 0, 0);
+                else __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, voff[I], (uint32_t)t * C::VROW, 0, 0);
+            }
+        } else {
+            const int slot = wave + NW * (I - C::NI);
+            lds_ptr_t dst = (lds_ptr_t)(stage + C::SC_OFF + slot * 256);
+            const uint32_t so = ks16 ? (uint32_t)t * 16u : (uint32_t)t * 4u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff[C::NI], so, 0, 0);
+        }
+    }
+    __device__ __forceinline__ void issue_all(uint8_t* stage, int t) const {
+        static_for<0, C::NI + C::NSC>([&](auto i) { issue<decltype(i)::value>(stage, t); });
+    }
+};
+#else
+// Host pass: the buffer builtins exist only for the gfx950 target; this
+// interface-only stand-in lets the kernel body parse.
+template <int DP, int PV, int NW, int NR>
+struct TileCopyBuf {
+    __device__ TileCopyBuf(const int8_t*, const uint8_t*, uint32_t, const float*, uint32_t, uint32_t, uint32_t, bool,
+                           int, int) {}
+    template <int I> __device__ void issue(uint8_t*, int) const {}
+    __device__ void issue_all(uint8_t*, int) const {}
+};
+#endif
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
@@ -180,6 +255,13 @@ __device__ __forceinline__ void load_kfrag_cb(const uint8_t* ks, int n, int hh, 
         const int row = kb * 32 + n;
         kf[kb][cb] = *reinterpret_cast<const v4i*>(ks + row * DP + swz<DP>(row, cb * 2 + hh) * 16);
     }
+}
+
+// One K fragment: keys 32*kb .. +31, channel block cb.
+template <int DP>
+__device__ __forceinline__ void load_kfrag_kb(const uint8_t* ks, int n, int hh, int kb, int cb, v4i (&kf)[2][DP / 32]) {
+    const int row = kb * 32 + n;
+    kf[kb][cb] = *reinterpret_cast<const v4i*>(ks + row * DP + swz<DP>(row, cb * 2 + hh) * 16);
 }
 
 // S^T of one row block: S[kb][i] = bias + S(query n of the block,
@@ -469,15 +551,20 @@ struct SoftmaxPieces {
     template <int H>
     __device__ __forceinline__ void head(const v16i (&S)[2], const float (&ksv)[4], float cq, float& m_ref,
                                          float& m_prev) {
+        head<H>(S[0], S[1], ksv, cq, m_ref, m_prev);
+    }
+    template <int H>
+    __device__ __forceinline__ void head(const v16i& S0, const v16i& S1, const float (&ksv)[4], float cq,
+                                         float& m_ref, float& m_prev) {
         if constexpr (H == 0) {
 #pragma unroll
             for (int g = 0; g < 4; ++g) f[g] = ksv[g] * cq;
-            group_max(S, 0);
+            group_max(S0, 0);
         } else if constexpr (H == 1) {
-            group_max(S, 1);
-            group_max(S, 2);
+            group_max(S0, 1);
+            group_max(S1, 2);
         } else if constexpr (H == 2) {
-            group_max(S, 3);
+            group_max(S1, 3);
             smax = -INFINITY;
 #pragma unroll
             for (int g = 0; g < 4; ++g) smax = fmaxf(smax, (bits_f(mi[g]) - kAccBias) * f[g]);
@@ -491,6 +578,32 @@ struct SoftmaxPieces {
             for (int g = 0; g < 4; ++g) cg[g] = __builtin_fmaf(-kAccBias, f[g], nb);
         }
     }
+    // The same head split for a loop that computes P speculatively with the
+    // reference maximum it has before the tile: prep() and gmax() need only
+    // the scores, spec() gives the exponent offsets for the current maximum,
+    // decide() the raise decision and the new maximum (same roundings as
+    // head<>()).  A row that does not raise keeps its maximum, so its
+    // speculative P is exact; a wavefront with a raising row redoes P.
+    __device__ __forceinline__ void prep(const float (&ksv)[4], float cq) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) f[g] = ksv[g] * cq;
+    }
+    __device__ __forceinline__ void gmax(const v16i& Sk, int g) { group_max(Sk, g); }
+    __device__ __forceinline__ void spec(float m_ref) {
+        const float nb = p_log2_scale - m_ref;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) cg[g] = __builtin_fmaf(-kAccBias, f[g], nb);
+    }
+    __device__ __forceinline__ void decide(float& m_ref, float& m_prev) {
+        smax = -INFINITY;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) smax = fmaxf(smax, (bits_f(mi[g]) - kAccBias) * f[g]);
+        smax = swap_half_max(smax);
+        m_prev = m_ref;
+        raise = smax > m_ref + (float)kTau;
+        m_ref = raise ? smax : m_ref;
+    }
+
     // Keys 2E and 2E+1 of the lane's 32 become P in three stages, which the
     // loop skews over consecutive pieces (piece e: products of chunk e, exp2
     // of chunk e-1, conversion of chunk e-2), so that no instruction waits
@@ -500,10 +613,16 @@ struct SoftmaxPieces {
 
     template <int E>
     __device__ __forceinline__ void piece(const v16i (&S)[2], PHalf<PV>& P) {
+        piece<E>(S[0], S[1], P);
+    }
+    // Pieces 0-7 read only S0 and pieces 8-15 only S1.
+    template <int E>
+    __device__ __forceinline__ void piece(const v16i& S0, const v16i& S1, PHalf<PV>& P) {
         if constexpr (E < 16) {
             constexpr int kb = E >> 3, i0 = (2 * E) & 15, g = 2 * kb + (i0 >> 3);
-            xv[2 * E] = __builtin_fmaf(bits_f(S[kb][i0]), f[g], cg[g]);
-            xv[2 * E + 1] = __builtin_fmaf(bits_f(S[kb][i0 + 1]), f[g], cg[g]);
+            const v16i& Sk = kb == 0 ? S0 : S1;
+            xv[2 * E] = __builtin_fmaf(bits_f(Sk[i0]), f[g], cg[g]);
+            xv[2 * E + 1] = __builtin_fmaf(bits_f(Sk[i0 + 1]), f[g], cg[g]);
         }
         if constexpr (E >= 1 && E - 1 < 16) {
             pv[2 * E - 2] = __builtin_amdgcn_exp2f(xv[2 * E - 2]);
@@ -530,11 +649,11 @@ struct SoftmaxPieces {
     }
 
   private:
-    __device__ __forceinline__ void group_max(const v16i (&S)[2], int g) {
-        const int kb = g >> 1, i0 = (g & 1) * 8;
-        int m = S[kb][i0];
+    __device__ __forceinline__ void group_max(const v16i& Sk, int g) {
+        const int i0 = (g & 1) * 8;
+        int m = Sk[i0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) m = max(m, S[kb][i0 + i]);
+        for (int i = 1; i < 8; ++i) m = max(m, Sk[i0 + i]);
         mi[g] = m;
     }
 };
@@ -919,17 +1038,18 @@ constexpr int kThreads8 = 64 * kWaves8;
 
 template <int DP, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
-    constexpr int PV = 0, NW = kWaves8;
-    using C = AttnCfg<DP, PV, NW>;
+    constexpr int PV = 0, NW = kWaves8;                 // every wavefront copies its share
+    using C = AttnCfg<DP, PV, NW, NW>;
     constexpr int NCB = C::NCB;
     constexpr int AHEAD = 3;
     constexpr int NST = AHEAD + 2;
-    constexpr int LPT = C::NI + 1;
+    constexpr int LPT = C::NI + C::NSC;                 // copy instructions per copying wavefront per tile
     __shared__ __attribute__((aligned(16))) uint8_t smem[NST * C::STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, hh = lane >> 5;
+    const bool lead_wave = wave < kWaves8 / 2;          // wave-uniform: wavefronts 0-3 lead by half a step
 
     const int wg = xcd_remap(blockIdx.x, a.num_wg);
     int qt = wg % a.n_qtiles;
@@ -992,7 +1112,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) ksv[g] = k4[g];
     };
-    const TileCopy<DP, PV, NW> copier{kbase, vbase, vrow_stride, ksbase, ks16, wave, lane};
+    const TileCopyBuf<DP, PV, NW, NW> copier(kbase, vbase, (uint32_t)vrow_stride, ksbase,
+                                                  (uint32_t)a.nk_pad * DP, (uint32_t)a.nk_pad * DP,
+                                                  (uint32_t)(a.nk_pad >> a.gk_shift) * 4u, ks16, wave, lane);
     auto issue = [&](int t) {
         if (t < ntiles) copier.issue_all(stage_of(t), t);
     };
@@ -1011,8 +1133,24 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     constexpr int NQK = 2 * NCB;
     constexpr int NPV = NCB;
     constexpr int NRS = 1;
-    constexpr int NDMA = C::NI + 1;
-    v16i S[2][2];
+    constexpr int NDMA = LPT;
+    // Step t is two regions:
+    //   H(t): QK^T of tile t, then P.V of tile t-1 and the row sums, with the
+    //         group maxima of tile t between the P.V MFMAs, the copy of tile
+    //         t+3, and the K and V^T fragments of the next step (matrix-core
+    //         work);
+    //   E(t): P of tile t, computed with the reference maximum from before
+    //         the tile while the raise decision completes; if a row raises,
+    //         O is rescaled and P recomputed (VALU work).
+    // Wavefronts 4-7 run half a step behind wavefronts 0-3, so that on each
+    // SIMD one wavefront is in H while the other is in E; every half step
+    // ends with a workgroup barrier.  The ring of NST = AHEAD + 2 stages stays
+    // valid: each wavefront copies its share of tile t+3 in its H(t), into
+    // the stage of tile t-2, whose last reads (V^T fragments in H(t-2) of
+    // either group) precede the barrier before that H(t); and each wavefront
+    // waits for its share of tile t+2 before the barrier that ends its H(t),
+    // which precedes every read of tile t+2 (fragments in H(t+1)).
+    v16i S[2];
     PHalf<PV> P;
     phalf_zero<PV>(P);                                  // P.V for "tile -1" adds exact zeros
     v4i kf[2][NCB];
@@ -1022,76 +1160,86 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         load_kfrag<DP>(stage_of(0), n, hh, kf);
         ks_of(stage_of(0), ksv);
         load_va<DP, PV>(stage_of(0) + C::KT_BYTES, n, hh, va);
-        qk_half<DP>(kf, qf, biasv, S[0]);
     }
-    // The loop body is written for an even/odd pair of tiles so that the two
-    // score buffers keep fixed registers.
-    auto step = [&](int t, v16i (&Sc)[2], v16i (&Sn)[2]) {
+    constexpr int NH = NQK + NPV + NRS;                 // matrix-core jobs of H
+    static_assert(NPV + NRS >= 3, "room for the group maxima");
+    // u = t % NST as a compile-time constant: every LDS address of the step
+    // is a fixed offset from one base
+    auto regionH = [&](auto u, int t, SoftmaxPieces<PV>& sp) {
+        constexpr int U = decltype(u)::value;
         const int tc = min(t + AHEAD, ntiles - 1);
-        uint8_t* st_copy = stage_of(t + AHEAD);
+        uint8_t* st_copy = smem + ((U + AHEAD) % NST) * C::STAGE;
         if (live) {
-            const uint8_t* st = stage_of(t);
-            const uint8_t* st_next = stage_of(t + 1);
-            const uint8_t* st_prev = stage_of(t > 0 ? t - 1 : 0);
-            // H
-            SoftmaxPieces<PV> sp;
-            interleave<NPV + NRS, 4>(
-                [&](auto kc) {
-                    constexpr int k = decltype(kc)::value;
-                    if constexpr (k < NPV) pv8_job<DP, k>(va, P, o);
-                    else rs_job<PV, 0>(P, ones, ls);
-                    // K of tile t+1, channel blocks 0-1 (the rest follow in E); with
-                    // Dp = 128 the upper half of V^T (tile t-1) arrives here too
-                    if constexpr (k == 0) {
-                        load_kfrag_cb<DP>(st_next, n, hh, 0, kf);
-                        load_kfrag_cb<DP>(st_next, n, hh, 1, kf);
+            const uint8_t* st = smem + U * C::STAGE;
+            const uint8_t* st_next = smem + ((U + 1) % NST) * C::STAGE;
+            static_for<0, NH>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if constexpr (k < NQK) {
+                    constexpr int kb = k & 1, cb = k >> 1;
+                    S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[cb], cb == 0 ? biasv : S[kb], 0, 0, 0);
+                } else if constexpr (k < NQK + NPV) {
+                    pv8_job<DP, k - NQK>(va, P, o);
+                } else {
+                    rs_job<PV, 0>(P, ones, ls);
+                }
+                if constexpr (k >= 1 && k - 1 < NDMA) copier.template issue<k - 1>(st_copy, tc);
+                if constexpr (k == 0) sp.prep(ksv, cq);
+                if constexpr (k == NQK - 1) {           // K of tile t+1 (kf is free once the last QK^T MFMA issued)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        load_kfrag_kb<DP>(st_next, n, hh, 0, cb, kf);
+                        load_kfrag_kb<DP>(st_next, n, hh, 1, cb, kf);
                     }
-                    if constexpr (NCB == 4 && k == 1) {
-                        load_va_cb<DP>(st_prev + C::KT_BYTES, n, hh, 2, va);
-                        load_va_cb<DP>(st_prev + C::KT_BYTES, n, hh, 3, va);
-                    }
-                },
-                [&](auto hc) { sp.template head<decltype(hc)::value>(Sc, ksv, cq, m_ref, m_prev); });
-            if (__any(sp.raise)) rescale_half<DP>(m_ref, m_prev, o, ls);
-            // E
-            interleave<NQK, SoftmaxPieces<PV>::NPIECE>(
-                [&](auto kc) {
-                    constexpr int k = decltype(kc)::value;
-                    constexpr int cb = k >> 1, kb = k & 1;
-                    Sn[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[cb], cb == 0 ? biasv : Sn[kb], 0, 0,
-                                                                   0);
-                    if constexpr (k == 0) {                                            // V of tile t
-                        load_va_cb<DP>(st + C::KT_BYTES, n, hh, 0, va);
-                        load_va_cb<DP>(st + C::KT_BYTES, n, hh, 1, va);
-                    }
-                    if constexpr (NCB == 4 && (k == 2 || k == 4)) load_kfrag_cb<DP>(st_next, n, hh, k / 2 + 1, kf);
-                    if constexpr (k >= 1 && k - 1 < NDMA) copier.template issue<k - 1>(st_copy, tc);
-                    if constexpr (k == NQK - 1) ks_of(st_next, ksv);                     // K scales of tile t+1
-                },
-                [&](auto ec) { sp.template piece<decltype(ec)::value>(Sc, P); });
-            keep_here<PV>(P);
+                }
+                // group maxima of tile t, one or two per P.V MFMA
+                if constexpr (k == NQK + 1) { sp.gmax(S[0], 0); sp.gmax(S[0], 1); }
+                if constexpr (k == NQK + 2) { sp.gmax(S[1], 2); sp.gmax(S[1], 3); }
+                if constexpr (k == NH - 1) {            // V of tile t (va is free once the last P.V MFMA issued)
+                    ks_of(st_next, ksv);
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) load_va_cb<DP>(st + C::KT_BYTES, n, hh, cb, va);
+                }
+                sched_fence();
+            });
         } else {
             copier.issue_all(st_copy, tc);
         }
-        wait_vmcnt<LPT * (AHEAD - 2)>();
+        wait_vmcnt<LPT * (AHEAD - 2)>();                // own share of tile t+2 has landed
+    };
+    auto regionE = [&](SoftmaxPieces<PV>& sp) {
+        if (!live) return;
+        sp.spec(m_ref);
+        static_for<0, SoftmaxPieces<PV>::NPIECE>([&](auto ec) {
+            constexpr int e = decltype(ec)::value;
+            sp.template piece<e>(S, P);
+            if constexpr (e == 1) sp.decide(m_ref, m_prev);
+        });
+        if (__any(sp.raise)) {                          // rare: some row raised its maximum
+            rescale_half<DP>(m_ref, m_prev, o, ls);
+            sp.spec(m_ref);
+            static_for<0, SoftmaxPieces<PV>::NPIECE>([&](auto ec) { sp.template piece<decltype(ec)::value>(S, P); });
+        }
+        keep_here<PV>(P);
+    };
+    // wavefronts 4-7: one barrier first (paired with the end of H(0) of
+    // wavefronts 0-3) and none after their last E, so both groups pass the
+    // same number of barriers
+    auto step = [&](auto u, int t) {
+        SoftmaxPieces<PV> sp;
+        regionH(u, t, sp);
         block_sync();
+        regionE(sp);
+        if (lead_wave || t + 1 < n_main) block_sync();
     };
     int t = 0;
-    for (; t + 1 < n_main; t += 2) {
-        step(t, S[0], S[1]);
-        step(t + 1, S[1], S[0]);
+    if (!lead_wave && n_main > 0) block_sync();
+    for (; t < n_main; t += NST) {                      // stage slots 0 .. NST-1 in turn
+        static_for<0, NST>([&](auto u) {
+            if (t + decltype(u)::value < n_main) step(u, t + decltype(u)::value);
+        });
     }
-    if (t < n_main) {
-        step(t, S[0], S[1]);
-        ++t;
-    }
-    if (live && n_main > 0) {                           // P.V of the last pipelined tile
-        if constexpr (NCB == 4) {                       // the upper half of its V^T is loaded in H, which has no next step
-            load_va_cb<DP>(stage_of(n_main - 1) + C::KT_BYTES, n, hh, 2, va);
-            load_va_cb<DP>(stage_of(n_main - 1) + C::KT_BYTES, n, hh, 3, va);
-        }
-        pv8_all<DP>(va, P, ones, o, ls);
-    }
+    t = n_main;
+    if (live && n_main > 0) pv8_all<DP>(va, P, ones, o, ls);   // P.V of the last pipelined tile
     wait_vmcnt<0>();
 
     // ---- remaining tiles (a ragged end, the causal diagonal): one at a time
