@@ -2,8 +2,8 @@
 """Throughput of the quantized attention forward on one MI355X.
 
 One step = one pass of the whole hot path over one batch already resident in
-HBM: sage_quant_qk (K mean, INT8 Q/K), sage_quant_v (V statistics, FP8 V^T)
-and sage_attn_fwd (INT8 QK^T, online softmax, FP8 P.V).  The default workload
+HBM: sage_quant_qkv (K mean and V statistics, INT8 Q/K, FP8 V^T, in two
+launches) and sage_attn_fwd (INT8 QK^T, online softmax, FP8 P.V).  The default workload
 is B=2, H=8, N=4096, head_dim=128, fp16, per_warp INT8 Q/K, FP8 V.
 
 Prints ONE JSON line.  `value` is whole-step TOPS (4*B*H*Nq*Nk*d per step,
@@ -112,15 +112,15 @@ def main() -> int:
     dev = torch.device("cuda:0")
     q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
     nk = w.Nk
-    ws = torch.empty(sage.workspace_bytes(w.B, w.Hkv, nk, w.d), dtype=torch.uint8, device=dev)
+    ws_k = torch.empty(sage.workspace_bytes(w.B, w.Hkv, nk, w.d), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty_like(ws_k)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        qk = sage.sage_quant_qk(q, k, tensor_layout=w.layout, qk_quant_gran=w.gran, smooth_k=w.smooth_k,
-                                workspace=ws)
-        qv = sage.sage_quant_v(v, tensor_layout=w.layout, v_dtype=w.v_dtype, smooth_v=w.smooth_v, workspace=ws)
+        qk, qv = sage.sage_quant_qkv(q, k, v, tensor_layout=w.layout, qk_quant_gran=w.gran, smooth_k=w.smooth_k,
+                                     v_dtype=w.v_dtype, smooth_v=w.smooth_v, workspace_k=ws_k, workspace_v=ws_v)
         if ev is not None:
             ev[1].record(stream)
         out = sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, is_causal=w.causal,

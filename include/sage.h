@@ -162,6 +162,18 @@ typedef struct sage_quant_v_params {
 int sage_quant_v(const sage_quant_v_params* p, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * sage_quant_qkv: sage_quant_qk and sage_quant_v in one call, with the same
+ * results bit for bit, in two kernel launches instead of four (the Q tiles
+ * and the K and V statistics share one launch, the K and V tiles the next).
+ * The two parameter blocks are those of the separate calls; they must agree
+ * on dtype, B, Hkv, Nk, d and cu_seqlens_k, and when both need a workspace
+ * the two workspaces must not overlap.
+ * Errors: as the separate calls, plus SAGE_EINVAL for a disagreement or
+ * overlapping workspaces; nothing is launched then.
+ * ------------------------------------------------------------------------- */
+int sage_quant_qkv(const sage_quant_qk_params* qk, const sage_quant_v_params* v, void* stream);
+
+/* ---------------------------------------------------------------------------
  * sage_attn_fwd: the fused attention forward on quantized operands.
  * Deployment guide sec. 1 (INT8 QK^T, FP8/FP16 P.V with fp32 accumulation,
  * FP16/BF16 output), sec. 4.1 (tensor_layout, is_causal, sm_scale default

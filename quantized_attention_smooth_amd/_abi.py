@@ -62,7 +62,7 @@ class AttnVarlenParams(ctypes.Structure):
     _fields_ = [("base", AttnParams), ("cu_seqlens_q", VP), ("cu_seqlens_k", VP), ("total_q", I)]
 
 
-EXPORTS = ["sage_quant_qk", "sage_quant_workspace_size", "sage_quant_v", "sage_attn_fwd",
+EXPORTS = ["sage_quant_qk", "sage_quant_workspace_size", "sage_quant_v", "sage_quant_qkv", "sage_attn_fwd",
            "sage_attn_varlen_fwd", "sage_debug_qk_scores", "sage_last_error", "sage_version"]
 
 _lib = None
@@ -85,6 +85,8 @@ def load(path: str = LIB_PATH):
     L.sage_quant_qk.restype = I
     L.sage_quant_v.argtypes = [ctypes.POINTER(QuantVParams), VP]
     L.sage_quant_v.restype = I
+    L.sage_quant_qkv.argtypes = [ctypes.POINTER(QuantQKParams), ctypes.POINTER(QuantVParams), VP]
+    L.sage_quant_qkv.restype = I
     L.sage_attn_fwd.argtypes = [ctypes.POINTER(AttnParams), VP]
     L.sage_attn_fwd.restype = I
     L.sage_attn_varlen_fwd.argtypes = [ctypes.POINTER(AttnVarlenParams), VP]

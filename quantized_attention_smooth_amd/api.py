@@ -108,12 +108,8 @@ def workspace_bytes(B: int, H: int, N: int, d: int) -> int:
     return int(A.load().sage_quant_workspace_size(B, H, N, d))
 
 
-def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, *, tensor_layout: str = "HND",
-                  qk_quant_gran: str = "per_thread", smooth_k: bool = True,
-                  cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
-                  max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
-                  workspace: Optional[torch.Tensor] = None) -> QuantQK:
-    L = A.load()
+def _quant_qk_params(q: torch.Tensor, k: torch.Tensor, tensor_layout: str, qk_quant_gran: str, smooth_k: bool,
+                     cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, workspace):
     if qk_quant_gran not in _GRAN:
         raise ValueError(f"qk_quant_gran must be one of {sorted(_GRAN)}")
     if q.dtype != k.dtype or q.device != k.device:
@@ -143,14 +139,12 @@ def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, *, tensor_layout: str = "HND
     p.q8, p.q_scale, p.k8, p.k_scale, p.k_mean = _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(km)
     p.workspace = _ptr(workspace)
     p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    A.check(L.sage_quant_qk(ctypes.byref(p), _stream()))
-    return QuantQK(q8, qs, k8, ks, km, qk_quant_gran, gq.B, gq.H, gk.H, gq.N, gk.N, gq.d, q.dtype)
+    res = QuantQK(q8, qs, k8, ks, km, qk_quant_gran, gq.B, gq.H, gk.H, gq.N, gk.N, gq.d, q.dtype)
+    return p, res, workspace
 
 
-def sage_quant_v(v: torch.Tensor, *, tensor_layout: str = "HND", v_dtype: str = "fp8", smooth_v: bool = False,
-                 cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_k: Optional[int] = None,
-                 workspace: Optional[torch.Tensor] = None) -> QuantV:
-    L = A.load()
+def _quant_v_params(v: torch.Tensor, tensor_layout: str, v_dtype: str, smooth_v: bool, cu_seqlens_k, max_seqlen_k,
+                    workspace):
     if v_dtype not in ("fp8", "fp16"):
         raise ValueError("v_dtype must be 'fp8' or 'fp16' (the input's 16-bit type)")
     g = _geometry(v, tensor_layout, cu_seqlens_k, max_seqlen_k)
@@ -174,8 +168,46 @@ def sage_quant_v(v: torch.Tensor, *, tensor_layout: str = "HND", v_dtype: str = 
     p.vt, p.v_scale, p.v_mean = _ptr(vt), _ptr(vs), _ptr(vm)
     p.workspace = _ptr(workspace)
     p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return p, QuantV(vt, vs, vm, v_dtype), workspace
+
+
+def sage_quant_qk(q: torch.Tensor, k: torch.Tensor, *, tensor_layout: str = "HND",
+                  qk_quant_gran: str = "per_thread", smooth_k: bool = True,
+                  cu_seqlens_q: Optional[torch.Tensor] = None, cu_seqlens_k: Optional[torch.Tensor] = None,
+                  max_seqlen_q: Optional[int] = None, max_seqlen_k: Optional[int] = None,
+                  workspace: Optional[torch.Tensor] = None) -> QuantQK:
+    L = A.load()
+    p, res, _ = _quant_qk_params(q, k, tensor_layout, qk_quant_gran, smooth_k, cu_seqlens_q, cu_seqlens_k,
+                                 max_seqlen_q, max_seqlen_k, workspace)
+    A.check(L.sage_quant_qk(ctypes.byref(p), _stream()))
+    return res
+
+
+def sage_quant_v(v: torch.Tensor, *, tensor_layout: str = "HND", v_dtype: str = "fp8", smooth_v: bool = False,
+                 cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_k: Optional[int] = None,
+                 workspace: Optional[torch.Tensor] = None) -> QuantV:
+    L = A.load()
+    p, res, _ = _quant_v_params(v, tensor_layout, v_dtype, smooth_v, cu_seqlens_k, max_seqlen_k, workspace)
     A.check(L.sage_quant_v(ctypes.byref(p), _stream()))
-    return QuantV(vt, vs, vm, v_dtype)
+    return res
+
+
+def sage_quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, tensor_layout: str = "HND",
+                   qk_quant_gran: str = "per_thread", smooth_k: bool = True, v_dtype: str = "fp8",
+                   smooth_v: bool = False, cu_seqlens_q: Optional[torch.Tensor] = None,
+                   cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
+                   max_seqlen_k: Optional[int] = None, workspace_k: Optional[torch.Tensor] = None,
+                   workspace_v: Optional[torch.Tensor] = None):
+    """sage_quant_qk and sage_quant_v in one call (two kernel launches);
+    the K and V workspaces, when given, must be distinct buffers."""
+    L = A.load()
+    if v.dtype != k.dtype or v.device != k.device:
+        raise ValueError("k and v must share dtype and device")
+    pk, rqk, _ = _quant_qk_params(q, k, tensor_layout, qk_quant_gran, smooth_k, cu_seqlens_q, cu_seqlens_k,
+                                  max_seqlen_q, max_seqlen_k, workspace_k)
+    pv, rv, _ = _quant_v_params(v, tensor_layout, v_dtype, smooth_v, cu_seqlens_k, max_seqlen_k, workspace_v)
+    A.check(L.sage_quant_qkv(ctypes.byref(pk), ctypes.byref(pv), _stream()))
+    return rqk, rv
 
 
 def _attn_params(qk: QuantQK, qv: QuantV, out: torch.Tensor, lse: Optional[torch.Tensor], is_causal: bool,
@@ -263,8 +295,8 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
         raise ValueError("q, k, v must have the same dtype (deployment guide sec. 4.1)")
     if not (q.device == k.device == v.device) or q.device.type != "cuda":
         raise ValueError("q, k, v must be on the same GPU")
-    qk = sage_quant_qk(q, k, tensor_layout=tensor_layout, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k)
-    qv = sage_quant_v(v, tensor_layout=tensor_layout, v_dtype=v_dtype, smooth_v=smooth_v)
+    qk, qv = sage_quant_qkv(q, k, v, tensor_layout=tensor_layout, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k,
+                            v_dtype=v_dtype, smooth_v=smooth_v)
     return sage_attn_fwd(qk, qv, tensor_layout=tensor_layout, is_causal=is_causal, sm_scale=sm_scale,
                          return_lse=return_lse, pv_accum_dtype=pv_accum_dtype)
 
@@ -281,9 +313,9 @@ def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
         raise ValueError("q, k, v must have the same dtype")
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
-    qk = sage_quant_qk(q, k, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k, cu_seqlens_q=cu_seqlens_q,
-                       cu_seqlens_k=cu_seqlens_k, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
-    qv = sage_quant_v(v, v_dtype=v_dtype, smooth_v=smooth_v, cu_seqlens_k=cu_seqlens_k, max_seqlen_k=max_seqlen_k)
+    qk, qv = sage_quant_qkv(q, k, v, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k, v_dtype=v_dtype,
+                            smooth_v=smooth_v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+                            max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
     return sage_attn_varlen_fwd(qk, qv, cu_seqlens_q, cu_seqlens_k, q.shape[0], is_causal=is_causal,
                                 sm_scale=sm_scale, return_lse=return_lse, pv_accum_dtype=pv_accum_dtype)
 

@@ -72,27 +72,14 @@ __device__ __forceinline__ const uint16_t* row_ptr(const void* base, int64_t sb,
 }
 
 // ---------------------------------------------------------------------------
-// The statistics of one (sequence, head), reduced from its chunk partials by
-// the threads tid < DP of a workgroup (one channel each): the mean
-// fl32(fl64(exact sum) / N) and, with want_minmax, the FP8 V scale amax / 448
-// and its reciprocal (amax over |v - mean| if smooth, else over |v|).
+// The statistics of one channel of one (sequence, head) from its exact sum
+// and (with want_minmax) its minimum and maximum: the mean
+// fl32(fl64(exact sum) / N) and the FP8 V scale amax / 448 and its
+// reciprocal (amax over |v - mean| if smooth, else over |v|).
 template <bool BF16>
-__device__ __forceinline__ void channel_stats(const StatsArgs& a, int h, int b, int c, bool smooth, float& mean,
-                                              float& scale, float& inv) {
-    using Acc = typename std::conditional<BF16, double, long long>::type;
-    int n0, N;
-    seq_range(a.cu, b, a.N, n0, N);
-    const int64_t base = ((int64_t)b * a.H + h) * a.chunks * a.dp + c;
-    Acc s = 0;
-    float lo = INFINITY, hi = -INFINITY;
-#pragma unroll 8
-    for (int k = 0; k < a.chunks; ++k) {                // chunks <= kMaxChunks
-        s += reinterpret_cast<const Acc*>(a.part_sum)[base + (int64_t)k * a.dp];
-        if (a.want_minmax) {
-            lo = fminf(lo, a.part_min[base + (int64_t)k * a.dp]);
-            hi = fmaxf(hi, a.part_max[base + (int64_t)k * a.dp]);
-        }
-    }
+__device__ __forceinline__ void finish_stats(typename std::conditional<BF16, double, long long>::type s, float lo,
+                                             float hi, int N, bool want_minmax, bool smooth, float& mean,
+                                             float& scale, float& inv) {
     mean = 0.f;
     if (N > 0) {
         double s64;
@@ -102,7 +89,7 @@ __device__ __forceinline__ void channel_stats(const StatsArgs& a, int h, int b, 
     }
     scale = 0.f;
     inv = 0.f;
-    if (a.want_minmax && N > 0) {
+    if (want_minmax && N > 0) {
         // rounding is monotonic, so max_n |fl(v_n - mean)| is reached at the
         // column's max or min
         const float amax = smooth ? fmaxf(hi - mean, mean - lo) : fmaxf(hi, -lo);
@@ -175,14 +162,50 @@ __device__ __forceinline__ void stats_body(const StatsArgs& a, int chunk, int h,
 }
 
 // Channel statistics of one (sequence, head) for a tile workgroup: threads
-// tid < DP reduce their channel's partials (channel_stats), tile 0 stores the
-// caller's outputs, and mean / inverse scale land in LDS for all threads.
+// The whole workgroup reduces the (at most kMaxChunks) chunk partials of its
+// (sequence, head): kThreads / DP threads per channel, each with all its
+// loads in flight at once, then one exact combination per channel (integer
+// sums, or fp64 sums that are exact on these inputs, so the order does not
+// matter).  Tile 0 stores the caller's outputs; mean and inverse scale land
+// in LDS for all threads.
 template <bool BF16, int DP>
 __device__ __forceinline__ void tile_stats(const StatsArgs& a, int tile, int h, int b, float* s_mu, float* s_inv) {
-    const int tid = threadIdx.x;
+    using Acc = typename std::conditional<BF16, double, long long>::type;
+    constexpr int TPC = kThreads / DP;                  // threads per channel
+    constexpr int PER = kMaxChunks / TPC;               // chunk slots per thread
+    static_assert(PER * TPC == kMaxChunks, "chunk slots");
+    __shared__ Acc r_sum[kThreads];
+    __shared__ float r_lo[kThreads], r_hi[kThreads];
+    const int tid = threadIdx.x, c = tid % DP, part = tid / DP;
+    const int64_t base = ((int64_t)b * a.H + h) * a.chunks * a.dp + c;
+    Acc sum = 0;
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int k = part + TPC * i;
+        if (k < a.chunks) {
+            sum += reinterpret_cast<const Acc*>(a.part_sum)[base + (int64_t)k * a.dp];
+            if (a.want_minmax) {
+                lo = fminf(lo, a.part_min[base + (int64_t)k * a.dp]);
+                hi = fmaxf(hi, a.part_max[base + (int64_t)k * a.dp]);
+            }
+        }
+    }
+    r_sum[tid] = sum;
+    r_lo[tid] = lo;
+    r_hi[tid] = hi;
+    __syncthreads();
     if (tid < DP) {
+#pragma unroll
+        for (int j = 1; j < TPC; ++j) {
+            sum += r_sum[tid + j * DP];
+            lo = fminf(lo, r_lo[tid + j * DP]);
+            hi = fmaxf(hi, r_hi[tid + j * DP]);
+        }
+        int n0, N;
+        seq_range(a.cu, b, a.N, n0, N);
         float mean, sc, iv;
-        channel_stats<BF16>(a, h, b, tid, a.smooth, mean, sc, iv);
+        finish_stats<BF16>(sum, lo, hi, N, a.want_minmax, a.smooth, mean, sc, iv);
         const int64_t o = ((int64_t)b * a.H + h) * DP + tid;
         if (tile == 0) {
             if (a.out_mean) a.out_mean[o] = mean;
@@ -306,23 +329,28 @@ __global__ __launch_bounds__(kThreads) void v_stats_kernel(StatsArgs vs) {
 // reduces the channel means / FP8 scales of its (sequence, head) while its
 // loads are in flight (tile 0 stores v_scale and v_mean).
 template <bool BF16, int DP, bool FP8, bool VEC>
-__global__ __launch_bounds__(kThreads) void quant_v_kernel(QuantVArgs a, StatsArgs vs, int have_stats) {
-    constexpr int TPR = DP / 8;
-    constexpr int RPP = kThreads / TPR;
-    constexpr int PASSES = kPad / RPP;
+__device__ __forceinline__ void quant_v_body(const QuantVArgs& a, const StatsArgs& vs, int have_stats, int tile,
+                                             int h, int b) {
+    // Thread (g, cg) loads the 8 channels cg*8 .. +7 of KPG consecutive keys
+    // g*KPG .. +KPG-1 of the 128-key tile (every wavefront reads whole rows),
+    // so that each channel's codes of 4 consecutive keys, which sit next to
+    // each other in the permuted V^T order, leave as one LDS word.
+    constexpr int TPR = DP / 8;                         // threads per key row
+    constexpr int NG = kThreads / TPR;                  // key groups per tile
+    constexpr int KPG = kPad / NG;                      // consecutive keys per thread (8 or 4)
+    static_assert(KPG % 4 == 0, "whole 4-key groups per thread");
     constexpr int E = FP8 ? 1 : 2;                      // bytes per element
-    const int tiles = a.npad / kPad;
-    const int tile = blockIdx.x % tiles, h = (blockIdx.x / tiles) % a.H, b = blockIdx.x / tiles / a.H;
+    constexpr int ROWB = kPad * E;                      // bytes per channel row of the tile in LDS
     int n0, N;
     seq_range(a.cu, b, a.N, n0, N);
-    const int tid = threadIdx.x, cg = tid % TPR, rr = tid / TPR;
+    const int tid = threadIdx.x, cg = tid % TPR, g = tid / TPR;
     const int row0 = tile * kPad;
-    __shared__ __attribute__((aligned(16))) uint8_t sv[DP * kPad * E];
+    __shared__ __attribute__((aligned(16))) uint8_t sv[DP * ROWB];
     const int64_t hb = ((int64_t)b * a.H + h) * DP;
-    float v[PASSES][8];
+    float v[KPG][8];
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int n = row0 + p * RPP + rr;
+    for (int p = 0; p < KPG; ++p) {
+        const int n = row0 + g * KPG + p;
         if (n < N) {
             load8<BF16, VEC>(row_ptr(a.v, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d, v[p]);
         } else {
@@ -338,34 +366,137 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(QuantVArgs a, StatsAr
         mu[j] = (have_stats && vs.smooth) ? s_mu[cg * 8 + j] : 0.f;
         inv[j] = (have_stats && FP8) ? s_inv[cg * 8 + j] : 1.f;
     }
+    // 16-byte chunks of a channel row are XOR-swizzled by the channel group
+    // so that the 16 channel groups of a wavefront hit different banks
+    auto chunk_swz = [](int c) { return (c >> 3) & 7; };
 #pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int r = p * RPP + rr, n = row0 + r;
-        const int pos = (r & ~63) | v_perm_pos(r & 63);
+    for (int q4 = 0; q4 < KPG / 4; ++q4) {
+        const int kk = (g * KPG + 4 * q4);              // first of 4 consecutive keys (tile-relative)
+        const int pos = (kk & ~63) | v_perm_pos(kk & 63);   // their 4 consecutive positions start here
+        bool valid[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) valid[e] = row0 + kk + e < N;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float x = v[p][j] - mu[j];
             const int c = cg * 8 + j;
+            const int byte = pos * E;
+            uint8_t* dst = sv + c * ROWB + (((byte >> 4) ^ chunk_swz(c)) << 4) + (byte & 15);
+            float x[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = v[4 * q4 + e][j] - mu[j];
             if constexpr (FP8) {
-                float t = x * inv[j];
-                t = fminf(fmaxf(t, -448.f), 448.f);
-                const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(t, 0.f, 0, false);
-                sv[c * kPad + pos] = (n < N) ? (uint8_t)(pk & 0xff) : 0;
+                float tq[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float tt = fminf(fmaxf(x[e] * inv[j], -448.f), 448.f);
+                    tq[e] = valid[e] ? tt : 0.f;
+                }
+                int w = __builtin_amdgcn_cvt_pk_fp8_f32(tq[0], tq[1], 0, false);
+                w = __builtin_amdgcn_cvt_pk_fp8_f32(tq[2], tq[3], w, true);
+                *reinterpret_cast<int*>(dst) = w;
             } else {
-                reinterpret_cast<uint16_t*>(sv)[c * kPad + pos] = (n < N) ? Half<BF16>::from_f(x) : 0;
+                uint16_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = valid[e] ? Half<BF16>::from_f(x[e]) : 0;
+                uint2 w;
+                w.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+                w.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+                *reinterpret_cast<uint2*>(dst) = w;
             }
         }
     }
     __syncthreads();
-    constexpr int ROWB = kPad * E;                       // bytes per channel row of the tile
     constexpr int CPR = ROWB / 16;
     constexpr int TOTAL = DP * CPR;
     uint8_t* out = reinterpret_cast<uint8_t*>(a.vt) + (hb * a.npad + row0) * E;
     for (int L = tid; L < TOTAL; L += kThreads) {
-        const int c = L / CPR, j = L % CPR;
-        *reinterpret_cast<uint4*>(out + (int64_t)c * a.npad * E + j * 16) =
-            *reinterpret_cast<const uint4*>(sv + c * ROWB + j * 16);
+        const int c = L / CPR, jc = L % CPR;
+        *reinterpret_cast<uint4*>(out + (int64_t)c * a.npad * E + jc * 16) =
+            *reinterpret_cast<const uint4*>(sv + c * ROWB + ((jc ^ chunk_swz(c)) << 4));
     }
+}
+
+template <bool BF16, int DP, bool FP8, bool VEC>
+__global__ __launch_bounds__(kThreads) void quant_v_kernel(QuantVArgs a, StatsArgs vs, int have_stats) {
+    const int tiles = a.npad / kPad;
+    quant_v_body<BF16, DP, FP8, VEC>(a, vs, have_stats, blockIdx.x % tiles, (blockIdx.x / tiles) % a.H,
+                                     blockIdx.x / tiles / a.H);
+}
+
+// ---------------------------------------------------------------------------
+// Q, K and V in two launches (the same workgroup bodies as above).
+// Pass 1: Q tiles; K statistics chunks (smooth_k) or K tiles; V statistics
+// chunks (when V needs them).  Pass 2: K tiles minus their means (smooth_k);
+// V tiles.
+template <bool BF16, int DP, bool VEC>
+__global__ __launch_bounds__(kThreads) void qkv_pass1_kernel(QuantRowsArgs q, QuantRowsArgs k, StatsArgs ks,
+                                                             StatsArgs vs, int nq_blocks, int nk_blocks,
+                                                             int smooth_k) {
+    int bid = blockIdx.x;
+    if (bid < nq_blocks) {
+        const int tiles = q.npad / kPad;
+        quant_rows_body<BF16, DP, VEC>(q, bid % tiles, (bid / tiles) % q.H, bid / tiles / q.H, nullptr);
+        return;
+    }
+    bid -= nq_blocks;
+    if (bid < nk_blocks) {
+        if (smooth_k) {
+            stats_body<BF16, DP, VEC>(ks, bid % ks.chunks, (bid / ks.chunks) % ks.H, bid / ks.chunks / ks.H);
+        } else {
+            const int tiles = k.npad / kPad;
+            quant_rows_body<BF16, DP, VEC>(k, bid % tiles, (bid / tiles) % k.H, bid / tiles / k.H, nullptr);
+        }
+        return;
+    }
+    bid -= nk_blocks;
+    stats_body<BF16, DP, VEC>(vs, bid % vs.chunks, (bid / vs.chunks) % vs.H, bid / vs.chunks / vs.H);
+}
+
+template <bool BF16, int DP, bool FP8, bool VEC>
+__global__ __launch_bounds__(kThreads) void qkv_pass2_kernel(QuantRowsArgs k, StatsArgs ks, QuantVArgs v,
+                                                             StatsArgs vs, int nk_blocks, int v_stats) {
+    int bid = blockIdx.x;
+    if (bid < nk_blocks) {
+        const int tiles = k.npad / kPad;
+        quant_rows_body<BF16, DP, VEC>(k, bid % tiles, (bid / tiles) % k.H, bid / tiles / k.H, &ks);
+        return;
+    }
+    bid -= nk_blocks;
+    const int tiles = v.npad / kPad;
+    quant_v_body<BF16, DP, FP8, VEC>(v, vs, v_stats, bid % tiles, (bid / tiles) % v.H, bid / tiles / v.H);
+}
+
+template <bool BF16, int DP, bool FP8, bool VEC>
+static hipError_t quant_qkv_dispatch(const QuantRowsArgs& q, const QuantRowsArgs& k, const StatsArgs& ks,
+                                     bool smooth_k, const QuantVArgs& v, const StatsArgs& vs, bool v_stats,
+                                     hipStream_t s) {
+    const int nq = (q.npad / kPad) * q.H * q.B;
+    const int k_tiles = (k.npad / kPad) * k.H * k.B;
+    const int nk1 = smooth_k ? ks.chunks * ks.H * ks.B : k_tiles;
+    const int nv1 = v_stats ? vs.chunks * vs.H * vs.B : 0;
+    qkv_pass1_kernel<BF16, DP, VEC><<<nq + nk1 + nv1, kThreads, 0, s>>>(q, k, ks, vs, nq, nk1, smooth_k ? 1 : 0);
+    if (hipError_t e = hipGetLastError()) return e;
+    const int nk2 = smooth_k ? k_tiles : 0;
+    const int nv2 = (v.npad / kPad) * v.H * v.B;
+    qkv_pass2_kernel<BF16, DP, FP8, VEC><<<nk2 + nv2, kThreads, 0, s>>>(k, ks, v, vs, nk2, v_stats ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_qkv(const QuantRowsArgs& q, const QuantRowsArgs& k, const StatsArgs& ks, bool smooth_k,
+                            const QuantVArgs& v, const StatsArgs& vs, bool v_stats, bool bf16, bool fp8, bool vec,
+                            hipStream_t s) {
+    const int dp = q.d <= 64 ? 64 : 128;
+#define SAGE_QKV(BF, D, F, V) return quant_qkv_dispatch<BF, D, F, V>(q, k, ks, smooth_k, v, vs, v_stats, s)
+#define SAGE_QKV2(BF, D, F) { if (vec) SAGE_QKV(BF, D, F, true); else SAGE_QKV(BF, D, F, false); }
+    if (bf16) {
+        if (dp == 128) { if (fp8) SAGE_QKV2(true, 128, true) else SAGE_QKV2(true, 128, false) }
+        else { if (fp8) SAGE_QKV2(true, 64, true) else SAGE_QKV2(true, 64, false) }
+    } else {
+        if (dp == 128) { if (fp8) SAGE_QKV2(false, 128, true) else SAGE_QKV2(false, 128, false) }
+        else { if (fp8) SAGE_QKV2(false, 64, true) else SAGE_QKV2(false, 64, false) }
+    }
+#undef SAGE_QKV2
+#undef SAGE_QKV
 }
 
 // ---------------------------------------------------------------------------

@@ -90,7 +90,24 @@ size_t sage_quant_workspace_size(int B, int H, int N, int d) {
     return ws_layout(B, H, N, d).total;
 }
 
-int sage_quant_qk(const sage_quant_qk_params* p, void* stream) {
+namespace {
+// Validated launch arguments of one quantize call.
+struct QKPrep {
+    sage::QuantRowsArgs qa, ka;
+    sage::StatsArgs st;
+    bool smooth, bf16, vec;
+    const void* ws;
+    size_t ws_used;
+};
+struct VPrep {
+    sage::QuantVArgs va;
+    sage::StatsArgs st;
+    bool need_stats, smooth, bf16, fp8, vec;
+    const void* ws;
+    size_t ws_used;
+};
+
+int prepare_qk(const sage_quant_qk_params* p, QKPrep& o) {
     if (!p) return fail(SAGE_EINVAL, "params is NULL");
     if (p->struct_size < sizeof(sage_quant_qk_params)) return fail(SAGE_EINVAL, "struct_size too small");
     if (!valid_dtype(p->dtype)) return fail(SAGE_EINVAL, "unknown dtype %d", p->dtype);
@@ -114,7 +131,6 @@ int sage_quant_qk(const sage_quant_qk_params* p, void* stream) {
         if (p->workspace_bytes < ws.total)
             return fail(SAGE_EINVAL, "workspace too small: %zu < %zu bytes", p->workspace_bytes, ws.total);
     }
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool bf16 = p->dtype == SAGE_BF16;
     const int dp = dp_of(p->d);
     const int nq_pad = (int)round_up(p->Nq, sage::kPad), nk_pad = (int)round_up(p->Nk, sage::kPad);
@@ -140,13 +156,18 @@ int sage_quant_qk(const sage_quant_qk_params* p, void* stream) {
     ka.group_shift = k_group_shift(p->gran); ka.out = p->k8; ka.scale = p->k_scale;
     const bool vec = vec_ok(p->q, p->q_stride_b, p->q_stride_h, p->q_stride_n) &&
                      vec_ok(p->k, p->k_stride_b, p->k_stride_h, p->k_stride_n);
-    if (int r = hip_status(sage::launch_quant_qk(qa, ka, st, p->smooth_k, bf16, vec, s),
-                           "Q/K quantize launch"))
-        return r;
-    return ok();
+    o.qa = qa;
+    o.ka = ka;
+    o.st = st;
+    o.smooth = p->smooth_k != 0;
+    o.bf16 = bf16;
+    o.vec = vec;
+    o.ws = p->smooth_k ? p->workspace : nullptr;
+    o.ws_used = p->smooth_k ? ws.total : 0;
+    return 0;
 }
 
-int sage_quant_v(const sage_quant_v_params* p, void* stream) {
+int prepare_v(const sage_quant_v_params* p, VPrep& o) {
     if (!p) return fail(SAGE_EINVAL, "params is NULL");
     if (p->struct_size < sizeof(sage_quant_v_params)) return fail(SAGE_EINVAL, "struct_size too small");
     if (!valid_dtype(p->dtype)) return fail(SAGE_EINVAL, "unknown dtype %d", p->dtype);
@@ -169,7 +190,6 @@ int sage_quant_v(const sage_quant_v_params* p, void* stream) {
         if (p->workspace_bytes < ws.total)
             return fail(SAGE_EINVAL, "workspace too small: %zu < %zu bytes", p->workspace_bytes, ws.total);
     }
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const bool bf16 = p->dtype == SAGE_BF16;
     const int dp = dp_of(p->d);
     const int nk_pad = (int)round_up(p->Nk, sage::kPad);
@@ -191,8 +211,55 @@ int sage_quant_v(const sage_quant_v_params* p, void* stream) {
     va.B = p->B; va.H = p->Hkv; va.N = p->Nk; va.npad = nk_pad; va.d = p->d; va.vt = p->vt;
     const bool vec = aligned(p->v, 16) && p->d % 8 == 0 && p->v_stride_b % 8 == 0 && p->v_stride_h % 8 == 0 &&
                      p->v_stride_n % 8 == 0;
-    if (int r = hip_status(sage::launch_quant_v(va, st, need_stats, p->smooth_v, bf16, fp8, vec, s),
+    o.va = va;
+    o.st = st;
+    o.need_stats = need_stats;
+    o.smooth = p->smooth_v != 0;
+    o.bf16 = bf16;
+    o.fp8 = fp8;
+    o.vec = vec;
+    o.ws = need_stats ? p->workspace : nullptr;
+    o.ws_used = need_stats ? ws.total : 0;
+    return 0;
+}
+}  // namespace
+
+int sage_quant_qk(const sage_quant_qk_params* p, void* stream) {
+    QKPrep o;
+    if (int r = prepare_qk(p, o)) return r;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (int r = hip_status(sage::launch_quant_qk(o.qa, o.ka, o.st, o.smooth, o.bf16, o.vec, s), "Q/K quantize launch"))
+        return r;
+    return ok();
+}
+
+int sage_quant_v(const sage_quant_v_params* p, void* stream) {
+    VPrep o;
+    if (int r = prepare_v(p, o)) return r;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (int r = hip_status(sage::launch_quant_v(o.va, o.st, o.need_stats, o.smooth, o.bf16, o.fp8, o.vec, s),
                            "V quantize launch"))
+        return r;
+    return ok();
+}
+
+int sage_quant_qkv(const sage_quant_qk_params* qk, const sage_quant_v_params* v, void* stream) {
+    QKPrep a;
+    VPrep b;
+    if (int r = prepare_qk(qk, a)) return r;
+    if (int r = prepare_v(v, b)) return r;
+    if (qk->dtype != v->dtype || qk->B != v->B || qk->Hkv != v->Hkv || qk->Nk != v->Nk || qk->d != v->d ||
+        qk->cu_seqlens_k != v->cu_seqlens_k)
+        return fail(SAGE_EINVAL, "K and V must share dtype, B, Hkv, Nk, head_dim and cu_seqlens_k");
+    if (a.ws_used && b.ws_used) {
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.ws), b0 = reinterpret_cast<uintptr_t>(b.ws);
+        if (a0 < b0 + b.ws_used && b0 < a0 + a.ws_used)
+            return fail(SAGE_EINVAL, "the K and V workspaces overlap; the fused call needs one of each");
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (int r = hip_status(sage::launch_quant_qkv(a.qa, a.ka, a.st, a.smooth, b.va, b.st, b.need_stats, a.bf16, b.fp8,
+                                                  a.vec && b.vec, s),
+                           "Q/K/V quantize launch"))
         return r;
     return ok();
 }

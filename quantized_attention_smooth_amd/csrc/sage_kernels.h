@@ -91,6 +91,11 @@ hipError_t launch_quant_qk(const QuantRowsArgs& q, const QuantRowsArgs& k, const
 // V: statistics (when stats), then the tiles.
 hipError_t launch_quant_v(const QuantVArgs& a, const StatsArgs& vs, bool stats, bool smooth, bool bf16, bool fp8,
                           bool vec, hipStream_t s);
+// Q, K and V together in two launches; ks and vs must use disjoint
+// workspaces.
+hipError_t launch_quant_qkv(const QuantRowsArgs& q, const QuantRowsArgs& k, const StatsArgs& ks, bool smooth_k,
+                            const QuantVArgs& v, const StatsArgs& vs, bool v_stats, bool bf16, bool fp8, bool vec,
+                            hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int dp, int pv /*0 fp8, 1 fp16, 2 bf16*/, bool out_bf16,
                        hipStream_t s);
 hipError_t launch_qk_scores(const AttnArgs& a, int dp, hipStream_t s);

@@ -217,3 +217,40 @@ def test_workspace_size(lib):
     cells = 2 * 8 * 32 * 128
     assert n >= cells * 16
     assert lib.sage_quant_workspace_size(1, 1, 257, 64) > lib.sage_quant_workspace_size(1, 1, 256, 64)
+
+
+def _qkv_valid():
+    """A matching pair for the fused call: K and V agree and use distinct workspaces."""
+    pk = _qk_valid()
+    pv = _v_valid()
+    pv.dtype, pv.B, pv.Hkv, pv.Nk, pv.d = pk.dtype, pk.B, pk.Hkv, pk.Nk, pk.d
+    pv.v_stride_b, pv.v_stride_h, pv.v_stride_n = pk.k_stride_b, pk.k_stride_h, pk.k_stride_n
+    pv.workspace, pv.workspace_bytes = FAKE + 0x2000000, 1 << 20
+    return pk, pv
+
+
+QKV_BREAKS = {
+    "dtype differs": lambda pk, pv: setattr(pv, "dtype", A.SAGE_BF16),
+    "Nk differs": lambda pk, pv: setattr(pv, "Nk", pk.Nk + 1),
+    "Hkv differs": lambda pk, pv: setattr(pv, "Hkv", 1),
+    "head_dim differs": lambda pk, pv: setattr(pv, "d", 32),
+    "cu_seqlens_k differs": lambda pk, pv: (setattr(pk, "cu_seqlens_q", FAKE + 0x3000000),
+                                            setattr(pk, "cu_seqlens_k", FAKE + 0x3100000)),
+    "workspaces overlap": lambda pk, pv: setattr(pv, "workspace", pk.workspace + 256),
+    "K params invalid": lambda pk, pv: setattr(pk, "gran", 7),
+    "V params invalid": lambda pk, pv: setattr(pv, "v_dtype", 9),
+}
+
+
+@pytest.mark.parametrize("case", sorted(QKV_BREAKS))
+def test_quant_qkv_rejects(lib, case):
+    pk, pv = _qkv_valid()
+    QKV_BREAKS[case](pk, pv)
+    assert lib.sage_quant_qkv(ctypes.byref(pk), ctypes.byref(pv), None) == A.SAGE_EINVAL
+    assert len(lib.sage_last_error()) > 0
+
+
+def test_quant_qkv_null_params(lib):
+    pk, pv = _qkv_valid()
+    assert lib.sage_quant_qkv(None, ctypes.byref(pv), None) == A.SAGE_EINVAL
+    assert lib.sage_quant_qkv(ctypes.byref(pk), None, None) == A.SAGE_EINVAL

@@ -252,3 +252,64 @@ def test_page_shape_examples():
         ref = torch.nn.functional.scaled_dot_product_attention(q.float(), k.float(), v.float(),
                                                                is_causal=bool(int(causal)))
         assert (out.float() - ref).abs().mean().item() < 1e-2
+
+
+# ------------------------------------------------------------------ fused quantize call
+def _quant_pair(inp, w, fused, v_dtype=None, smooth_v=None):
+    dev = "cuda"
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    vd = v_dtype or w.v_dtype
+    sv = w.smooth_v if smooth_v is None else smooth_v
+    kw = {}
+    if w.varlen:
+        cu = inp["cu_seqlens"].to(dev)
+        ms = inp["max_seqlen"]
+        kw = dict(cu_seqlens_k=cu, max_seqlen_k=ms)
+        kq = dict(cu_seqlens_q=cu, max_seqlen_q=ms)
+    else:
+        kw = dict(tensor_layout=w.layout)
+        kq = {}
+    if fused:
+        return sage.sage_quant_qkv(q, k, v, qk_quant_gran=w.gran, smooth_k=w.smooth_k, v_dtype=vd, smooth_v=sv,
+                                   **kq, **kw)
+    qk = sage.sage_quant_qk(q, k, qk_quant_gran=w.gran, smooth_k=w.smooth_k, **kq, **kw)
+    qv = sage.sage_quant_v(v, v_dtype=vd, smooth_v=sv, **kw)
+    return qk, qv
+
+
+@pytest.mark.parametrize("name", workloads.WORKLOAD_ORDER)
+def test_fused_quantize_equals_separate_calls(name):
+    """sage_quant_qkv (two launches) writes the same bits as sage_quant_qk +
+    sage_quant_v (four launches), on every workload at full size."""
+    w = workloads.WORKLOADS[name]
+    _announce(f"fused quantize {name}")
+    inp = workloads.make_inputs(w)
+    a_qk, a_v = _quant_pair(inp, w, fused=False)
+    b_qk, b_v = _quant_pair(inp, w, fused=True)
+    torch.cuda.synchronize()
+    for f in ("q8", "q_scale", "k8", "k_scale", "k_mean"):
+        x, y = getattr(a_qk, f), getattr(b_qk, f)
+        assert (x is None) == (y is None), f
+        if x is not None:
+            assert torch.equal(x, y), f
+    for f in ("vt", "v_scale", "v_mean"):
+        x, y = getattr(a_v, f), getattr(b_v, f)
+        assert (x is None) == (y is None), f
+        if x is not None:
+            assert torch.equal(x, y), f
+
+
+@pytest.mark.parametrize("v_dtype,smooth_v", [("fp8", True), ("fp16", False), ("fp16", True)])
+def test_fused_quantize_equals_separate_calls_v_modes(v_dtype, smooth_v):
+    w = dataclasses.replace(workloads.WORKLOADS["gqa_prefill_n8192"], Nq=1000, Nk=1000)
+    _announce(f"fused quantize v_dtype={v_dtype} smooth_v={smooth_v} (GQA prefill recipe, N=1000)")
+    inp = workloads.make_inputs(w)
+    a_qk, a_v = _quant_pair(inp, w, fused=False, v_dtype=v_dtype, smooth_v=smooth_v)
+    b_qk, b_v = _quant_pair(inp, w, fused=True, v_dtype=v_dtype, smooth_v=smooth_v)
+    torch.cuda.synchronize()
+    for x, y in ((a_qk.q8, b_qk.q8), (a_qk.k8, b_qk.k8), (a_qk.k_scale, b_qk.k_scale), (a_v.vt, b_v.vt)):
+        assert torch.equal(x, y)
+    for x, y in ((a_v.v_scale, b_v.v_scale), (a_v.v_mean, b_v.v_mean)):
+        assert (x is None) == (y is None)
+        if x is not None:
+            assert torch.equal(x, y)
