@@ -1041,8 +1041,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     constexpr int PV = 0, NW = kWaves8;                 // every wavefront copies its share
     using C = AttnCfg<DP, PV, NW, NW>;
     constexpr int NCB = C::NCB;
-    constexpr int AHEAD = 3;
-    constexpr int NST = AHEAD + 2;
+    constexpr int AHEAD = 5;                            // tiles in flight ahead of the one being read
+    constexpr int NST = AHEAD + 3;                      // ring stages (see the key-loop comment)
     constexpr int LPT = C::NI + C::NSC;                 // copy instructions per copying wavefront per tile
     __shared__ __attribute__((aligned(16))) uint8_t smem[NST * C::STAGE];
 
@@ -1103,6 +1103,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     v16i biasv;
 #pragma unroll
     for (int i = 0; i < 16; ++i) biasv[i] = kAccBiasBits;
+    // d = 64 has registers to spare: keep the bias in 16 VGPRs for the whole
+    // loop instead of rebuilding it before every QK^T
+    if constexpr (DP == 64) asm volatile("" : "+v"(biasv));
     Ones<PV> ones;
     make_ones<PV>(ones, rowsum_parity(lane));
 
@@ -1126,7 +1129,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
 
 #pragma unroll
     for (int u = 0; u < AHEAD; ++u) issue(u);
-    if (ntiles >= AHEAD) wait_vmcnt<LPT * (AHEAD - 2)>();
+    if (ntiles >= AHEAD) wait_vmcnt<LPT * (AHEAD - 3)>();
     else wait_vmcnt<0>();
     block_sync();
 
@@ -1137,19 +1140,26 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     // Step t is two regions:
     //   H(t): QK^T of tile t, then P.V of tile t-1 and the row sums, with the
     //         group maxima of tile t between the P.V MFMAs, the copy of tile
-    //         t+3, and the K and V^T fragments of the next step (matrix-core
-    //         work);
+    //         t+AHEAD, and the K and V^T fragments of the next step
+    //         (matrix-core work);
     //   E(t): P of tile t, computed with the reference maximum from before
     //         the tile while the raise decision completes; if a row raises,
     //         O is rescaled and P recomputed (VALU work).
-    // Wavefronts 4-7 run half a step behind wavefronts 0-3, so that on each
-    // SIMD one wavefront is in H while the other is in E; every half step
-    // ends with a workgroup barrier.  The ring of NST = AHEAD + 2 stages stays
-    // valid: each wavefront copies its share of tile t+3 in its H(t), into
-    // the stage of tile t-2, whose last reads (V^T fragments in H(t-2) of
-    // either group) precede the barrier before that H(t); and each wavefront
-    // waits for its share of tile t+2 before the barrier that ends its H(t),
-    // which precedes every read of tile t+2 (fragments in H(t+1)).
+    // One workgroup barrier per step: wavefronts 0-3 pass barrier t right
+    // after their H(t), wavefronts 4-7 right before theirs, so between
+    // barriers t and t+1 the leading group runs E(t) then H(t+1) while the
+    // other runs H(t) then E(t), and on each SIMD one wavefront is mostly in
+    // H while the other is in E.  The ring stays valid with NST = AHEAD + 3
+    // stages when every wavefront waits for its own share of tile t+3 at the
+    // end of its H(t):
+    //  * reads of tile t+1 (K fragments in H(t)) come after barrier t-1 for
+    //    the leading group and after barrier t for the other; every share of
+    //    tile t+1 was waited for in an H(t-2), which both groups finish
+    //    before barrier t-1;
+    //  * the copy in H(t) overwrites the stage of tile t+AHEAD-NST = t-3,
+    //    whose last fragment reads (V^T in H(t-3), consumed by the MFMAs of
+    //    H(t-2)) both groups finish before barrier t-1, which precedes H(t)
+    //    of either group.
     v16i S[2];
     PHalf<PV> P;
     phalf_zero<PV>(P);                                  // P.V for "tile -1" adds exact zeros
@@ -1204,7 +1214,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         } else {
             copier.issue_all(st_copy, tc);
         }
-        wait_vmcnt<LPT * (AHEAD - 2)>();                // own share of tile t+2 has landed
+        wait_vmcnt<LPT * (AHEAD - 3)>();                // own share of tile t+3 has landed
     };
     auto regionE = [&](SoftmaxPieces<PV>& sp) {
         if (!live) return;
@@ -1221,18 +1231,16 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         }
         keep_here<PV>(P);
     };
-    // wavefronts 4-7: one barrier first (paired with the end of H(0) of
-    // wavefronts 0-3) and none after their last E, so both groups pass the
-    // same number of barriers
+    // both groups pass one barrier per step (see above); a last barrier
+    // after the loop orders every wavefront's final waits before the tail
     auto step = [&](auto u, int t) {
         SoftmaxPieces<PV> sp;
+        if (!lead_wave) block_sync();
         regionH(u, t, sp);
-        block_sync();
+        if (lead_wave) block_sync();
         regionE(sp);
-        if (lead_wave || t + 1 < n_main) block_sync();
     };
     int t = 0;
-    if (!lead_wave && n_main > 0) block_sync();
     for (; t < n_main; t += NST) {                      // stage slots 0 .. NST-1 in turn
         static_for<0, NST>([&](auto u) {
             if (t + decltype(u)::value < n_main) step(u, t + decltype(u)::value);
@@ -1241,6 +1249,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     t = n_main;
     if (live && n_main > 0) pv8_all<DP>(va, P, ones, o, ls);   // P.V of the last pipelined tile
     wait_vmcnt<0>();
+    block_sync();
 
     // ---- remaining tiles (a ragged end, the causal diagonal): one at a time
     for (; t < ntiles; ++t) {
