@@ -9,7 +9,9 @@ is B=2, H=8, N=4096, head_dim=128, fp16, per_warp INT8 Q/K, FP8 V.
 Prints ONE JSON line.  `value` is whole-step TOPS (4*B*H*Nq*Nk*d per step,
 halved for causal).  `roofline` describes the attention kernel, timed with HIP
 events on the stream it runs on; `cpu_baseline` is the CPU oracle timed on a
-bounded sample of the same workload.
+bounded sample of the same workload; `secondary` gives the attention kernel's
+TOPS on the 17 550-token video-DiT shape (B=1, H=48, d=64), the metric's
+other sequence length.
 """
 from __future__ import annotations
 
@@ -82,37 +84,21 @@ def cpu_baseline(w, inp, seconds: float) -> dict:
                       f"quantization included; {t_total:.1f} s"}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="b2h8n4096d128")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--traffic-calibration", action="store_true",
-                    help="before the steps, run a plain 1 GiB -> 1 GiB fp32 elementwise copy three times, so "
-                         "that hardware byte counters of the attention kernel can be scaled by what the same "
-                         "counters read for a kernel of known traffic")
-    args = ap.parse_args()
-
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the quantized attention forward here runs on a single "
-              "MI355X (--gpus 1); multi-GPU sharding is not part of this build.", file=sys.stderr)
-        return 2
-
+def time_workload(w, steps: int, warmup: int, calibrate: bool = False):
+    """Run `warmup` untimed and `steps` timed steps of the hot path (fused
+    quantize + attention) on inputs resident in HBM.  Returns the inputs and
+    (ms per step from the host clock, quantize ms and attention ms from HIP
+    events recorded on the stream the kernels run on)."""
     import torch
     import workloads
     import quantized_attention_smooth_amd as sage
 
-    w = workloads.WORKLOADS[args.workload]
     if w.varlen:
         raise SystemExit("the benchmark workload must be dense")
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
     q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
-    nk = w.Nk
-    ws_k = torch.empty(sage.workspace_bytes(w.B, w.Hkv, nk, w.d), dtype=torch.uint8, device=dev)
+    ws_k = torch.empty(sage.workspace_bytes(w.B, w.Hkv, w.Nk, w.d), dtype=torch.uint8, device=dev)
     ws_v = torch.empty_like(ws_k)
     stream = torch.cuda.current_stream()
 
@@ -129,7 +115,7 @@ def main() -> int:
             ev[2].record(stream)
         return out
 
-    if args.traffic_calibration:
+    if calibrate:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
@@ -137,19 +123,48 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / steps
+    attn_ms = sum(e[1].elapsed_time(e[2]) for e in events) / steps
+    return inp, ms_per_step, quant_ms, attn_ms
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="b2h8n4096d128")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--secondary", default="video_dit_n17550",
+                    help="a second workload whose attention-kernel TOPS is reported beside the main line "
+                         "('none' to skip); the metric is quoted at sequence 4096 and 17.5k")
+    ap.add_argument("--traffic-calibration", action="store_true",
+                    help="before the steps, run a plain 1 GiB -> 1 GiB fp32 elementwise copy three times, so "
+                         "that hardware byte counters of the attention kernel can be scaled by what the same "
+                         "counters read for a kernel of known traffic")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the quantized attention forward here runs on a single "
+              "MI355X (--gpus 1); multi-GPU sharding is not part of this build.", file=sys.stderr)
+        return 2
+
+    import workloads
+
+    w = workloads.WORKLOADS[args.workload]
+    inp, ms_per_step, quant_ms, attn_ms = time_workload(w, args.steps, args.warmup, args.traffic_calibration)
 
     ops = workloads.attention_ops(w)
     value = ops / (ms_per_step * 1e-3) / 1e12
@@ -184,6 +199,17 @@ def main() -> int:
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tops / peak, 4), "traffic": measured_traffic(w.name)},
     }
+    if args.secondary != "none" and args.secondary != w.name:
+        w2 = workloads.WORKLOADS[args.secondary]
+        _, ms2, qms2, ams2 = time_workload(w2, 10, 3)
+        ops2 = workloads.attention_ops(w2)
+        at2 = ops2 / (ams2 * 1e-3) / 1e12
+        rec["secondary"] = {"workload": w2.name, "seq_len": w2.Nq, "head_dim": w2.d, "B": w2.B, "Hq": w2.Hq,
+                            "qk_quant_gran": w2.gran, "v_dtype": w2.v_dtype, "smooth_v": w2.smooth_v,
+                            "steps": 10, "warmup": 3, "ms_per_step": round(ms2, 4),
+                            "step_tops": round(ops2 / (ms2 * 1e-3) / 1e12, 2), "quant_ms": round(qms2, 4),
+                            "attn_kernel_ms": round(ams2, 4), "attn_kernel_tops": round(at2, 2),
+                            "attn_pct_of_peak": round(100.0 * at2 / PEAK_TOPS[w2.v_dtype], 2)}
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)
