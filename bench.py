@@ -11,7 +11,8 @@ halved for causal).  `roofline` describes the attention kernel, timed with HIP
 events on the stream it runs on; `cpu_baseline` is the CPU oracle timed on a
 bounded sample of the same workload; `secondary` gives the attention kernel's
 TOPS on the 17 550-token video-DiT shape (B=1, H=48, d=64), the metric's
-other sequence length.
+other sequence length; `merge` gives the HBM throughput of sage_merge_states
+combining two partial results of the workload's output shape.
 """
 from __future__ import annotations
 
@@ -139,6 +140,36 @@ def time_workload(w, steps: int, warmup: int, calibrate: bool = False):
     return inp, ms_per_step, quant_ms, attn_ms
 
 
+def time_merge(w, parts: int = 2, iters: int = 20) -> dict:
+    """HBM throughput of sage_merge_states combining `parts` partial results
+    of the workload's output shape (what a split of its keys into `parts`
+    sets, each run with return_lse, hands to the merge)."""
+    import torch
+    import workloads
+    import quantized_attention_smooth_amd as sage
+
+    inp = workloads.make_merge_inputs(w.seed, parts, w.B, w.Hq, w.Nq, w.d, w.dtype, w.layout)
+    dev = torch.device("cuda:0")
+    o, l = inp["out_parts"].to(dev), inp["lse_parts"].to(dev)
+    out = torch.empty(o.shape[1:], dtype=o.dtype, device=dev)
+    for _ in range(3):
+        sage.sage_merge_states(o, l, tensor_layout=w.layout, out=out)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(iters):
+        sage.sage_merge_states(o, l, tensor_layout=w.layout, out=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    rows = w.B * w.Hq * w.Nq
+    nbytes = parts * rows * (2 * w.d + 4) + rows * (2 * w.d + 4)     # read parts + LSEs, write out + LSE
+    return {"kernel": "merge_kernel (sage_merge_states)", "parts": parts, "shape": list(o.shape),
+            "us": round(us, 2), "bytes": nbytes, "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "roofline": {"bound": "hbm", "achieved": round(nbytes / (us * 1e-6) / 1e9, 1), "peak": 8000.0,
+                         "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 8e12, 4)}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +178,7 @@ def main() -> int:
     ap.add_argument("--workload", default="b2h8n4096d128")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-merge", action="store_true", help="skip timing sage_merge_states")
     ap.add_argument("--secondary", default="video_dit_n17550",
                     help="a second workload whose attention-kernel TOPS is reported beside the main line "
                          "('none' to skip); the metric is quoted at sequence 4096 and 17.5k")
@@ -210,6 +242,8 @@ def main() -> int:
                             "step_tops": round(ops2 / (ms2 * 1e-3) / 1e12, 2), "quant_ms": round(qms2, 4),
                             "attn_kernel_ms": round(ams2, 4), "attn_kernel_tops": round(at2, 2),
                             "attn_pct_of_peak": round(100.0 * at2 / PEAK_TOPS[w2.v_dtype], 2)}
+    if not args.no_merge:
+        rec["merge"] = time_merge(w)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

@@ -245,6 +245,41 @@ int sage_attn_varlen_fwd(const sage_attn_varlen_params* p, void* stream);
  * ------------------------------------------------------------------------- */
 int sage_debug_qk_scores(const sage_attn_params* p, int mode, void* scores, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * sage_merge_states: combine attention results computed over S disjoint key
+ * sets of the same queries, using the log-sum-exp each one returned
+ * (deployment guide sec. 4.1: return_lse, for Ring-Attention-style use).
+ * With o_s the normalised output of key set s and L_s its natural-log LSE,
+ * the attention over all keys is out = sum_s exp(L_s - L) o_s and
+ * L = log sum_s exp(L_s), exactly in real arithmetic.
+ * Computed per row in fp32: m = max_s L_s, w_s = exp(L_s - m) (0 when
+ * L_s = -inf), W = sum_s w_s, out = sum_s (w_s / W) o_s rounded once to the
+ * output dtype (nearest even), L = m + log W.  A row whose S values are all
+ * -inf (it saw no key) gives out = 0 and L = -inf.  Sums run s = 0 .. S-1.
+ * parts: S fp16/bf16 results, element (s, b, h, n, c) at parts + s*ps_s +
+ * b*ps_b + h*ps_h + n*ps_n + c for c < d; the output row (b, h, n) at out +
+ * b*o_stride_b + h*o_stride_h + n*o_stride_n.  lse_parts is fp32
+ * [S][B][H][N] contiguous (what sage_attn_fwd writes for each set, stacked);
+ * lse (optional) receives fp32 [B][H][N].  out must not overlap the inputs.
+ * Sizes: 1 <= S <= 64, 1 <= d <= 1024, B, H, N >= 1.
+ * Errors: SAGE_EINVAL for invalid sizes or dtype, NULL parts/lse_parts/out,
+ * or pointers not aligned to their element size.
+ * ------------------------------------------------------------------------- */
+typedef struct sage_merge_params {
+    size_t struct_size;
+    int n_parts;                        /* S */
+    int dtype;                          /* enum sage_dtype: parts and out */
+    int B, H, N, d;
+    const void* parts;
+    int64_t ps_s, ps_b, ps_h, ps_n;     /* element strides of parts */
+    const float* lse_parts;             /* [S][B][H][N] */
+    void* out;
+    int64_t o_stride_b, o_stride_h, o_stride_n;
+    float* lse;                         /* NULL: no merged LSE */
+} sage_merge_params;
+
+int sage_merge_states(const sage_merge_params* p, void* stream);
+
 const char* sage_last_error(void);
 int sage_version(void);
 

@@ -329,3 +329,29 @@ def exact_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, layout: str = 
             outs.append(o); lses.append(ls)
         res["out"].append(np.stack(outs)); res["lse"].append(np.stack(lses))
     return res
+
+
+def merge_states(out_parts: np.ndarray, lse_parts: np.ndarray):
+    """Attention over the union of S disjoint key sets from the S partial
+    results (the use of return_lse in [guide] sec. 4.1, Ring-Attention-style
+    merging): with o_s the normalised output of set s and L_s its natural-log
+    log-sum-exp, exp(L_s) is set s's softmax denominator, so
+        out = sum_s exp(L_s - L) o_s,   L = log sum_s exp(L_s).
+    Written out in fp64 with the largest L_s as reference point; parts with
+    L_s = -inf (no key) weigh 0, and a row with no key at all gives out = 0,
+    L = -inf.
+
+    out_parts: (S, R, d) values (decoded fp16/bf16); lse_parts: (S, R).
+    Returns out (R, d) and L (R,), fp64."""
+    o = np.asarray(out_parts, dtype=np.float64)
+    ls = np.asarray(lse_parts, dtype=np.float64)
+    m = ls.max(axis=0)
+    empty = m == -np.inf
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(ls - m_safe[None, :])                  # exp(-inf) = 0 for empty parts
+    W = w.sum(axis=0)
+    W_safe = np.where(empty, 1.0, W)
+    out = np.einsum("sr,srd->rd", w / W_safe[None, :], o)
+    out[empty] = 0.0
+    L = np.where(empty, -np.inf, m_safe + np.log(W_safe))
+    return out, L

@@ -62,8 +62,16 @@ class AttnVarlenParams(ctypes.Structure):
     _fields_ = [("base", AttnParams), ("cu_seqlens_q", VP), ("cu_seqlens_k", VP), ("total_q", I)]
 
 
+class MergeParams(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", SZ), ("n_parts", I), ("dtype", I), ("B", I), ("H", I), ("N", I), ("d", I),
+        ("parts", VP), ("ps_s", I64), ("ps_b", I64), ("ps_h", I64), ("ps_n", I64), ("lse_parts", VP),
+        ("out", VP), ("o_stride_b", I64), ("o_stride_h", I64), ("o_stride_n", I64), ("lse", VP),
+    ]
+
+
 EXPORTS = ["sage_quant_qk", "sage_quant_workspace_size", "sage_quant_v", "sage_quant_qkv", "sage_attn_fwd",
-           "sage_attn_varlen_fwd", "sage_debug_qk_scores", "sage_last_error", "sage_version"]
+           "sage_attn_varlen_fwd", "sage_debug_qk_scores", "sage_merge_states", "sage_last_error", "sage_version"]
 
 _lib = None
 
@@ -93,6 +101,8 @@ def load(path: str = LIB_PATH):
     L.sage_attn_varlen_fwd.restype = I
     L.sage_debug_qk_scores.argtypes = [ctypes.POINTER(AttnParams), I, VP, VP]
     L.sage_debug_qk_scores.restype = I
+    L.sage_merge_states.argtypes = [ctypes.POINTER(MergeParams), VP]
+    L.sage_merge_states.restype = I
     L.sage_quant_workspace_size.argtypes = [I, I, I, I]
     L.sage_quant_workspace_size.restype = SZ
     L.sage_last_error.argtypes = []

@@ -281,6 +281,55 @@ def sage_debug_qk_scores(qk: QuantQK, checksums: bool = False) -> torch.Tensor:
     return buf
 
 
+def sage_merge_states(out_parts: torch.Tensor, lse_parts: torch.Tensor, *, tensor_layout: str = "HND",
+                      return_lse: bool = True, out: Optional[torch.Tensor] = None):
+    """Combine attention results over S disjoint key sets of the same queries
+    (the consumer of return_lse, deployment guide sec. 4.1).
+
+    out_parts: fp16/bf16 [S, B, H, N, d] (HND) or [S, B, N, H, d] (NHD), the
+    normalised outputs of the S sets; lse_parts: fp32 [S, B, H, N], their
+    natural-log LSEs.  Returns out (layout of one part) and, with return_lse,
+    the merged fp32 LSE [B, H, N]."""
+    L = A.load()
+    if out_parts.dim() != 5 or lse_parts.dim() != 4:
+        raise ValueError("out_parts must be 5-D [S, ...] and lse_parts 4-D [S, B, H, N]")
+    if out_parts.dtype not in _DT:
+        raise ValueError("out_parts must be fp16 or bf16")
+    if lse_parts.dtype != torch.float32 or not lse_parts.is_contiguous():
+        raise ValueError("lse_parts must be contiguous fp32")
+    if out_parts.stride(-1) != 1:
+        raise ValueError("the last dimension of out_parts must be contiguous")
+    S = out_parts.shape[0]
+    if tensor_layout == "HND":
+        _, B, H, N, d = out_parts.shape
+        ps = (out_parts.stride(0), out_parts.stride(1), out_parts.stride(2), out_parts.stride(3))
+    elif tensor_layout == "NHD":
+        _, B, N, H, d = out_parts.shape
+        ps = (out_parts.stride(0), out_parts.stride(1), out_parts.stride(3), out_parts.stride(2))
+    else:
+        raise ValueError(f"tensor_layout must be HND or NHD, got {tensor_layout!r}")
+    if tuple(lse_parts.shape) != (S, B, H, N):
+        raise ValueError(f"lse_parts shape {tuple(lse_parts.shape)} != {(S, B, H, N)}")
+    if out is None:
+        out = torch.empty(out_parts.shape[1:], dtype=out_parts.dtype, device=out_parts.device)
+    if out.stride(-1) != 1:
+        raise ValueError("the last dimension of out must be contiguous")
+    os_ = (out.stride(0), out.stride(1), out.stride(2)) if tensor_layout == "HND" else \
+        (out.stride(0), out.stride(2), out.stride(1))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=out_parts.device) if return_lse else None
+    p = A.MergeParams()
+    p.struct_size = ctypes.sizeof(A.MergeParams)
+    p.n_parts, p.dtype, p.B, p.H, p.N, p.d = S, _DT[out_parts.dtype], B, H, N, d
+    p.parts = _ptr(out_parts)
+    p.ps_s, p.ps_b, p.ps_h, p.ps_n = ps
+    p.lse_parts = _ptr(lse_parts)
+    p.out = _ptr(out)
+    p.o_stride_b, p.o_stride_h, p.o_stride_n = os_
+    p.lse = _ptr(lse)
+    A.check(L.sage_merge_states(ctypes.byref(p), _stream()))
+    return (out, lse) if return_lse else out
+
+
 def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND",
              is_causal: bool = False, sm_scale: Optional[float] = None, return_lse: bool = False, *,
              qk_quant_gran: str = "per_thread", pv_accum_dtype: str = "fp32+fp32", smooth_k: bool = True,

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsage.so")
-SOURCES = ["quant.hip", "attn.hip", "sage_api.hip"]
+SOURCES = ["quant.hip", "attn.hip", "merge.hip", "sage_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = [

@@ -359,4 +359,42 @@ int sage_debug_qk_scores(const sage_attn_params* p, int mode, void* scores, void
     return ok();
 }
 
+int sage_merge_states(const sage_merge_params* p, void* stream) {
+    if (!p) return fail(SAGE_EINVAL, "params is NULL");
+    if (p->struct_size < sizeof(sage_merge_params)) return fail(SAGE_EINVAL, "struct_size too small");
+    if (p->n_parts < 1 || p->n_parts > 64) return fail(SAGE_EINVAL, "n_parts %d must be 1..64", p->n_parts);
+    if (p->B < 1 || p->H < 1 || p->N < 1) return fail(SAGE_EINVAL, "sizes must be >= 1 (B=%d H=%d N=%d)", p->B, p->H, p->N);
+    if (p->d < 1 || p->d > 1024) return fail(SAGE_EINVAL, "d %d must be 1..1024", p->d);
+    if ((int64_t)p->B * p->H * p->N > ((int64_t)1 << 40) / p->d) return fail(SAGE_EINVAL, "sizes too large");
+    if (!valid_dtype(p->dtype)) return fail(SAGE_EINVAL, "invalid dtype %d", p->dtype);
+    if (!p->parts || !p->lse_parts || !p->out) return fail(SAGE_EINVAL, "NULL pointer");
+    if (!aligned(p->parts, 2) || !aligned(p->out, 2) || !aligned(p->lse_parts, 4) || (p->lse && !aligned(p->lse, 4)))
+        return fail(SAGE_EINVAL, "misaligned pointer");
+    sage::MergeArgs a{};
+    a.parts = p->parts;
+    a.ps = p->ps_s;
+    a.pb = p->ps_b;
+    a.ph = p->ps_h;
+    a.pn = p->ps_n;
+    a.lse_parts = p->lse_parts;
+    a.out = p->out;
+    a.ob = p->o_stride_b;
+    a.oh = p->o_stride_h;
+    a.on = p->o_stride_n;
+    a.lse = p->lse;
+    a.S = p->n_parts;
+    a.B = p->B;
+    a.H = p->H;
+    a.N = p->N;
+    a.d = p->d;
+    // 16-byte pieces of every row: d and every stride a multiple of 8 elements, bases 16-byte aligned
+    const bool vec = p->d % 8 == 0 && aligned(p->parts, 16) && aligned(p->out, 16) && p->ps_s % 8 == 0 &&
+                     p->ps_b % 8 == 0 && p->ps_h % 8 == 0 && p->ps_n % 8 == 0 && p->o_stride_b % 8 == 0 &&
+                     p->o_stride_h % 8 == 0 && p->o_stride_n % 8 == 0;
+    if (int r = hip_status(sage::launch_merge(a, p->dtype == SAGE_BF16, vec, reinterpret_cast<hipStream_t>(stream)),
+                           "merge launch"))
+        return r;
+    return ok();
+}
+
 }  // extern "C"

@@ -82,6 +82,17 @@ struct AttnArgs {
     int dbg_mode;
 };
 
+// Merge of partial attention results over disjoint key sets (merge.hip).
+struct MergeArgs {
+    const void* parts;           // part s, row (b, h, n), channel c at parts + s*ps + b*pb + h*ph + n*pn + c
+    int64_t ps, pb, ph, pn;
+    const float* lse_parts;      // [S][B][H][N], natural log
+    void* out;                   // row (b, h, n) at out + b*ob + h*oh + n*on
+    int64_t ob, oh, on;
+    float* lse;                  // [B][H][N] or null
+    int S, B, H, N, d;
+};
+
 // Launchers (defined in the kernel translation units).  Each returns the
 // hipError_t of the launch.
 // Q and K: Q tiles and the K statistics (smooth) in one launch, then the K
@@ -99,6 +110,8 @@ hipError_t launch_quant_qkv(const QuantRowsArgs& q, const QuantRowsArgs& k, cons
 hipError_t launch_attn(const AttnArgs& a, int dp, int pv /*0 fp8, 1 fp16, 2 bf16*/, bool out_bf16,
                        hipStream_t s);
 hipError_t launch_qk_scores(const AttnArgs& a, int dp, hipStream_t s);
+// vec: d % 8 == 0 and every part/out row start 16-byte aligned (8 channels per thread)
+hipError_t launch_merge(const MergeArgs& a, bool bf16, bool vec, hipStream_t s);
 
 // Statistics chunks: kStatsChunk tokens, or longer for long sequences so
 // that a (b, h) has at most kMaxChunks partials (every tile workgroup of the

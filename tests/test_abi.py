@@ -45,6 +45,7 @@ def test_struct_layouts_match_c(tmp_path):
         "sage_quant_qk_params": A.QuantQKParams,
         "sage_quant_v_params": A.QuantVParams,
         "sage_attn_params": A.AttnParams,
+        "sage_merge_params": A.MergeParams,
     }
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "sage.h"', "int main(void) {"]
     for cname, py in structs.items():
@@ -254,3 +255,43 @@ def test_quant_qkv_null_params(lib):
     pk, pv = _qkv_valid()
     assert lib.sage_quant_qkv(None, ctypes.byref(pv), None) == A.SAGE_EINVAL
     assert lib.sage_quant_qkv(ctypes.byref(pk), None, None) == A.SAGE_EINVAL
+
+
+def _merge_valid():
+    p = A.MergeParams()
+    p.struct_size = ctypes.sizeof(p)
+    p.n_parts, p.dtype, p.B, p.H, p.N, p.d = 2, A.SAGE_F16, 2, 4, 100, 128
+    p.parts = FAKE
+    p.ps_s, p.ps_b, p.ps_h, p.ps_n = 2 * 4 * 100 * 128, 4 * 100 * 128, 100 * 128, 128
+    p.lse_parts, p.out, p.lse = FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000
+    p.o_stride_b, p.o_stride_h, p.o_stride_n = 4 * 100 * 128, 100 * 128, 128
+    return p
+
+
+MERGE_BREAKS = {
+    "struct_size": lambda p: setattr(p, "struct_size", 8),
+    "no parts": lambda p: setattr(p, "n_parts", 0),
+    "65 parts": lambda p: setattr(p, "n_parts", 65),
+    "d = 0": lambda p: setattr(p, "d", 0),
+    "d = 1025": lambda p: setattr(p, "d", 1025),
+    "N = 0": lambda p: setattr(p, "N", 0),
+    "dtype": lambda p: setattr(p, "dtype", 4),
+    "null parts": lambda p: setattr(p, "parts", None),
+    "null lse_parts": lambda p: setattr(p, "lse_parts", None),
+    "null out": lambda p: setattr(p, "out", None),
+    "parts misaligned": lambda p: setattr(p, "parts", FAKE + 1),
+    "lse_parts misaligned": lambda p: setattr(p, "lse_parts", FAKE + 0x1000002),
+    "lse misaligned": lambda p: setattr(p, "lse", FAKE + 0x3000001),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MERGE_BREAKS))
+def test_merge_rejects(lib, case):
+    p = _merge_valid()
+    MERGE_BREAKS[case](p)
+    assert lib.sage_merge_states(ctypes.byref(p), None) == A.SAGE_EINVAL
+    assert len(lib.sage_last_error()) > 0
+
+
+def test_merge_null_params(lib):
+    assert lib.sage_merge_states(None, None) == A.SAGE_EINVAL

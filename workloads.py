@@ -153,3 +153,29 @@ def attention_ops(w: Workload, lens=None) -> float:
     else:
         ops = 4.0 * w.B * w.Hq * float(w.Nq) * float(w.Nk) * w.d
     return ops / 2.0 if w.causal else ops
+
+
+def make_merge_inputs(seed: int, S: int, B: int, H: int, N: int, d: int, dtype: str = "fp16",
+                      layout: str = "HND", empty_part_frac: float = 0.05, empty_row_frac: float = 0.01) -> dict:
+    """Seeded inputs of the merge of partial attention results.
+
+    Recipe: one PCG64 generator seeded with ``seed`` draws, in this order,
+    the S partial outputs as standard normals in fp32 (shape (S, B, H, N, d)
+    for HND, (S, B, N, H, d) for NHD), the S log-sum-exp values per row as
+    normals with mean 8 and standard deviation 2 (fp32, (S, B, H, N)), a
+    uniform [0, 1) draw per (part, row) that marks the part empty (LSE =
+    -inf, it saw no key) below ``empty_part_frac``, and a uniform draw per row
+    that marks the whole row empty below ``empty_row_frac``; the outputs are
+    then rounded once to fp16/bf16 (nearest even).  An empty part's output is
+    zero, as the forward writes it."""
+    rng = np.random.default_rng(seed)
+    shape = (S, B, H, N, d) if layout == "HND" else (S, B, N, H, d)
+    o = rng.standard_normal(shape, dtype=np.float32)
+    lse = (8.0 + 2.0 * rng.standard_normal((S, B, H, N))).astype(np.float32)
+    empty = rng.random((S, B, H, N)) < empty_part_frac
+    empty |= (rng.random((B, H, N)) < empty_row_frac)[None]
+    lse[empty] = -np.inf
+    mask = empty if layout == "HND" else np.transpose(empty, (0, 1, 3, 2))
+    o[mask] = 0.0
+    return {"out_parts": round_to(o, dtype), "lse_parts": torch.from_numpy(lse), "layout": layout,
+            "dtype": dtype, "shape": (S, B, H, N, d)}
