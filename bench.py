@@ -12,7 +12,9 @@ events on the stream it runs on; `cpu_baseline` is the CPU oracle timed on a
 bounded sample of the same workload; `secondary` gives the attention kernel's
 TOPS on the 17 550-token video-DiT shape (B=1, H=48, d=64), the metric's
 other sequence length; `merge` gives the HBM throughput of sage_merge_states
-combining two partial results of the workload's output shape.
+combining two partial results of the workload's output shape; `vs_torch_sdpa`
+times sageattn against torch's scaled_dot_product_attention on the WSL page's
+comparison shape and on the benchmark workload.
 """
 from __future__ import annotations
 
@@ -170,6 +172,53 @@ def time_merge(w, parts: int = 2, iters: int = 20) -> dict:
                          "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 8e12, 4)}}
 
 
+def time_vs_sdpa(w, warmup: int = 10, iters: int = 100) -> dict:
+    """sageattn (quantize + attention, default knobs) against PyTorch's
+    scaled_dot_product_attention on the same fp16 inputs, the comparison the
+    WSL page makes (section 5: B=8, H=32, N=2048, d=128, fp16, 10 warmup and
+    100 timed calls).  SDPA may use its flash or memory-efficient kernels; the
+    math fallback is excluded."""
+    import torch
+    import quantized_attention_smooth_amd as sage
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import workloads
+
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    rec = {"workload": f"B{w.B} H{w.Hq} N{w.Nq} d{w.d} {w.dtype} {w.layout}, non-causal", "warmup": warmup,
+           "iters": iters}
+    sage_ms = timed(lambda: sage.sageattn(q, k, v))
+    rec["sageattn_ms"] = round(sage_ms, 4)
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+            sdpa_ms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v))
+            ref = torch.nn.functional.scaled_dot_product_attention(q, k, v).float()
+        got = sage.sageattn(q, k, v).float()
+        torch.cuda.synchronize()
+        rec["sdpa_ms"] = round(sdpa_ms, 4)
+        rec["speedup"] = round(sdpa_ms / sage_ms, 3)
+        rec["cosine_vs_sdpa"] = round(float(torch.nn.functional.cosine_similarity(
+            got.flatten(), ref.flatten(), dim=0)), 6)
+    except RuntimeError as e:                  # no fused SDPA kernel for this shape/dtype
+        rec["sdpa_error"] = str(e)[:200]
+    return rec
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,6 +228,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-merge", action="store_true", help="skip timing sage_merge_states")
+    ap.add_argument("--no-sdpa", action="store_true", help="skip the comparison with torch SDPA")
     ap.add_argument("--secondary", default="video_dit_n17550",
                     help="a second workload whose attention-kernel TOPS is reported beside the main line "
                          "('none' to skip); the metric is quoted at sequence 4096 and 17.5k")
@@ -242,6 +292,8 @@ def main() -> int:
                             "step_tops": round(ops2 / (ms2 * 1e-3) / 1e12, 2), "quant_ms": round(qms2, 4),
                             "attn_kernel_ms": round(ams2, 4), "attn_kernel_tops": round(at2, 2),
                             "attn_pct_of_peak": round(100.0 * at2 / PEAK_TOPS[w2.v_dtype], 2)}
+    if not args.no_sdpa:
+        rec["vs_torch_sdpa"] = [time_vs_sdpa(workloads.WORKLOADS["wsl_sdpa_b8h32n2048d128"]), time_vs_sdpa(w)]
     if not args.no_merge:
         rec["merge"] = time_merge(w)
     if not args.no_cpu_baseline:

@@ -83,6 +83,12 @@ WORKLOADS = {
                              layout="NHD", causal=True, gran="per_thread", v_dtype="fp8", pv_accum="fp32+fp32",
                              smooth_k=True, smooth_v=False, return_lse=False, seed=5,
                              varlen=True, len_lo=128, len_hi=4096),
+    # the WSL page's timing comparison with torch's attention (section 5: batch 8, 32 heads, 2048 tokens,
+    # head_dim 128, fp16), run with sageattn's default knobs
+    "wsl_sdpa_b8h32n2048d128": Workload("wsl_sdpa_b8h32n2048d128", B=8, Hq=32, Hkv=32, Nq=2048, Nk=2048, d=128,
+                                        dtype="fp16", layout="HND", causal=False, gran="per_thread",
+                                        v_dtype="fp8", pv_accum="fp32+fp32", smooth_k=True, smooth_v=False,
+                                        return_lse=False, seed=6),
 }
 
 # the order in which the workloads are listed as configurations
