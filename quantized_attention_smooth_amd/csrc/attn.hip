@@ -540,7 +540,12 @@ __device__ __forceinline__ bool softmax_half(const v16i (&S)[2], const float (&k
 // loop interleaves with MFMAs: head<0..3>() compute the scale factors and the
 // tile maximum and take the raise decision (the same steps and roundings as
 // softmax_half), piece<E>() turns the lane's 32 keys into P two at a time.
-template <int PV>
+// KS16: the tile has four K-scale groups of 16 keys; otherwise one group of
+// 64 keys, whose scale the four slots of ksv repeat, so that one scale
+// factor, one exponent offset and one maximum serve the whole tile (the same
+// values as the four-group steps give: the factor is >= 0, so scaling the
+// integer maximum equals the maximum of the scaled groups).
+template <int PV, bool KS16 = true>
 struct SoftmaxPieces {
     static constexpr float p_log2_scale = PV == 0 ? kLog2_448 - (float)kTau : 0.f;
     float f[4], cg[4], smax;
@@ -585,19 +590,36 @@ struct SoftmaxPieces {
     // head<>()).  A row that does not raise keeps its maximum, so its
     // speculative P is exact; a wavefront with a raising row redoes P.
     __device__ __forceinline__ void prep(const float (&ksv)[4], float cq) {
+        if constexpr (KS16) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) f[g] = ksv[g] * cq;
+            for (int g = 0; g < 4; ++g) f[g] = ksv[g] * cq;
+        } else {
+            const float f0 = ksv[0] * cq;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) f[g] = f0;
+        }
     }
     __device__ __forceinline__ void gmax(const v16i& Sk, int g) { group_max(Sk, g); }
     __device__ __forceinline__ void spec(float m_ref) {
         const float nb = p_log2_scale - m_ref;
+        if constexpr (KS16) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) cg[g] = __builtin_fmaf(-kAccBias, f[g], nb);
+            for (int g = 0; g < 4; ++g) cg[g] = __builtin_fmaf(-kAccBias, f[g], nb);
+        } else {
+            const float c0 = __builtin_fmaf(-kAccBias, f[0], nb);
+#pragma unroll
+            for (int g = 0; g < 4; ++g) cg[g] = c0;
+        }
     }
     __device__ __forceinline__ void decide(float& m_ref, float& m_prev) {
-        smax = -INFINITY;
+        if constexpr (KS16) {
+            smax = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) smax = fmaxf(smax, (bits_f(mi[g]) - kAccBias) * f[g]);
+            for (int g = 0; g < 4; ++g) smax = fmaxf(smax, (bits_f(mi[g]) - kAccBias) * f[g]);
+        } else {
+            const int m4 = max(max(mi[0], mi[1]), max(mi[2], mi[3]));
+            smax = (bits_f(m4) - kAccBias) * f[0];
+        }
         smax = swap_half_max(smax);
         m_prev = m_ref;
         raise = smax > m_ref + (float)kTau;
@@ -1036,7 +1058,7 @@ __device__ __forceinline__ void pv8_all(const VA<DP, 0>& va, const PHalf<0>& P, 
 constexpr int kWaves8 = 8;
 constexpr int kThreads8 = 64 * kWaves8;
 
-template <int DP, bool OUT_BF16>
+template <int DP, bool OUT_BF16, bool KS16>
 __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     constexpr int PV = 0, NW = kWaves8;                 // every wavefront copies its share
     using C = AttnCfg<DP, PV, NW, NW>;
@@ -1175,7 +1197,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     static_assert(NPV + NRS >= 3, "room for the group maxima");
     // u = t % NST as a compile-time constant: every LDS address of the step
     // is a fixed offset from one base
-    auto regionH = [&](auto u, int t, SoftmaxPieces<PV>& sp) {
+    auto regionH = [&](auto u, int t, SoftmaxPieces<PV, KS16>& sp) {
         constexpr int U = decltype(u)::value;
         const int tc = min(t + AHEAD, ntiles - 1);
         uint8_t* st_copy = smem + ((U + AHEAD) % NST) * C::STAGE;
@@ -1216,10 +1238,10 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         }
         wait_vmcnt<LPT * (AHEAD - 3)>();                // own share of tile t+3 has landed
     };
-    auto regionE = [&](SoftmaxPieces<PV>& sp) {
+    auto regionE = [&](SoftmaxPieces<PV, KS16>& sp) {
         if (!live) return;
         sp.spec(m_ref);
-        static_for<0, SoftmaxPieces<PV>::NPIECE>([&](auto ec) {
+        static_for<0, SoftmaxPieces<PV, KS16>::NPIECE>([&](auto ec) {
             constexpr int e = decltype(ec)::value;
             sp.template piece<e>(S, P);
             if constexpr (e == 1) sp.decide(m_ref, m_prev);
@@ -1227,14 +1249,14 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         if (__any(sp.raise)) {                          // rare: some row raised its maximum
             rescale_half<DP>(m_ref, m_prev, o, ls);
             sp.spec(m_ref);
-            static_for<0, SoftmaxPieces<PV>::NPIECE>([&](auto ec) { sp.template piece<decltype(ec)::value>(S, P); });
+            static_for<0, SoftmaxPieces<PV, KS16>::NPIECE>([&](auto ec) { sp.template piece<decltype(ec)::value>(S, P); });
         }
         keep_here<PV>(P);
     };
     // both groups pass one barrier per step (see above); a last barrier
     // after the loop orders every wavefront's final waits before the tail
     auto step = [&](auto u, int t) {
-        SoftmaxPieces<PV> sp;
+        SoftmaxPieces<PV, KS16> sp;
         if (!lead_wave) block_sync();
         regionH(u, t, sp);
         if (lead_wave) block_sync();
@@ -1412,8 +1434,14 @@ __global__ __launch_bounds__(kThreads) void qk_scores_kernel(AttnArgs a) {
 template <int DP, int PV>
 static void attn_dispatch_out(const AttnArgs& a, bool out_bf16, hipStream_t s) {
     if constexpr (PV == 0) {
-        if (out_bf16) attn8_fwd_kernel<DP, true><<<a.num_wg, kThreads8, 0, s>>>(a);
-        else attn8_fwd_kernel<DP, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+        const bool ks16 = a.gk_shift == 4;              // per_thread K groups of 16 keys
+        if (out_bf16) {
+            if (ks16) attn8_fwd_kernel<DP, true, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+            else attn8_fwd_kernel<DP, true, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+        } else {
+            if (ks16) attn8_fwd_kernel<DP, false, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+            else attn8_fwd_kernel<DP, false, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+        }
     } else {
         if (out_bf16) attn_fwd_kernel<DP, PV, true><<<a.num_wg, kThreads, 0, s>>>(a);
         else attn_fwd_kernel<DP, PV, false><<<a.num_wg, kThreads, 0, s>>>(a);

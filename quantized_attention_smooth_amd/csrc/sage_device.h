@@ -70,9 +70,12 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 }
 
 __device__ __forceinline__ float swap_half_max(float x) {
-    // max over lanes l and l ^ 32
+    // max over lanes l and l ^ 32; x is never NaN here, so the plain
+    // instruction serves (fmaxf would first quiet both operands)
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
-    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+    float m;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m) : "v"(__int_as_float(r[0])), "v"(__int_as_float(r[1])));
+    return m;
 }
 __device__ __forceinline__ float swap_half_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
