@@ -14,7 +14,8 @@ TOPS on the 17 550-token video-DiT shape (B=1, H=48, d=64), the metric's
 other sequence length; `merge` gives the HBM throughput of sage_merge_states
 combining two partial results of the workload's output shape; `vs_torch_sdpa`
 times sageattn against torch's scaled_dot_product_attention on the WSL page's
-comparison shape and on the benchmark workload.
+comparison shape and on the benchmark workload; `splitkv` compares the plain
+kernel with the split-KV forward on a 16-query, 32 768-key GQA shape.
 """
 from __future__ import annotations
 
@@ -172,6 +173,51 @@ def time_merge(w, parts: int = 2, iters: int = 20) -> dict:
                          "unit": "GB/s", "frac": round(nbytes / (us * 1e-6) / 8e12, 4)}}
 
 
+def time_splitkv(w, iters: int = 20) -> dict:
+    """Attention on a few-queries / many-keys shape: the plain kernel (one
+    workgroup per 256-query tile) against the split-KV forward (key ranges in
+    parallel, merged by LSE).  Bound by HBM: the algorithmic bytes are the
+    INT8 K and FP8 V^T read once, Q8 and the output."""
+    import torch
+    import workloads
+    import quantized_attention_smooth_amd as sage
+
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    qk, qv = sage.sage_quant_qkv(q, k, v, tensor_layout=w.layout, qk_quant_gran=w.gran, smooth_k=w.smooth_k,
+                                 v_dtype=w.v_dtype, smooth_v=w.smooth_v)
+    ns = sage.splitkv_plan(w.B, w.Hq, w.Nq, w.Nk)
+    ws = torch.empty(int(sage.load_library().sage_attn_splitkv_workspace_size(w.B, w.Hq, w.Nq, w.Nk, w.d, ns)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / iters
+
+    plain = timed(lambda: sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, out=out))
+    split = timed(lambda: sage.sage_attn_fwd_splitkv(qk, qv, n_splits=ns, tensor_layout=w.layout, out=out,
+                                                     workspace=ws))
+    dp = 64 if w.d <= 64 else 128
+    nk_pad = -(-w.Nk // 128) * 128
+    nbytes = w.B * w.Hkv * nk_pad * dp * 2 + w.B * w.Hq * w.Nq * (dp + 2 * w.d)
+    gbps = nbytes / (split * 1e-6) / 1e9
+    return {"workload": f"B{w.B} Hq{w.Hq} Hkv{w.Hkv} Nq{w.Nq} Nk{w.Nk} d{w.d} {w.dtype} {w.layout} {w.gran}",
+            "n_splits": ns, "plain_us": round(plain, 2), "splitkv_us": round(split, 2),
+            "speedup": round(plain / split, 2), "bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": 8000.0, "unit": "GB/s",
+                         "frac": round(gbps / 8000.0, 4)}}
+
+
 def time_vs_sdpa(w, warmup: int = 10, iters: int = 100) -> dict:
     """sageattn (quantize + attention, default knobs) against PyTorch's
     scaled_dot_product_attention on the same fp16 inputs, the comparison the
@@ -296,6 +342,7 @@ def main() -> int:
         rec["vs_torch_sdpa"] = [time_vs_sdpa(workloads.WORKLOADS["wsl_sdpa_b8h32n2048d128"]), time_vs_sdpa(w)]
     if not args.no_merge:
         rec["merge"] = time_merge(w)
+        rec["splitkv"] = time_splitkv(workloads.WORKLOADS["decode_gqa_b4_q16_k32768"])
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(rec), flush=True)

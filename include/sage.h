@@ -246,6 +246,31 @@ int sage_attn_varlen_fwd(const sage_attn_varlen_params* p, void* stream);
 int sage_debug_qk_scores(const sage_attn_params* p, int mode, void* scores, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * sage_attn_fwd_splitkv: sage_attn_fwd for few queries against many keys
+ * (deployment guide sec. 4.1: q and k/v lengths may differ, e.g. encoder-
+ * decoder attention or decoding against a long context), where one workgroup
+ * per 256-query tile would leave most of the GPU idle.  The keys are cut into
+ * ranges of split_len = round_up(ceil(Nk / n_splits), 128) keys (the last one
+ * shorter; ranges that would be empty are dropped, so S = ceil(Nk /
+ * split_len) <= n_splits).  Each range runs the same online softmax as
+ * sage_attn_fwd, starting afresh at its first key; its normalised output is
+ * rounded to out_dtype and stored with its log-sum-exp in the workspace, and
+ * the S partial results are then combined as sage_merge_states does.  With
+ * S = 1 the result is bit-identical to sage_attn_fwd.
+ * Same parameters and layouts as sage_attn_fwd; FP8 V and non-causal only.
+ * workspace: device memory, 256-byte aligned, of at least
+ * sage_attn_splitkv_workspace_size(B, Hq, Nq, Nk, d, n_splits) bytes (0 for
+ * invalid sizes); it holds S x [B][Hq][Nq][d] outputs and S x [B][Hq][Nq]
+ * fp32 LSEs and need not be initialised.
+ * Errors: as sage_attn_fwd; SAGE_EINVAL for n_splits outside 1..64 or a
+ * missing, misaligned or too small workspace; SAGE_EUNSUPPORTED for fp16/bf16
+ * V or is_causal.
+ * ------------------------------------------------------------------------- */
+size_t sage_attn_splitkv_workspace_size(int B, int Hq, int Nq, int Nk, int d, int n_splits);
+int sage_attn_fwd_splitkv(const sage_attn_params* p, int n_splits, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* ---------------------------------------------------------------------------
  * sage_merge_states: combine attention results computed over S disjoint key
  * sets of the same queries, using the log-sum-exp each one returned
  * (deployment guide sec. 4.1: return_lse, for Ring-Attention-style use).

@@ -355,3 +355,87 @@ def merge_states(out_parts: np.ndarray, lse_parts: np.ndarray):
     out[empty] = 0.0
     L = np.where(empty, -np.inf, m_safe + np.log(W_safe))
     return out, L
+
+
+def splitkv_ranges(nk: int, n_splits: int):
+    """Key ranges of the split-KV forward as the library defines them: ranges
+    of round_up(ceil(nk / n_splits), 128) keys, the last one shorter, none
+    empty."""
+    per = -(-nk // n_splits)
+    slen = -(-per // 128) * 128
+    return [(a, min(nk, a + slen)) for a in range(0, nk, slen)]
+
+
+def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str, n_splits: int,
+                              layout: str = "HND", sm_scale: Optional[float] = None, gran: str = "per_thread",
+                              smooth_k: bool = True, smooth_v: bool = False,
+                              rows: Optional[Callable[[int, int], np.ndarray]] = None) -> dict:
+    """The split-KV forward (few queries against many keys; FP8 V, non-causal)
+    step by step: quantize Q, K, V over the whole sequence as
+    reference_forward does; for each key range (splitkv_ranges) run the
+    online-softmax attention of that range alone, starting afresh at its first
+    key ([guide] sec. 4.1: q and k/v lengths may differ), and round its
+    normalised output to the input dtype; combine the ranges with merge_states
+    (the return_lse merge of [guide] sec. 4.1).
+
+    Returns per sequence b: out[b] (Hq, nrows, d) fp64 merged output before
+    its final rounding, lse[b] (Hq, nrows), allow[b] (Hq, nrows, d): the
+    per-range flip allowances plus one output ulp of each rounded range
+    output, weighted as in the merge; parts_scale[b] (Hq, nrows): the largest
+    |range output| of the row; rows[b]."""
+    d = q.shape[-1]
+    dp = padded_head_dim(d)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    sm32 = float(np.float32(sm_scale))
+    gq, gk = Q_GROUP[gran], K_GROUP[gran]
+    qz = reference_forward(q, k, v, dtype=dtype, layout=layout, gran=gran, v_dtype="fp8", smooth_k=smooth_k,
+                           smooth_v=smooth_v, attention=False)
+    mbits, emin = (7, -126) if dtype == "bf16" else (10, -14)
+    L = lib()
+    res = {"out": [], "lse": [], "allow": [], "parts_scale": [], "rows": []}
+    for b in range(len(qz["q8"])):
+        q8, qs = qz["q8"][b], qz["q_scale"][b]
+        k8, ks, km = qz["k8"][b], qz["k_scale"][b], qz["k_mean"][b]
+        v8, vs, vm = qz["v8"][b], qz["v_scale"][b], qz["v_mean"][b]
+        hq, nq = q8.shape[0], q8.shape[1]
+        hkv, nk = k8.shape[0], k8.shape[1]
+        grp = hq // hkv
+        r = np.arange(nq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows(b, nq), dtype=np.int32)
+        res["rows"].append(r)
+        outs, lses, alws, scs = [], [], [], []
+        for h in range(hq):
+            hk = h // grp
+            qs_row = np.ascontiguousarray(np.repeat(qs[h], gq)[:nq], dtype=np.float32)
+            ks_key = np.repeat(ks[hk], gk)[:nk]
+            vval = e4m3_decode(v8[hk])
+            po, pl, pa = [], [], []
+            for a0, a1 in splitkv_ranges(nk, n_splits):
+                o = np.zeros((len(r), dp), dtype=np.float64)
+                ls = np.zeros(len(r), dtype=np.float64)
+                al = np.zeros((len(r), dp), dtype=np.float64)
+                rc = L.oracle_attn_rows(nq, a1 - a0, dp, _p(q8[h]), _p(qs_row),
+                                        _p(np.ascontiguousarray(k8[hk][a0:a1])),
+                                        _p(np.ascontiguousarray(ks_key[a0:a1], dtype=np.float32)),
+                                        _p(np.ascontiguousarray(vval[a0:a1], dtype=np.float32)), _p(vs[hk]),
+                                        _p(vm[hk] if smooth_v else None), _p(km[hk] if smooth_k else None),
+                                        sm32, 0, 0, DEFAULT_BK, DEFAULT_TAU, 0, len(r), _p(r), _p(o), _p(ls),
+                                        None, _p(al), None)
+                if rc != 0:
+                    raise RuntimeError(f"oracle_attn_rows failed ({rc})")
+                # the range's output, rounded to the output dtype as it is stored
+                po.append(round_half(o[:, :d].astype(np.float32), dtype).astype(np.float64))
+                pl.append(ls)
+                a = np.maximum(np.abs(o[:, :d]), 2.0 ** emin)
+                pa.append(al[:, :d] + np.exp2(np.floor(np.log2(a)) - mbits))
+            po, pl, pa = np.stack(po), np.stack(pl), np.stack(pa)
+            mo, ml = merge_states(po, pl)
+            m = pl.max(axis=0)
+            w = np.exp(pl - np.where(np.isneginf(m), 0.0, m)[None, :])
+            w = w / np.maximum(w.sum(axis=0), 1e-300)[None, :]
+            outs.append(mo); lses.append(ml)
+            alws.append(np.einsum("sr,srd->rd", w, pa))
+            scs.append(np.abs(po).max(axis=(0, 2)))
+        res["out"].append(np.stack(outs)); res["lse"].append(np.stack(lses))
+        res["allow"].append(np.stack(alws)); res["parts_scale"].append(np.stack(scs))
+    return res

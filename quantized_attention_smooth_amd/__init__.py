@@ -6,14 +6,15 @@ P.V with fp32 accumulation, FP16/BF16 output and optional LSE.  The compute
 lives in libsage.so (hand-written HIP for gfx950, C ABI in include/sage.h);
 this package only marshals arguments.
 """
-from .api import (QuantQK, QuantV, padded_head_dim, sage_attn_fwd, sage_attn_varlen_fwd,
+from .api import (QuantQK, QuantV, padded_head_dim, sage_attn_fwd, sage_attn_fwd_splitkv, sage_attn_varlen_fwd,
+                  splitkv_plan,
                   sage_debug_qk_scores, sage_merge_states, sage_quant_qk, sage_quant_qkv, sage_quant_v, sageattn,
                   sageattn_varlen, workspace_bytes)
 from ._abi import LIB_PATH, SageError, load as load_library
 
 __all__ = [
     "QuantQK", "QuantV", "padded_head_dim", "sage_attn_fwd", "sage_attn_varlen_fwd", "sage_debug_qk_scores",
-    "sage_merge_states",
+    "sage_merge_states", "sage_attn_fwd_splitkv", "splitkv_plan",
     "sage_quant_qk", "sage_quant_qkv", "sage_quant_v", "sageattn", "sageattn_varlen", "workspace_bytes", "LIB_PATH", "SageError",
     "load_library",
 ]

@@ -71,7 +71,8 @@ class MergeParams(ctypes.Structure):
 
 
 EXPORTS = ["sage_quant_qk", "sage_quant_workspace_size", "sage_quant_v", "sage_quant_qkv", "sage_attn_fwd",
-           "sage_attn_varlen_fwd", "sage_debug_qk_scores", "sage_merge_states", "sage_last_error", "sage_version"]
+           "sage_attn_varlen_fwd", "sage_debug_qk_scores", "sage_merge_states", "sage_attn_splitkv_workspace_size",
+           "sage_attn_fwd_splitkv", "sage_last_error", "sage_version"]
 
 _lib = None
 
@@ -101,6 +102,10 @@ def load(path: str = LIB_PATH):
     L.sage_attn_varlen_fwd.restype = I
     L.sage_debug_qk_scores.argtypes = [ctypes.POINTER(AttnParams), I, VP, VP]
     L.sage_debug_qk_scores.restype = I
+    L.sage_attn_fwd_splitkv.argtypes = [ctypes.POINTER(AttnParams), I, VP, SZ, VP]
+    L.sage_attn_fwd_splitkv.restype = I
+    L.sage_attn_splitkv_workspace_size.argtypes = [I, I, I, I, I, I]
+    L.sage_attn_splitkv_workspace_size.restype = SZ
     L.sage_merge_states.argtypes = [ctypes.POINTER(MergeParams), VP]
     L.sage_merge_states.restype = I
     L.sage_quant_workspace_size.argtypes = [I, I, I, I]

@@ -246,6 +246,37 @@ def sage_attn_fwd(qk: QuantQK, qv: QuantV, *, tensor_layout: str = "HND", is_cau
     return (out, lse) if return_lse else out
 
 
+def splitkv_plan(B: int, Hq: int, Nq: int, Nk: int, n_splits: Optional[int] = None) -> int:
+    """Number of key ranges to ask for: enough workgroups to fill the GPU
+    (about 512, two per compute unit) with ranges of at least 256 keys."""
+    if n_splits is not None:
+        return int(n_splits)
+    tiles = B * Hq * ((Nq + 255) // 256)
+    return max(1, min(64, -(-512 // tiles), Nk // 256))
+
+
+def sage_attn_fwd_splitkv(qk: QuantQK, qv: QuantV, *, n_splits: Optional[int] = None, tensor_layout: str = "HND",
+                          sm_scale: Optional[float] = None, return_lse: bool = False,
+                          pv_accum_dtype: str = "fp32+fp32", out: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None):
+    """sage_attn_fwd with the keys cut into ranges that run in parallel and are
+    merged by their log-sum-exp (few queries, many keys; FP8 V, non-causal)."""
+    L = A.load()
+    dev = qk.q8.device
+    if out is None:
+        shape = (qk.B, qk.Hq, qk.Nq, qk.d) if tensor_layout == "HND" else (qk.B, qk.Nq, qk.Hq, qk.d)
+        out = torch.empty(shape, dtype=qk.dtype, device=dev)
+    g = _geometry(out, tensor_layout, None, None)
+    lse = torch.empty((qk.B, qk.Hq, qk.Nq), dtype=torch.float32, device=dev) if return_lse else None
+    ns = splitkv_plan(qk.B, qk.Hq, qk.Nq, qk.Nk, n_splits)
+    need = int(L.sage_attn_splitkv_workspace_size(qk.B, qk.Hq, qk.Nq, qk.Nk, qk.d, ns))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    p = _attn_params(qk, qv, out, lse, False, sm_scale, pv_accum_dtype, (g.sb, g.sh, g.sn))
+    A.check(L.sage_attn_fwd_splitkv(ctypes.byref(p), ns, _ptr(workspace), workspace.numel(), _stream()))
+    return (out, lse) if return_lse else out
+
+
 def sage_attn_varlen_fwd(qk: QuantQK, qv: QuantV, cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
                          total_q: int, *, is_causal: bool = False, sm_scale: Optional[float] = None,
                          return_lse: bool = False, pv_accum_dtype: str = "fp32+fp32",

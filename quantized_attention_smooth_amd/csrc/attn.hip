@@ -1073,7 +1073,12 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const int n = lane & 31, hh = lane >> 5;
     const bool lead_wave = wave < kWaves8 / 2;          // wave-uniform: wavefronts 0-3 lead by half a step
 
-    const int wg = xcd_remap(blockIdx.x, a.num_wg);
+    int wg = xcd_remap(blockIdx.x, a.num_wg);
+    int split = 0;
+    if (a.n_splits > 1) {                               // split-KV: consecutive workgroups, consecutive key ranges
+        split = wg % a.n_splits;
+        wg /= a.n_splits;
+    }
     int qt = wg % a.n_qtiles;
     const int bh = wg / a.n_qtiles, h = bh % a.Hq, b = bh / a.Hq;
     if (a.causal) qt = a.n_qtiles - 1 - qt;
@@ -1083,6 +1088,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         Lq = a.cu_q[b + 1] - qoff;
         Lk = a.cu_k[b + 1] - a.cu_k[b];
     }
+    const int kb0 = split * a.split_len;                // first key of this workgroup's range
+    if (a.n_splits > 1) Lk = min(Lk - kb0, a.split_len);
     const int q0 = qt * kBQ;
     if (q0 >= Lq) return;
     const int hk = h / (a.Hq / a.Hkv);
@@ -1109,9 +1116,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const float cq = (qscale * a.sm_scale) * kLog2e;
 
     const int64_t khead = (int64_t)b * a.Hkv + hk;
-    const int8_t* kbase = a.k8 + khead * a.nk_pad * DP;
-    const float* ksbase = a.ks + khead * (a.nk_pad >> a.gk_shift);
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vt) + khead * DP * a.nk_pad;
+    const int8_t* kbase = a.k8 + khead * a.nk_pad * DP + (int64_t)kb0 * DP;
+    const float* ksbase = a.ks + khead * (a.nk_pad >> a.gk_shift) + (kb0 >> a.gk_shift);
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vt) + khead * DP * a.nk_pad + kb0;
     const int64_t vrow_stride = a.nk_pad;
     const bool ks16 = a.gk_shift == 4;
 
@@ -1138,8 +1145,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         for (int g = 0; g < 4; ++g) ksv[g] = k4[g];
     };
     const TileCopyBuf<DP, PV, NW, NW> copier(kbase, vbase, (uint32_t)vrow_stride, ksbase,
-                                                  (uint32_t)a.nk_pad * DP, (uint32_t)a.nk_pad * DP,
-                                                  (uint32_t)(a.nk_pad >> a.gk_shift) * 4u, ks16, wave, lane);
+                                                  (uint32_t)(a.nk_pad - kb0) * DP, (uint32_t)(a.nk_pad * DP - kb0),
+                                                  (uint32_t)((a.nk_pad - kb0) >> a.gk_shift) * 4u, ks16, wave, lane);
     auto issue = [&](int t) {
         if (t < ntiles) copier.issue_all(stage_of(t), t);
     };
@@ -1305,7 +1312,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const float l_tot = ls[0];
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (qrow < Lq) {
-        uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) +
+        uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + split * a.split_out +
                          (a.cu_q ? (int64_t)(qoff + qrow) * a.on + (int64_t)h * a.oh
                                  : (int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)qrow * a.on);
 #pragma unroll
@@ -1351,7 +1358,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         if (hh == 0 && qrow < Lq) {
             const float corr = a.kmean ? a.sm_scale * qscale * dot : 0.f;
             const float lse = (m_ref + __log2f(l_tot) - p_log2_scale) * kLn2 + corr;
-            const int64_t li = a.lse_varlen ? (int64_t)h * a.total_q + qoff + qrow : qhead * a.Nq + qrow;
+            const int64_t li = split * a.split_lse +
+                               (a.lse_varlen ? (int64_t)h * a.total_q + qoff + qrow : qhead * a.Nq + qrow);
             a.lse[li] = lse;
         }
     }
@@ -1451,7 +1459,8 @@ static void attn_dispatch_out(const AttnArgs& a, bool out_bf16, hipStream_t s) {
 hipError_t launch_attn(const AttnArgs& a_in, int dp, int pv, bool out_bf16, hipStream_t s) {
     AttnArgs a = a_in;
     a.n_qtiles = (a.Nq + kBQ - 1) / kBQ;
-    a.num_wg = a.B * a.Hq * a.n_qtiles;
+    if (a.n_splits < 1) a.n_splits = 1;
+    a.num_wg = a.B * a.Hq * a.n_qtiles * a.n_splits;
     if (dp == 128) {
         if (pv == 0) attn_dispatch_out<128, 0>(a, out_bf16, s);
         else if (pv == 1) attn_dispatch_out<128, 1>(a, out_bf16, s);

@@ -359,6 +359,82 @@ int sage_debug_qk_scores(const sage_attn_params* p, int mode, void* scores, void
     return ok();
 }
 
+namespace {
+struct SplitPlan {
+    int splits, split_len;
+    size_t parts_bytes, lse_bytes, total;
+};
+// Key ranges of n_splits requested splits: multiples of 128 keys, none empty.
+SplitPlan split_plan(int B, int Hq, int Nq, int Nk, int d, int n_splits) {
+    SplitPlan s{};
+    const int64_t per = (Nk + (int64_t)n_splits - 1) / n_splits;
+    s.split_len = (int)round_up(per, sage::kPad);
+    s.splits = (int)((Nk + (int64_t)s.split_len - 1) / s.split_len);
+    const size_t rows = (size_t)s.splits * B * Hq * Nq;
+    s.parts_bytes = (rows * d * 2 + 255) / 256 * 256;
+    s.lse_bytes = (rows * 4 + 255) / 256 * 256;
+    s.total = s.parts_bytes + s.lse_bytes;
+    return s;
+}
+}  // namespace
+
+size_t sage_attn_splitkv_workspace_size(int B, int Hq, int Nq, int Nk, int d, int n_splits) {
+    if (B < 1 || Hq < 1 || Nq < 1 || Nk < 1 || d < 1 || d > 128 || n_splits < 1 || n_splits > 64) return 0;
+    return split_plan(B, Hq, Nq, Nk, d, n_splits).total;
+}
+
+int sage_attn_fwd_splitkv(const sage_attn_params* p, int n_splits, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+    if (!p) return fail(SAGE_EINVAL, "params is NULL");
+    if (p->struct_size < sizeof(sage_attn_params)) return fail(SAGE_EINVAL, "struct_size too small");
+    if (int r = check_attn(p, false)) return r;
+    if (n_splits < 1 || n_splits > 64) return fail(SAGE_EINVAL, "n_splits %d must be 1..64", n_splits);
+    if (p->v_dtype != SAGE_V_FP8) return fail(SAGE_EUNSUPPORTED, "split-KV needs FP8 V");
+    if (p->is_causal) return fail(SAGE_EUNSUPPORTED, "split-KV is non-causal only");
+    const SplitPlan sp = split_plan(p->B, p->Hq, p->Nq, p->Nk, p->d, n_splits);
+    if (!workspace || !aligned(workspace, 256)) return fail(SAGE_EINVAL, "workspace NULL or not 256-byte aligned");
+    if (workspace_bytes < sp.total)
+        return fail(SAGE_EINVAL, "workspace too small: %zu < %zu bytes", workspace_bytes, sp.total);
+    const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const int64_t d = p->d, rows = (int64_t)p->B * p->Hq * p->Nq;
+    // partial results of split s: out [B][Hq][Nq][d] and LSE [B][Hq][Nq]
+    sage::AttnArgs a = attn_args(p);
+    a.out = ws;
+    a.ob = (int64_t)p->Hq * p->Nq * d;
+    a.oh = (int64_t)p->Nq * d;
+    a.on = d;
+    a.out_vec4 = d % 4 == 0;
+    a.lse = reinterpret_cast<float*>(ws + sp.parts_bytes);
+    a.n_splits = sp.splits;
+    a.split_len = sp.split_len;
+    a.split_out = rows * d;
+    a.split_lse = rows;
+    const bool out_bf16 = p->out_dtype == SAGE_BF16;
+    if (int r = hip_status(sage::launch_attn(a, dp_of(p->d), 0, out_bf16, st), "split-KV attention launch")) return r;
+    sage::MergeArgs m{};
+    m.parts = ws;
+    m.ps = rows * d;
+    m.pb = a.ob;
+    m.ph = a.oh;
+    m.pn = d;
+    m.lse_parts = a.lse;
+    m.out = p->out;
+    m.ob = p->o_stride_b;
+    m.oh = p->o_stride_h;
+    m.on = p->o_stride_n;
+    m.lse = p->lse;
+    m.S = sp.splits;
+    m.B = p->B;
+    m.H = p->Hq;
+    m.N = p->Nq;
+    m.d = p->d;
+    const bool vec = p->d % 8 == 0 && aligned(p->out, 16) && p->o_stride_b % 8 == 0 && p->o_stride_h % 8 == 0 &&
+                     p->o_stride_n % 8 == 0;
+    if (int r = hip_status(sage::launch_merge(m, out_bf16, vec, st), "split-KV merge launch")) return r;
+    return ok();
+}
+
 int sage_merge_states(const sage_merge_params* p, void* stream) {
     if (!p) return fail(SAGE_EINVAL, "params is NULL");
     if (p->struct_size < sizeof(sage_merge_params)) return fail(SAGE_EINVAL, "struct_size too small");

@@ -77,6 +77,12 @@ struct AttnArgs {
     int total_q;
     int n_qtiles;                // query tiles per (b, h)
     int num_wg;
+    // split-KV (FP8 V, dense, non-causal): workgroup split s of a query tile
+    // covers keys [s * split_len, min(Nk, (s + 1) * split_len)) and writes its
+    // output and LSE split_out / split_lse elements after split 0's
+    int n_splits;                // 1: no split
+    int split_len;               // multiple of 128
+    int64_t split_out, split_lse;
     // debug score dump (sage_debug_qk_scores)
     void* dbg;
     int dbg_mode;

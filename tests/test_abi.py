@@ -295,3 +295,36 @@ def test_merge_rejects(lib, case):
 
 def test_merge_null_params(lib):
     assert lib.sage_merge_states(None, None) == A.SAGE_EINVAL
+
+
+SPLIT_BREAKS = {
+    "n_splits 0": (lambda p: None, 0, 1 << 24, 0, A.SAGE_EINVAL),
+    "n_splits 65": (lambda p: None, 65, 1 << 24, 0, A.SAGE_EINVAL),
+    "causal": (lambda p: setattr(p, "is_causal", 1), 4, 1 << 24, 0, A.SAGE_EUNSUPPORTED),
+    "fp16 V": (lambda p: setattr(p, "v_dtype", A.SAGE_V_FP16), 4, 1 << 24, 0, A.SAGE_EUNSUPPORTED),
+    "workspace too small": (lambda p: None, 4, 4096, 0, A.SAGE_EINVAL),
+    "workspace misaligned": (lambda p: None, 4, 1 << 24, 128, A.SAGE_EINVAL),
+    "head_dim 129": (lambda p: setattr(p, "d", 129), 4, 1 << 24, 0, A.SAGE_EINVAL),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SPLIT_BREAKS))
+def test_splitkv_rejects(lib, case):
+    brk, ns, nbytes, off, code = SPLIT_BREAKS[case]
+    p = _attn_valid()
+    brk(p)
+    assert lib.sage_attn_fwd_splitkv(ctypes.byref(p), ns, FAKE + 0x4000000 + off, nbytes, None) == code
+    assert len(lib.sage_last_error()) > 0
+
+
+def test_splitkv_workspace_size(lib):
+    assert lib.sage_attn_splitkv_workspace_size(1, 8, 4, 4133, 128, 0) == 0
+    assert lib.sage_attn_splitkv_workspace_size(1, 8, 4, 4133, 129, 5) == 0
+    # 5 requested ranges of 4133 keys: ranges of 896 keys, 5 of them
+    rows = 5 * 1 * 8 * 4
+    want = -(-(rows * 128 * 2) // 256) * 256 + -(-(rows * 4) // 256) * 256
+    assert lib.sage_attn_splitkv_workspace_size(1, 8, 4, 4133, 128, 5) == want
+    # 7 requested ranges of 1000 keys: ranges of 256 keys, only 4 of them
+    rows = 4 * 2 * 3 * 10
+    want = -(-(rows * 64 * 2) // 256) * 256 + -(-(rows * 4) // 256) * 256
+    assert lib.sage_attn_splitkv_workspace_size(2, 3, 10, 1000, 64, 7) == want

@@ -89,6 +89,12 @@ WORKLOADS = {
                                         dtype="fp16", layout="HND", causal=False, gran="per_thread",
                                         v_dtype="fp8", pv_accum="fp32+fp32", smooth_k=True, smooth_v=False,
                                         return_lse=False, seed=6),
+    # few queries against a long context ([guide] sec. 4.1: q and k/v lengths may differ): 16 query rows per
+    # (batch, head) against 32 768 keys, grouped K/V heads, for the split-KV forward
+    "decode_gqa_b4_q16_k32768": Workload("decode_gqa_b4_q16_k32768", B=4, Hq=32, Hkv=8, Nq=16, Nk=32768, d=128,
+                                         dtype="bf16", layout="NHD", causal=False, gran="per_thread",
+                                         v_dtype="fp8", pv_accum="fp32+fp32", smooth_k=True, smooth_v=False,
+                                         return_lse=False, seed=7),
 }
 
 # the order in which the workloads are listed as configurations
