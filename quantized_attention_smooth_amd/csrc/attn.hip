@@ -1058,7 +1058,7 @@ __device__ __forceinline__ void pv8_all(const VA<DP, 0>& va, const PHalf<0>& P, 
 constexpr int kWaves8 = 8;
 constexpr int kThreads8 = 64 * kWaves8;
 
-template <int DP, bool OUT_BF16, bool KS16>
+template <int DP, bool OUT_BF16, bool KS16, bool PACK>
 __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     constexpr int PV = 0, NW = kWaves8;                 // every wavefront copies its share
     using C = AttnCfg<DP, PV, NW, NW>;
@@ -1080,7 +1080,13 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         wg /= a.n_splits;
     }
     int qt = wg % a.n_qtiles;
-    const int bh = wg / a.n_qtiles, h = bh % a.Hq, b = bh / a.Hq;
+    const int bh = wg / a.n_qtiles, grp = a.Hq / a.Hkv;
+    // packed GQA rows (non-causal, dense): the workgroup covers row r of the
+    // rows of all grp query heads of one K/V head, query head
+    // hk * grp + r / Nq, query r % Nq, so K and V stream once per group
+    constexpr bool pack = PACK;                         // a.pack_gqa != 0
+    const int b = pack ? bh / a.Hkv : bh / a.Hq;
+    const int h0 = pack ? (bh % a.Hkv) * grp : bh % a.Hq;
     if (a.causal) qt = a.n_qtiles - 1 - qt;
     int Lq = a.Nq, Lk = a.Nk, qoff = 0;
     if (a.cu_q) {
@@ -1090,18 +1096,31 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     }
     const int kb0 = split * a.split_len;                // first key of this workgroup's range
     if (a.n_splits > 1) Lk = min(Lk - kb0, a.split_len);
+    const int Lrows = pack ? grp * Lq : Lq;             // rows of the workgroup's row space
     const int q0 = qt * kBQ;
-    if (q0 >= Lq) return;
-    const int hk = h / (a.Hq / a.Hkv);
+    if (q0 >= Lrows) return;
+    const int hk = h0 / grp;
     const int kend = a.causal ? min(Lk, q0 + kBQ) : Lk;
     const int ntiles = (kend + kBK - 1) / kBK;
     const int n_main = (a.causal ? min(q0, Lk) : Lk) / kBK;
 
-    // ---- per-lane query state: row wq0 + n
+    // ---- per-lane query state: row wq0 + n of the row space
     const int wq0 = q0 + wave * 32;
-    const bool live = wq0 < Lq;
+    const bool live = wq0 < Lrows;
+    int h, qrow;
+    bool lane_ok;
+    if (pack) {
+        const int r = wq0 + n;
+        lane_ok = r < Lrows;
+        const int hi = lane_ok ? r / Lq : 0;
+        h = h0 + hi;
+        qrow = lane_ok ? r - hi * Lq : 0;
+    } else {
+        h = h0;
+        qrow = wq0 + n;
+        lane_ok = qrow < Lq;
+    }
     const int64_t qhead = (int64_t)b * a.Hq + h;
-    const int qrow = wq0 + n;
     v4i qf[NCB];
     float qscale = 0.f;
     if (live) {
@@ -1311,7 +1330,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const float* vmu = a.vmean ? a.vmean + khead * DP : nullptr;
     const float l_tot = ls[0];
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (qrow < Lq) {
+    if (lane_ok) {
         uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + split * a.split_out +
                          (a.cu_q ? (int64_t)(qoff + qrow) * a.on + (int64_t)h * a.oh
                                  : (int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)qrow * a.on);
@@ -1355,7 +1374,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
                 }
         }
         const float dot = swap_half_sum(part);
-        if (hh == 0 && qrow < Lq) {
+        if (hh == 0 && lane_ok) {
             const float corr = a.kmean ? a.sm_scale * qscale * dot : 0.f;
             const float lse = (m_ref + __log2f(l_tot) - p_log2_scale) * kLn2 + corr;
             const int64_t li = split * a.split_lse +
@@ -1443,12 +1462,20 @@ template <int DP, int PV>
 static void attn_dispatch_out(const AttnArgs& a, bool out_bf16, hipStream_t s) {
     if constexpr (PV == 0) {
         const bool ks16 = a.gk_shift == 4;              // per_thread K groups of 16 keys
-        if (out_bf16) {
-            if (ks16) attn8_fwd_kernel<DP, true, true><<<a.num_wg, kThreads8, 0, s>>>(a);
-            else attn8_fwd_kernel<DP, true, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+        if (a.pack_gqa) {
+            if (out_bf16) {
+                if (ks16) attn8_fwd_kernel<DP, true, true, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+                else attn8_fwd_kernel<DP, true, false, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+            } else {
+                if (ks16) attn8_fwd_kernel<DP, false, true, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+                else attn8_fwd_kernel<DP, false, false, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+            }
+        } else if (out_bf16) {
+            if (ks16) attn8_fwd_kernel<DP, true, true, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+            else attn8_fwd_kernel<DP, true, false, false><<<a.num_wg, kThreads8, 0, s>>>(a);
         } else {
-            if (ks16) attn8_fwd_kernel<DP, false, true><<<a.num_wg, kThreads8, 0, s>>>(a);
-            else attn8_fwd_kernel<DP, false, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+            if (ks16) attn8_fwd_kernel<DP, false, true, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+            else attn8_fwd_kernel<DP, false, false, false><<<a.num_wg, kThreads8, 0, s>>>(a);
         }
     } else {
         if (out_bf16) attn_fwd_kernel<DP, PV, true><<<a.num_wg, kThreads, 0, s>>>(a);
@@ -1458,9 +1485,10 @@ static void attn_dispatch_out(const AttnArgs& a, bool out_bf16, hipStream_t s) {
 
 hipError_t launch_attn(const AttnArgs& a_in, int dp, int pv, bool out_bf16, hipStream_t s) {
     AttnArgs a = a_in;
-    a.n_qtiles = (a.Nq + kBQ - 1) / kBQ;
+    const int grp = a.Hq / a.Hkv;
+    a.n_qtiles = ((a.pack_gqa ? grp : 1) * a.Nq + kBQ - 1) / kBQ;
     if (a.n_splits < 1) a.n_splits = 1;
-    a.num_wg = a.B * a.Hq * a.n_qtiles * a.n_splits;
+    a.num_wg = a.B * (a.pack_gqa ? a.Hkv : a.Hq) * a.n_qtiles * a.n_splits;
     if (dp == 128) {
         if (pv == 0) attn_dispatch_out<128, 0>(a, out_bf16, s);
         else if (pv == 1) attn_dispatch_out<128, 1>(a, out_bf16, s);

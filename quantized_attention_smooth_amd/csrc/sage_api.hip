@@ -305,6 +305,12 @@ static sage::AttnArgs attn_args(const sage_attn_params* p) {
     return a;
 }
 
+// Few queries per head with grouped K/V heads: one workgroup takes the rows
+// of every query head that shares a K/V head (FP8 V, non-causal, dense).
+static int pack_gqa(const sage_attn_params* p) {
+    return p->v_dtype == SAGE_V_FP8 && !p->is_causal && p->Hq > p->Hkv && p->Nq <= sage::kPackMaxNq;
+}
+
 static int pv_kind(const sage_attn_params* p) {
     return p->v_dtype == SAGE_V_FP8 ? 0 : (p->in_dtype == SAGE_BF16 ? 2 : 1);
 }
@@ -314,6 +320,7 @@ int sage_attn_fwd(const sage_attn_params* p, void* stream) {
     if (p->struct_size < sizeof(sage_attn_params)) return fail(SAGE_EINVAL, "struct_size too small");
     if (int r = check_attn(p, false)) return r;
     sage::AttnArgs a = attn_args(p);
+    a.pack_gqa = pack_gqa(p);
     if (int r = hip_status(sage::launch_attn(a, dp_of(p->d), pv_kind(p), p->out_dtype == SAGE_BF16,
                                              reinterpret_cast<hipStream_t>(stream)),
                            "attention launch"))
@@ -410,6 +417,7 @@ int sage_attn_fwd_splitkv(const sage_attn_params* p, int n_splits, void* workspa
     a.split_len = sp.split_len;
     a.split_out = rows * d;
     a.split_lse = rows;
+    a.pack_gqa = pack_gqa(p);
     const bool out_bf16 = p->out_dtype == SAGE_BF16;
     if (int r = hip_status(sage::launch_attn(a, dp_of(p->d), 0, out_bf16, st), "split-KV attention launch")) return r;
     sage::MergeArgs m{};

@@ -80,6 +80,7 @@ struct AttnArgs {
     // split-KV (FP8 V, dense, non-causal): workgroup split s of a query tile
     // covers keys [s * split_len, min(Nk, (s + 1) * split_len)) and writes its
     // output and LSE split_out / split_lse elements after split 0's
+    int pack_gqa;                // FP8 V, non-causal, dense only: rows of all query heads of a K/V head together
     int n_splits;                // 1: no split
     int split_len;               // multiple of 128
     int64_t split_out, split_lse;
@@ -123,6 +124,9 @@ hipError_t launch_merge(const MergeArgs& a, bool bf16, bool vec, hipStream_t s);
 // that a (b, h) has at most kMaxChunks partials (every tile workgroup of the
 // quantize pass reduces all partials of its (b, h)).
 constexpr int kStatsChunk = 128;
+// Query heads sharing a K/V head are packed into one workgroup's rows when
+// each has at most this many queries.
+constexpr int kPackMaxNq = 128;
 constexpr int kMaxChunks = 32;
 
 }  // namespace sage

@@ -89,3 +89,26 @@ def test_decode_shape_close_to_exact_attention():
     got = out.float().cpu().numpy()[0].transpose(1, 0, 2)
     assert cosine(got, ex["out"][0]) >= COS_EXACT
     assert np.abs(lse.cpu().numpy()[0] - ex["lse"][0]).max() < 0.05
+
+
+@pytest.mark.parametrize("nq", [1, 16, 100])
+def test_packed_gqa_rows_equal_repeated_kv(nq):
+    """Few queries with grouped K/V heads run with the rows of a group packed
+    into one workgroup; every row's arithmetic is unchanged, so the result is
+    bit-identical to the same heads with K/V repeated per query head (which is
+    not packed)."""
+    print(f"[gpu-case] packed GQA rows: B2 Hq8 Hkv2 Nq{nq} Nk1000 d128 fp16 per_thread seed 2", flush=True)
+    w = workloads.WORKLOADS["b2h8n4096d128"]
+    inp = workloads.make_inputs(w, {"B": 2, "Hq": 8, "Hkv": 2, "Nq": nq, "Nk": 1000})
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    kr, vr = (t.repeat_interleave(4, dim=1).contiguous() for t in (k, v))
+    outs = []
+    for kk, vv in ((k, v), (kr, vr)):
+        qk, qv = _quantize(q, kk, vv, "HND", "per_thread", False)
+        outs.append(sage.sage_attn_fwd(qk, qv, return_lse=True))
+        outs.append(sage.sage_attn_fwd_splitkv(qk, qv, n_splits=3, return_lse=True))
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        assert torch.equal(outs[i][0].view(torch.int16), outs[i + 2][0].view(torch.int16))
+        assert torch.equal(outs[i][1], outs[i + 2][1])
