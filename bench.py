@@ -187,7 +187,7 @@ def time_splitkv(w, iters: int = 20) -> dict:
     q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
     qk, qv = sage.sage_quant_qkv(q, k, v, tensor_layout=w.layout, qk_quant_gran=w.gran, smooth_k=w.smooth_k,
                                  v_dtype=w.v_dtype, smooth_v=w.smooth_v)
-    ns = sage.splitkv_plan(w.B, w.Hq, w.Nq, w.Nk)
+    ns = sage.splitkv_plan(w.B, w.Hq, w.Nq, w.Nk, Hkv=w.Hkv)
     ws = torch.empty(int(sage.load_library().sage_attn_splitkv_workspace_size(w.B, w.Hq, w.Nq, w.Nk, w.d, ns)),
                      dtype=torch.uint8, device=dev)
     out = torch.empty_like(q)

@@ -246,12 +246,21 @@ def sage_attn_fwd(qk: QuantQK, qv: QuantV, *, tensor_layout: str = "HND", is_cau
     return (out, lse) if return_lse else out
 
 
-def splitkv_plan(B: int, Hq: int, Nq: int, Nk: int, n_splits: Optional[int] = None) -> int:
+PACK_MAX_NQ = 128       # the library packs the query heads of a K/V head together up to this many queries
+
+
+def splitkv_plan(B: int, Hq: int, Nq: int, Nk: int, n_splits: Optional[int] = None, Hkv: Optional[int] = None) -> int:
     """Number of key ranges to ask for: enough workgroups to fill the GPU
-    (about 512, two per compute unit) with ranges of at least 256 keys."""
+    (about 512, two per compute unit) with ranges of at least 256 keys.  With
+    grouped K/V heads and few queries, the library runs the rows of all query
+    heads of a K/V head in one workgroup, so there are fewer row tiles."""
     if n_splits is not None:
         return int(n_splits)
-    tiles = B * Hq * ((Nq + 255) // 256)
+    Hkv = Hq if Hkv is None else Hkv
+    if Hq > Hkv and Nq <= PACK_MAX_NQ:
+        tiles = B * Hkv * ((Hq // Hkv * Nq + 255) // 256)
+    else:
+        tiles = B * Hq * ((Nq + 255) // 256)
     return max(1, min(64, -(-512 // tiles), Nk // 256))
 
 
@@ -268,7 +277,7 @@ def sage_attn_fwd_splitkv(qk: QuantQK, qv: QuantV, *, n_splits: Optional[int] = 
         out = torch.empty(shape, dtype=qk.dtype, device=dev)
     g = _geometry(out, tensor_layout, None, None)
     lse = torch.empty((qk.B, qk.Hq, qk.Nq), dtype=torch.float32, device=dev) if return_lse else None
-    ns = splitkv_plan(qk.B, qk.Hq, qk.Nq, qk.Nk, n_splits)
+    ns = splitkv_plan(qk.B, qk.Hq, qk.Nq, qk.Nk, n_splits, qk.Hkv)
     need = int(L.sage_attn_splitkv_workspace_size(qk.B, qk.Hq, qk.Nq, qk.Nk, qk.d, ns))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
