@@ -373,19 +373,28 @@ def sage_merge_states(out_parts: torch.Tensor, lse_parts: torch.Tensor, *, tenso
 def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND",
              is_causal: bool = False, sm_scale: Optional[float] = None, return_lse: bool = False, *,
              qk_quant_gran: str = "per_thread", pv_accum_dtype: str = "fp32+fp32", smooth_k: bool = True,
-             smooth_v: bool = False, v_dtype: str = "fp8"):
+             smooth_v: bool = False, v_dtype: str = "fp8", kv_splits=None):
     """Quantized attention forward: out = softmax(q k^T * sm_scale) v.
 
     q, k, v: fp16/bf16 CUDA tensors, (B, H, N, D) for HND or (B, N, H, D) for
     NHD, same dtype; Hq must be a multiple of Hkv; D <= 128.
+    kv_splits: None runs one pass over the keys; "auto" or an int runs the
+    split-KV forward (key ranges in parallel, merged by log-sum-exp) for few
+    queries against many keys -- non-causal, FP8 V only.
     Returns out (same dtype and layout as q) and, with return_lse, the fp32
     log-sum-exp [B, Hq, Nq]."""
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must have the same dtype (deployment guide sec. 4.1)")
     if not (q.device == k.device == v.device) or q.device.type != "cuda":
         raise ValueError("q, k, v must be on the same GPU")
+    if kv_splits is not None and (is_causal or v_dtype != "fp8"):
+        raise NotImplementedError("kv_splits needs a non-causal call with FP8 V")
     qk, qv = sage_quant_qkv(q, k, v, tensor_layout=tensor_layout, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k,
                             v_dtype=v_dtype, smooth_v=smooth_v)
+    if kv_splits is not None:
+        return sage_attn_fwd_splitkv(qk, qv, n_splits=None if kv_splits == "auto" else int(kv_splits),
+                                     tensor_layout=tensor_layout, sm_scale=sm_scale, return_lse=return_lse,
+                                     pv_accum_dtype=pv_accum_dtype)
     return sage_attn_fwd(qk, qv, tensor_layout=tensor_layout, is_causal=is_causal, sm_scale=sm_scale,
                          return_lse=return_lse, pv_accum_dtype=pv_accum_dtype)
 

@@ -112,3 +112,26 @@ def test_packed_gqa_rows_equal_repeated_kv(nq):
     for i in (0, 1):
         assert torch.equal(outs[i][0].view(torch.int16), outs[i + 2][0].view(torch.int16))
         assert torch.equal(outs[i][1], outs[i + 2][1])
+
+
+def test_sageattn_kv_splits_matches_oracle():
+    """sageattn(..., kv_splits="auto") on a decode shape equals the oracle's
+    split emulation with the number of ranges the plan picks."""
+    print("[gpu-case] sageattn kv_splits=auto: B2 Hq8 Hkv8 Nq8 Nk5000 d64 fp16 HND seed 2", flush=True)
+    w = workloads.WORKLOADS["b2h8n4096d128"]
+    inp = workloads.make_inputs(w, {"B": 2, "Hq": 8, "Hkv": 8, "Nq": 8, "Nk": 5000, "d": 64})
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    out = sage.sageattn(q, k, v, kv_splits="auto")
+    torch.cuda.synchronize()
+    ns = sage.splitkv_plan(2, 8, 8, 5000, Hkv=8)
+    assert ns > 1
+    ref = oracle.reference_forward_splitkv(*(inp[x].float().numpy() for x in ("q", "k", "v")), dtype="fp16",
+                                           n_splits=ns)
+    got = out.float().cpu().numpy()
+    for b in range(2):
+        r = ref["out"][b]
+        tol = 2e-3 + 2 * out_ulp(r, "fp16") + ref["allow"][b] + 1e-4 * ref["parts_scale"][b][..., None]
+        assert (np.abs(got[b] - r) <= tol).all()
+    with pytest.raises(NotImplementedError):
+        sage.sageattn(q, k, v, is_causal=True, kv_splits=2)
