@@ -60,8 +60,14 @@ struct WsLayout {
 WsLayout ws_layout(int B, int H, int N, int d) {
     WsLayout w{};
     const int dp = dp_of(d);
-    // kStatsChunk tokens per chunk, longer (a multiple of it) beyond kMaxChunks chunks
-    const int64_t per = (N + sage::kMaxChunks - 1) / sage::kMaxChunks;
+    // kStatsChunk tokens per chunk, longer (a multiple of it) beyond the target
+    // number of chunks per (sequence, head): about 256 statistics workgroups in
+    // all, 8 to kMaxChunks per head.  Fewer chunks mean fewer partials for
+    // every tile workgroup of the second pass to reduce; enough of them keep
+    // the statistics pass spread over the GPU.
+    const int64_t heads = (int64_t)B * H;
+    const int64_t target = std::min<int64_t>(sage::kMaxChunks, std::max<int64_t>(8, (256 + heads - 1) / heads));
+    const int64_t per = (N + target - 1) / target;
     w.chunk_len = (int)std::max<int64_t>(sage::kStatsChunk, round_up(per, sage::kStatsChunk));
     w.chunks = (int)((N + w.chunk_len - 1) / w.chunk_len);
     const size_t cells = (size_t)B * H * w.chunks * dp;

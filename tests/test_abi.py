@@ -213,10 +213,13 @@ def test_debug_scores_rejects(lib):
 def test_workspace_size(lib):
     assert lib.sage_quant_workspace_size(0, 1, 1, 64) == 0
     assert lib.sage_quant_workspace_size(1, 1, 1, 129) == 0
-    # chunks of 128 tokens, 8-byte sums + fp32 min/max per (b, h, chunk, channel)
+    # 8-byte sums + fp32 min/max per (b, h, chunk, channel); about 256 chunks over all heads, 8 to 32 per head,
+    # each a multiple of 128 tokens
     n = lib.sage_quant_workspace_size(2, 8, 4096, 128)
-    cells = 2 * 8 * 32 * 128
+    cells = 2 * 8 * 16 * 128
     assert n >= cells * 16
+    assert lib.sage_quant_workspace_size(1, 8, 8192, 128) >= 8 * 32 * 128 * 16
+    assert lib.sage_quant_workspace_size(1, 48, 17550, 64) >= 48 * 8 * 64 * 16
     assert lib.sage_quant_workspace_size(1, 1, 257, 64) > lib.sage_quant_workspace_size(1, 1, 256, 64)
 
 
