@@ -53,6 +53,16 @@ __device__ __forceinline__ void load8(const uint16_t* row, int c0, int d, float 
     }
 }
 
+// Workgroup id -> (unit, head, sequence), the head varying fastest: with
+// token-major layouts (NHD, packed varlen) the rows of all heads of a token
+// are adjacent, so workgroups that run together read adjacent memory.
+struct UnitHeadB {
+    int unit, h, b;
+};
+__device__ __forceinline__ UnitHeadB unit_head_b(int bid, int units, int H) {
+    return UnitHeadB{(bid / H) % units, bid % H, bid / H / units};
+}
+
 __device__ __forceinline__ void seq_range(const int32_t* cu, int b, int Ndense, int& n0, int& N) {
     if (cu) {
         n0 = cu[b];
@@ -297,15 +307,18 @@ __global__ __launch_bounds__(kThreads) void qk_pass1_kernel(QuantRowsArgs q, Qua
     int bid = blockIdx.x;
     if (bid < nq_blocks) {
         const int tiles = q.npad / kPad;
-        quant_rows_body<BF16, DP, VEC>(q, bid % tiles, (bid / tiles) % q.H, bid / tiles / q.H, nullptr);
+        const UnitHeadB u = unit_head_b(bid, tiles, q.H);
+        quant_rows_body<BF16, DP, VEC>(q, u.unit, u.h, u.b, nullptr);
         return;
     }
     bid -= nq_blocks;
     if (smooth) {
-        stats_body<BF16, DP, VEC>(ks, bid % ks.chunks, (bid / ks.chunks) % ks.H, bid / ks.chunks / ks.H);
+        const UnitHeadB u = unit_head_b(bid, ks.chunks, ks.H);
+        stats_body<BF16, DP, VEC>(ks, u.unit, u.h, u.b);
     } else {
         const int tiles = k.npad / kPad;
-        quant_rows_body<BF16, DP, VEC>(k, bid % tiles, (bid / tiles) % k.H, bid / tiles / k.H, nullptr);
+        const UnitHeadB u = unit_head_b(bid, tiles, k.H);
+        quant_rows_body<BF16, DP, VEC>(k, u.unit, u.h, u.b, nullptr);
     }
 }
 
@@ -314,15 +327,16 @@ __global__ __launch_bounds__(kThreads) void qk_pass1_kernel(QuantRowsArgs q, Qua
 template <bool BF16, int DP, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_pass2_kernel(QuantRowsArgs k, StatsArgs ks) {
     const int tiles = k.npad / kPad;
-    const int tile = blockIdx.x % tiles, h = (blockIdx.x / tiles) % k.H, b = blockIdx.x / tiles / k.H;
-    quant_rows_body<BF16, DP, VEC>(k, tile, h, b, &ks);
+    const UnitHeadB u = unit_head_b(blockIdx.x, tiles, k.H);
+    quant_rows_body<BF16, DP, VEC>(k, u.unit, u.h, u.b, &ks);
 }
 
 // ---------------------------------------------------------------------------
 template <bool BF16, int DP, bool VEC>
 __global__ __launch_bounds__(kThreads) void v_stats_kernel(StatsArgs vs) {
     const int bid = blockIdx.x;
-    stats_body<BF16, DP, VEC>(vs, bid % vs.chunks, (bid / vs.chunks) % vs.H, bid / vs.chunks / vs.H);
+    const UnitHeadB u = unit_head_b(bid, vs.chunks, vs.H);
+    stats_body<BF16, DP, VEC>(vs, u.unit, u.h, u.b);
 }
 
 // V -> V^T codes for one 128-key tile.  With statistics, the workgroup
@@ -419,8 +433,8 @@ __device__ __forceinline__ void quant_v_body(const QuantVArgs& a, const StatsArg
 template <bool BF16, int DP, bool FP8, bool VEC>
 __global__ __launch_bounds__(kThreads) void quant_v_kernel(QuantVArgs a, StatsArgs vs, int have_stats) {
     const int tiles = a.npad / kPad;
-    quant_v_body<BF16, DP, FP8, VEC>(a, vs, have_stats, blockIdx.x % tiles, (blockIdx.x / tiles) % a.H,
-                                     blockIdx.x / tiles / a.H);
+    const UnitHeadB u = unit_head_b(blockIdx.x, tiles, a.H);
+    quant_v_body<BF16, DP, FP8, VEC>(a, vs, have_stats, u.unit, u.h, u.b);
 }
 
 // ---------------------------------------------------------------------------
@@ -435,21 +449,25 @@ __global__ __launch_bounds__(kThreads) void qkv_pass1_kernel(QuantRowsArgs q, Qu
     int bid = blockIdx.x;
     if (bid < nq_blocks) {
         const int tiles = q.npad / kPad;
-        quant_rows_body<BF16, DP, VEC>(q, bid % tiles, (bid / tiles) % q.H, bid / tiles / q.H, nullptr);
+        const UnitHeadB u = unit_head_b(bid, tiles, q.H);
+        quant_rows_body<BF16, DP, VEC>(q, u.unit, u.h, u.b, nullptr);
         return;
     }
     bid -= nq_blocks;
     if (bid < nk_blocks) {
         if (smooth_k) {
-            stats_body<BF16, DP, VEC>(ks, bid % ks.chunks, (bid / ks.chunks) % ks.H, bid / ks.chunks / ks.H);
+            const UnitHeadB u = unit_head_b(bid, ks.chunks, ks.H);
+            stats_body<BF16, DP, VEC>(ks, u.unit, u.h, u.b);
         } else {
             const int tiles = k.npad / kPad;
-            quant_rows_body<BF16, DP, VEC>(k, bid % tiles, (bid / tiles) % k.H, bid / tiles / k.H, nullptr);
+            const UnitHeadB u = unit_head_b(bid, tiles, k.H);
+            quant_rows_body<BF16, DP, VEC>(k, u.unit, u.h, u.b, nullptr);
         }
         return;
     }
     bid -= nk_blocks;
-    stats_body<BF16, DP, VEC>(vs, bid % vs.chunks, (bid / vs.chunks) % vs.H, bid / vs.chunks / vs.H);
+    const UnitHeadB u = unit_head_b(bid, vs.chunks, vs.H);
+    stats_body<BF16, DP, VEC>(vs, u.unit, u.h, u.b);
 }
 
 template <bool BF16, int DP, bool FP8, bool VEC>
@@ -458,12 +476,14 @@ __global__ __launch_bounds__(kThreads) void qkv_pass2_kernel(QuantRowsArgs k, St
     int bid = blockIdx.x;
     if (bid < nk_blocks) {
         const int tiles = k.npad / kPad;
-        quant_rows_body<BF16, DP, VEC>(k, bid % tiles, (bid / tiles) % k.H, bid / tiles / k.H, &ks);
+        const UnitHeadB u = unit_head_b(bid, tiles, k.H);
+        quant_rows_body<BF16, DP, VEC>(k, u.unit, u.h, u.b, &ks);
         return;
     }
     bid -= nk_blocks;
     const int tiles = v.npad / kPad;
-    quant_v_body<BF16, DP, FP8, VEC>(v, vs, v_stats, bid % tiles, (bid / tiles) % v.H, bid / tiles / v.H);
+    const UnitHeadB u = unit_head_b(bid, tiles, v.H);
+    quant_v_body<BF16, DP, FP8, VEC>(v, vs, v_stats, u.unit, u.h, u.b);
 }
 
 template <bool BF16, int DP, bool FP8, bool VEC>
