@@ -32,6 +32,7 @@ CASES = [
     (4, 1, 2, 65, 8, "bf16", "HND"),
     (2, 1, 1, 1, 1, "fp16", "NHD"),
     (16, 1, 2, 300, 64, "bf16", "NHD"),
+    (64, 1, 1, 40, 128, "fp16", "HND"),      # the largest number of parts the call accepts
 ]
 
 
