@@ -143,7 +143,7 @@ def time_workload(w, steps: int, warmup: int, calibrate: bool = False):
     return inp, ms_per_step, quant_ms, attn_ms
 
 
-def time_merge(w, parts: int = 2, iters: int = 20) -> dict:
+def time_merge(w, parts: int = 2, iters: int = 50) -> dict:
     """HBM throughput of sage_merge_states combining `parts` partial results
     of the workload's output shape (what a split of its keys into `parts`
     sets, each run with return_lse, hands to the merge)."""
@@ -155,7 +155,7 @@ def time_merge(w, parts: int = 2, iters: int = 20) -> dict:
     dev = torch.device("cuda:0")
     o, l = inp["out_parts"].to(dev), inp["lse_parts"].to(dev)
     out = torch.empty(o.shape[1:], dtype=o.dtype, device=dev)
-    for _ in range(3):
+    for _ in range(100):
         sage.sage_merge_states(o, l, tensor_layout=w.layout, out=out)
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -194,7 +194,7 @@ def time_splitkv(w, iters: int = 20) -> dict:
     stream = torch.cuda.current_stream()
 
     def timed(fn):
-        for _ in range(3):
+        for _ in range(20):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -269,7 +269,9 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU's clock rises over the first tens of milliseconds of work: 300 untimed steps (~40 ms on the default
+    # workload) let the timed steps run at the steady clock
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="b2h8n4096d128")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -329,12 +331,12 @@ def main() -> int:
     }
     if args.secondary != "none" and args.secondary != w.name:
         w2 = workloads.WORKLOADS[args.secondary]
-        _, ms2, qms2, ams2 = time_workload(w2, 10, 3)
+        _, ms2, qms2, ams2 = time_workload(w2, 10, 20)
         ops2 = workloads.attention_ops(w2)
         at2 = ops2 / (ams2 * 1e-3) / 1e12
         rec["secondary"] = {"workload": w2.name, "seq_len": w2.Nq, "head_dim": w2.d, "B": w2.B, "Hq": w2.Hq,
                             "qk_quant_gran": w2.gran, "v_dtype": w2.v_dtype, "smooth_v": w2.smooth_v,
-                            "steps": 10, "warmup": 3, "ms_per_step": round(ms2, 4),
+                            "steps": 10, "warmup": 20, "ms_per_step": round(ms2, 4),
                             "step_tops": round(ops2 / (ms2 * 1e-3) / 1e12, 2), "quant_ms": round(qms2, 4),
                             "attn_kernel_ms": round(ams2, 4), "attn_kernel_tops": round(at2, 2),
                             "attn_pct_of_peak": round(100.0 * at2 / PEAK_TOPS[w2.v_dtype], 2)}
