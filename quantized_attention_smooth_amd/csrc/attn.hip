@@ -727,10 +727,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
     const int n = lane & 31, hh = lane >> 5;
 
-    // ---- work item
-    const int wg = xcd_remap(blockIdx.x, a.num_wg);
-    int qt = wg % a.n_qtiles;
-    const int bh = wg / a.n_qtiles, h = bh % a.Hq, b = bh / a.Hq;
+    // ---- work item (the same order as the FP8 kernel: varlen batches
+    // round-robin over the XCDs, causal varlen longest tiles first)
+    const bool lpt = a.cu_q && a.causal;
+    const int wg = a.cu_q ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.num_wg);
+    const int nbh = a.num_wg / a.n_qtiles;
+    int qt = lpt ? wg / nbh : wg % a.n_qtiles;
+    const int bh = lpt ? wg % nbh : wg / a.n_qtiles, h = bh % a.Hq, b = bh / a.Hq;
     if (a.causal) qt = a.n_qtiles - 1 - qt;             // longest rows first
     int Lq = a.Nq, Lk = a.Nk, qoff = 0;
     if (a.cu_q) {
@@ -1073,14 +1076,19 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const int n = lane & 31, hh = lane >> 5;
     const bool lead_wave = wave < kWaves8 / 2;          // wave-uniform: wavefronts 0-3 lead by half a step
 
-    int wg = xcd_remap(blockIdx.x, a.num_wg);
+    // Varlen batches: sequences differ in length, so workgroups go round-robin
+    // over the XCDs (no remap) and, when causal, longest query tiles first
+    // over the whole grid; dense calls keep the tiles of a head on one XCD.
+    const bool lpt = a.cu_q && a.causal;
+    int wg = a.cu_q ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.num_wg);
     int split = 0;
     if (a.n_splits > 1) {                               // split-KV: consecutive workgroups, consecutive key ranges
         split = wg % a.n_splits;
         wg /= a.n_splits;
     }
-    int qt = wg % a.n_qtiles;
-    const int bh = wg / a.n_qtiles, grp = a.Hq / a.Hkv;
+    const int nbh = a.num_wg / (a.n_qtiles * a.n_splits);
+    int qt = lpt ? wg / nbh : wg % a.n_qtiles;
+    const int bh = lpt ? wg % nbh : wg / a.n_qtiles, grp = a.Hq / a.Hkv;
     // packed GQA rows (non-causal, dense): the workgroup covers row r of the
     // rows of all grp query heads of one K/V head, query head
     // hk * grp + r / Nq, query r % Nq, so K and V stream once per group
