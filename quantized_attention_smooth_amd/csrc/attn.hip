@@ -727,10 +727,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, kept in an SGPR
     const int n = lane & 31, hh = lane >> 5;
 
-    // ---- work item (the same order as the FP8 kernel: varlen batches
-    // round-robin over the XCDs, causal varlen longest tiles first)
-    const bool lpt = a.cu_q && a.causal;
-    const int wg = a.cu_q ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.num_wg);
+    // ---- work item (the same order as the FP8 kernel: causal calls and
+    // varlen batches round-robin over the XCDs, causal longest tiles first)
+    const bool lpt = a.causal;
+    const int wg = (a.cu_q || a.causal) ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.num_wg);
     const int nbh = a.num_wg / a.n_qtiles;
     int qt = lpt ? wg / nbh : wg % a.n_qtiles;
     const int bh = lpt ? wg % nbh : wg / a.n_qtiles, h = bh % a.Hq, b = bh / a.Hq;
@@ -1076,11 +1076,12 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const int n = lane & 31, hh = lane >> 5;
     const bool lead_wave = wave < kWaves8 / 2;          // wave-uniform: wavefronts 0-3 lead by half a step
 
-    // Varlen batches: sequences differ in length, so workgroups go round-robin
-    // over the XCDs (no remap) and, when causal, longest query tiles first
-    // over the whole grid; dense calls keep the tiles of a head on one XCD.
-    const bool lpt = a.cu_q && a.causal;
-    int wg = a.cu_q ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.num_wg);
+    // Causal calls and varlen batches have workgroups of very different
+    // lengths: those go round-robin over the XCDs (no remap) and, when causal,
+    // the longest query tiles start first over the whole grid.  Other calls
+    // keep the tiles of a head on one XCD, where they share its L2.
+    const bool lpt = a.causal;
+    int wg = (a.cu_q || a.causal) ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.num_wg);
     int split = 0;
     if (a.n_splits > 1) {                               // split-KV: consecutive workgroups, consecutive key ranges
         split = wg % a.n_splits;
