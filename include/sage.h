@@ -257,14 +257,14 @@ int sage_debug_qk_scores(const sage_attn_params* p, int mode, void* scores, void
  * rounded to out_dtype and stored with its log-sum-exp in the workspace, and
  * the S partial results are then combined as sage_merge_states does.  With
  * S = 1 the result is bit-identical to sage_attn_fwd.
- * Same parameters and layouts as sage_attn_fwd; FP8 V and non-causal only.
+ * Same parameters and layouts as sage_attn_fwd; non-causal only.
  * workspace: device memory, 256-byte aligned, of at least
  * sage_attn_splitkv_workspace_size(B, Hq, Nq, Nk, d, n_splits) bytes (0 for
  * invalid sizes); it holds S x [B][Hq][Nq][d] outputs and S x [B][Hq][Nq]
  * fp32 LSEs and need not be initialised.
  * Errors: as sage_attn_fwd; SAGE_EINVAL for n_splits outside 1..64 or a
- * missing, misaligned or too small workspace; SAGE_EUNSUPPORTED for fp16/bf16
- * V or is_causal.
+ * missing, misaligned or too small workspace; SAGE_EUNSUPPORTED for
+ * is_causal.
  * ------------------------------------------------------------------------- */
 size_t sage_attn_splitkv_workspace_size(int B, int Hq, int Nq, int Nk, int d, int n_splits);
 int sage_attn_fwd_splitkv(const sage_attn_params* p, int n_splits, void* workspace, size_t workspace_bytes,

@@ -368,9 +368,9 @@ def splitkv_ranges(nk: int, n_splits: int):
 
 def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str, n_splits: int,
                               layout: str = "HND", sm_scale: Optional[float] = None, gran: str = "per_thread",
-                              smooth_k: bool = True, smooth_v: bool = False,
+                              smooth_k: bool = True, smooth_v: bool = False, v_dtype: str = "fp8",
                               rows: Optional[Callable[[int, int], np.ndarray]] = None) -> dict:
-    """The split-KV forward (few queries against many keys; FP8 V, non-causal)
+    """The split-KV forward (few queries against many keys; non-causal)
     step by step: quantize Q, K, V over the whole sequence as
     reference_forward does; for each key range (splitkv_ranges) run the
     online-softmax attention of that range alone, starting afresh at its first
@@ -389,15 +389,18 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
         sm_scale = 1.0 / math.sqrt(d)
     sm32 = float(np.float32(sm_scale))
     gq, gk = Q_GROUP[gran], K_GROUP[gran]
-    qz = reference_forward(q, k, v, dtype=dtype, layout=layout, gran=gran, v_dtype="fp8", smooth_k=smooth_k,
+    qz = reference_forward(q, k, v, dtype=dtype, layout=layout, gran=gran, v_dtype=v_dtype, smooth_k=smooth_k,
                            smooth_v=smooth_v, attention=False)
+    p_mode = 0 if v_dtype == "fp8" else (2 if dtype == "bf16" else 1)
     mbits, emin = (7, -126) if dtype == "bf16" else (10, -14)
     L = lib()
     res = {"out": [], "lse": [], "allow": [], "parts_scale": [], "rows": []}
     for b in range(len(qz["q8"])):
         q8, qs = qz["q8"][b], qz["q_scale"][b]
         k8, ks, km = qz["k8"][b], qz["k_scale"][b], qz["k_mean"][b]
-        v8, vs, vm = qz["v8"][b], qz["v_scale"][b], qz["v_mean"][b]
+        vm = qz["v_mean"][b]
+        if v_dtype == "fp8":
+            v8, vs = qz["v8"][b], qz["v_scale"][b]
         hq, nq = q8.shape[0], q8.shape[1]
         hkv, nk = k8.shape[0], k8.shape[1]
         grp = hq // hkv
@@ -408,7 +411,7 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
             hk = h // grp
             qs_row = np.ascontiguousarray(np.repeat(qs[h], gq)[:nq], dtype=np.float32)
             ks_key = np.repeat(ks[hk], gk)[:nk]
-            vval = e4m3_decode(v8[hk])
+            vval = e4m3_decode(v8[hk]) if v_dtype == "fp8" else qz["v16"][b][hk]
             po, pl, pa = [], [], []
             for a0, a1 in splitkv_ranges(nk, n_splits):
                 o = np.zeros((len(r), dp), dtype=np.float64)
@@ -417,9 +420,10 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
                 rc = L.oracle_attn_rows(nq, a1 - a0, dp, _p(q8[h]), _p(qs_row),
                                         _p(np.ascontiguousarray(k8[hk][a0:a1])),
                                         _p(np.ascontiguousarray(ks_key[a0:a1], dtype=np.float32)),
-                                        _p(np.ascontiguousarray(vval[a0:a1], dtype=np.float32)), _p(vs[hk]),
+                                        _p(np.ascontiguousarray(vval[a0:a1], dtype=np.float32)),
+                                        _p(vs[hk] if v_dtype == "fp8" else None),
                                         _p(vm[hk] if smooth_v else None), _p(km[hk] if smooth_k else None),
-                                        sm32, 0, 0, DEFAULT_BK, DEFAULT_TAU, 0, len(r), _p(r), _p(o), _p(ls),
+                                        sm32, 0, 0, DEFAULT_BK, DEFAULT_TAU, p_mode, len(r), _p(r), _p(o), _p(ls),
                                         None, _p(al), None)
                 if rc != 0:
                     raise RuntimeError(f"oracle_attn_rows failed ({rc})")

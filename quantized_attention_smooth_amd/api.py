@@ -269,7 +269,7 @@ def sage_attn_fwd_splitkv(qk: QuantQK, qv: QuantV, *, n_splits: Optional[int] = 
                           pv_accum_dtype: str = "fp32+fp32", out: Optional[torch.Tensor] = None,
                           workspace: Optional[torch.Tensor] = None):
     """sage_attn_fwd with the keys cut into ranges that run in parallel and are
-    merged by their log-sum-exp (few queries, many keys; FP8 V, non-causal)."""
+    merged by their log-sum-exp (few queries, many keys; non-causal)."""
     L = A.load()
     dev = qk.q8.device
     if out is None:
@@ -380,15 +380,15 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
     NHD, same dtype; Hq must be a multiple of Hkv; D <= 128.
     kv_splits: None runs one pass over the keys; "auto" or an int runs the
     split-KV forward (key ranges in parallel, merged by log-sum-exp) for few
-    queries against many keys -- non-causal, FP8 V only.
+    queries against many keys -- non-causal only.
     Returns out (same dtype and layout as q) and, with return_lse, the fp32
     log-sum-exp [B, Hq, Nq]."""
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must have the same dtype (deployment guide sec. 4.1)")
     if not (q.device == k.device == v.device) or q.device.type != "cuda":
         raise ValueError("q, k, v must be on the same GPU")
-    if kv_splits is not None and (is_causal or v_dtype != "fp8"):
-        raise NotImplementedError("kv_splits needs a non-causal call with FP8 V")
+    if kv_splits is not None and is_causal:
+        raise NotImplementedError("kv_splits needs a non-causal call")
     qk, qv = sage_quant_qkv(q, k, v, tensor_layout=tensor_layout, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k,
                             v_dtype=v_dtype, smooth_v=smooth_v)
     if kv_splits is not None:

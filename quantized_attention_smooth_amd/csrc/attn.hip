@@ -730,8 +730,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     // ---- work item (the same order as the FP8 kernel: causal calls and
     // varlen batches round-robin over the XCDs, causal longest tiles first)
     const bool lpt = a.causal;
-    const int wg = (a.cu_q || a.causal) ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.num_wg);
-    const int nbh = a.num_wg / a.n_qtiles;
+    int wg = (a.cu_q || a.causal) ? (int)blockIdx.x : xcd_remap(blockIdx.x, a.num_wg);
+    int split = 0;
+    if (a.n_splits > 1) {                               // split-KV: consecutive workgroups, consecutive key ranges
+        split = wg % a.n_splits;
+        wg /= a.n_splits;
+    }
+    const int nbh = a.num_wg / (a.n_qtiles * a.n_splits);
     int qt = lpt ? wg / nbh : wg % a.n_qtiles;
     const int bh = lpt ? wg % nbh : wg / a.n_qtiles, h = bh % a.Hq, b = bh / a.Hq;
     if (a.causal) qt = a.n_qtiles - 1 - qt;             // longest rows first
@@ -741,6 +746,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         Lq = a.cu_q[b + 1] - qoff;
         Lk = a.cu_k[b + 1] - a.cu_k[b];
     }
+    const int kb0 = split * a.split_len;                // first key of this workgroup's range
+    if (a.n_splits > 1) Lk = min(Lk - kb0, a.split_len);
     const int q0 = qt * kBQ;
     if (q0 >= Lq) return;                               // whole workgroup, before any barrier
     const int hk = h / (a.Hq / a.Hkv);
@@ -772,9 +779,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     }
 
     const int64_t khead = (int64_t)b * a.Hkv + hk;
-    const int8_t* kbase = a.k8 + khead * a.nk_pad * DP;
-    const float* ksbase = a.ks + khead * (a.nk_pad >> a.gk_shift);
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vt) + khead * DP * a.nk_pad * C::VE;
+    const int8_t* kbase = a.k8 + khead * a.nk_pad * DP + (int64_t)kb0 * DP;
+    const float* ksbase = a.ks + khead * (a.nk_pad >> a.gk_shift) + (kb0 >> a.gk_shift);
+    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vt) + (khead * DP * a.nk_pad + kb0) * C::VE;
     const int64_t vrow_stride = (int64_t)a.nk_pad * C::VE;
     const bool ks16 = a.gk_shift == 4;                  // K scale groups of 16 keys (else 64)
 
@@ -977,7 +984,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         const float l_tot = ls[j][0];                   // the row-sum MFMA covers both lane halves
         const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
         if (qrow < Lq) {
-            uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) +
+            uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + split * a.split_out +
                              (a.cu_q ? (int64_t)(qoff + qrow) * a.on + (int64_t)h * a.oh
                                      : (int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)qrow * a.on);
 #pragma unroll
@@ -1025,7 +1032,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
             if (hh == 0 && qrow < Lq) {
                 const float corr = a.kmean ? a.sm_scale * qscale[j] * dot : 0.f;
                 const float lse = (m_ref[j] + __log2f(l_tot) - p_log2_scale) * kLn2 + corr;
-                const int64_t li = a.lse_varlen ? (int64_t)h * a.total_q + qoff + qrow : qhead * a.Nq + qrow;
+                const int64_t li = split * a.split_lse +
+                                   (a.lse_varlen ? (int64_t)h * a.total_q + qoff + qrow : qhead * a.Nq + qrow);
                 a.lse[li] = lse;
             }
         }

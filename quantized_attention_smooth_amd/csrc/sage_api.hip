@@ -402,7 +402,6 @@ int sage_attn_fwd_splitkv(const sage_attn_params* p, int n_splits, void* workspa
     if (p->struct_size < sizeof(sage_attn_params)) return fail(SAGE_EINVAL, "struct_size too small");
     if (int r = check_attn(p, false)) return r;
     if (n_splits < 1 || n_splits > 64) return fail(SAGE_EINVAL, "n_splits %d must be 1..64", n_splits);
-    if (p->v_dtype != SAGE_V_FP8) return fail(SAGE_EUNSUPPORTED, "split-KV needs FP8 V");
     if (p->is_causal) return fail(SAGE_EUNSUPPORTED, "split-KV is non-causal only");
     const SplitPlan sp = split_plan(p->B, p->Hq, p->Nq, p->Nk, p->d, n_splits);
     if (!workspace || !aligned(workspace, 256)) return fail(SAGE_EINVAL, "workspace NULL or not 256-byte aligned");
@@ -425,7 +424,8 @@ int sage_attn_fwd_splitkv(const sage_attn_params* p, int n_splits, void* workspa
     a.split_lse = rows;
     a.pack_gqa = pack_gqa(p);
     const bool out_bf16 = p->out_dtype == SAGE_BF16;
-    if (int r = hip_status(sage::launch_attn(a, dp_of(p->d), 0, out_bf16, st), "split-KV attention launch")) return r;
+    if (int r = hip_status(sage::launch_attn(a, dp_of(p->d), pv_kind(p), out_bf16, st), "split-KV attention launch"))
+        return r;
     sage::MergeArgs m{};
     m.parts = ws;
     m.ps = rows * d;

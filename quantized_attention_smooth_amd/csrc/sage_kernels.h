@@ -77,7 +77,7 @@ struct AttnArgs {
     int total_q;
     int n_qtiles;                // query tiles per (b, h)
     int num_wg;
-    // split-KV (FP8 V, dense, non-causal): workgroup split s of a query tile
+    // split-KV (dense, non-causal): workgroup split s of a query tile
     // covers keys [s * split_len, min(Nk, (s + 1) * split_len)) and writes its
     // output and LSE split_out / split_lse elements after split 0's
     int pack_gqa;                // FP8 V, non-causal, dense only: rows of all query heads of a K/V head together

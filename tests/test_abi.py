@@ -304,7 +304,6 @@ SPLIT_BREAKS = {
     "n_splits 0": (lambda p: None, 0, 1 << 24, 0, A.SAGE_EINVAL),
     "n_splits 65": (lambda p: None, 65, 1 << 24, 0, A.SAGE_EINVAL),
     "causal": (lambda p: setattr(p, "is_causal", 1), 4, 1 << 24, 0, A.SAGE_EUNSUPPORTED),
-    "fp16 V": (lambda p: setattr(p, "v_dtype", A.SAGE_V_FP16), 4, 1 << 24, 0, A.SAGE_EUNSUPPORTED),
     "workspace too small": (lambda p: None, 4, 4096, 0, A.SAGE_EINVAL),
     "workspace misaligned": (lambda p: None, 4, 1 << 24, 128, A.SAGE_EINVAL),
     "head_dim 129": (lambda p: setattr(p, "d", 129), 4, 1 << 24, 0, A.SAGE_EINVAL),

@@ -21,34 +21,38 @@ from parity_utils import COS_EMU, COS_EXACT, cosine, out_ulp
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # B, Hq, Hkv, Nq, Nk, d, dtype, layout, gran, smooth_v, n_splits, lse
-    (1, 8, 2, 4, 4133, 128, "fp16", "HND", "per_thread", False, 5, True),
-    (2, 4, 4, 33, 3000, 64, "bf16", "NHD", "per_warp", True, 3, True),
-    (1, 2, 2, 300, 1000, 96, "fp16", "HND", "per_block", False, 7, False),
-    (1, 4, 1, 1, 640, 128, "bf16", "HND", "per_thread", False, 64, True),
+    # B, Hq, Hkv, Nq, Nk, d, dtype, layout, gran, smooth_v, n_splits, lse, V
+    (1, 8, 2, 4, 4133, 128, "fp16", "HND", "per_thread", False, 5, True, "fp8"),
+    (2, 4, 4, 33, 3000, 64, "bf16", "NHD", "per_warp", True, 3, True, "fp8"),
+    (1, 2, 2, 300, 1000, 96, "fp16", "HND", "per_block", False, 7, False, "fp8"),
+    (1, 4, 1, 1, 640, 128, "bf16", "HND", "per_thread", False, 64, True, "fp8"),
+    (1, 4, 2, 8, 2100, 128, "fp16", "HND", "per_thread", False, 4, True, "fp16"),
+    (2, 2, 2, 40, 900, 64, "bf16", "NHD", "per_warp", True, 3, False, "fp16"),
 ]
 
 
-def _quantize(q, k, v, layout, gran, smooth_v):
-    return sage.sage_quant_qkv(q, k, v, tensor_layout=layout, qk_quant_gran=gran, smooth_k=True, v_dtype="fp8",
+def _quantize(q, k, v, layout, gran, smooth_v, v_dtype="fp8"):
+    return sage.sage_quant_qkv(q, k, v, tensor_layout=layout, qk_quant_gran=gran, smooth_k=True, v_dtype=v_dtype,
                                smooth_v=smooth_v)
 
 
-@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_Nq{}_Nk{}_d{}_{}_{}_{}_sv{}_S{}".format(*c[:11]))
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_Nq{}_Nk{}_d{}_{}_{}_{}_sv{}_S{}_V{}".format(
+    *c[:11], c[12]))
 def test_splitkv_matches_oracle(case):
-    B, Hq, Hkv, Nq, Nk, d, dtype, layout, gran, smooth_v, ns, want_lse = case
+    B, Hq, Hkv, Nq, Nk, d, dtype, layout, gran, smooth_v, ns, want_lse, v_dtype = case
     print(f"[gpu-case] split-KV {case} seed 2", flush=True)
     w = workloads.WORKLOADS["b2h8n4096d128"]
     inp = workloads.make_inputs(w, {"B": B, "Hq": Hq, "Hkv": Hkv, "Nq": Nq, "Nk": Nk, "d": d, "dtype": dtype,
                                     "layout": layout})
     dev = torch.device("cuda:0")
     q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
-    qk, qv = _quantize(q, k, v, layout, gran, smooth_v)
+    qk, qv = _quantize(q, k, v, layout, gran, smooth_v, v_dtype)
     res = sage.sage_attn_fwd_splitkv(qk, qv, n_splits=ns, tensor_layout=layout, return_lse=want_lse)
     out, lse = res if want_lse else (res, None)
     torch.cuda.synchronize()
     ref = oracle.reference_forward_splitkv(*(inp[x].float().numpy() for x in ("q", "k", "v")), dtype=dtype,
-                                           n_splits=ns, layout=layout, gran=gran, smooth_v=smooth_v)
+                                           n_splits=ns, layout=layout, gran=gran, smooth_v=smooth_v,
+                                           v_dtype=v_dtype)
     got = out.float().cpu().numpy()
     if layout == "NHD":
         got = got.transpose(0, 2, 1, 3)
@@ -135,3 +139,17 @@ def test_sageattn_kv_splits_matches_oracle():
         assert (np.abs(got[b] - r) <= tol).all()
     with pytest.raises(NotImplementedError):
         sage.sageattn(q, k, v, is_causal=True, kv_splits=2)
+
+
+def test_one_range_fp16_v_is_bit_identical_to_attn_fwd():
+    print("[gpu-case] split-KV fp16 V one range vs sage_attn_fwd: B1 H4 Nq200 Nk700 d128 bf16 seed 2", flush=True)
+    w = workloads.WORKLOADS["b2h8n4096d128"]
+    inp = workloads.make_inputs(w, {"B": 1, "Hq": 4, "Hkv": 4, "Nq": 200, "Nk": 700, "dtype": "bf16"})
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    qk, qv = _quantize(q, k, v, "HND", "per_thread", False, "fp16")
+    o1, l1 = sage.sage_attn_fwd(qk, qv, return_lse=True)
+    o2, l2 = sage.sage_attn_fwd_splitkv(qk, qv, n_splits=1, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)

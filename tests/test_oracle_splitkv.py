@@ -33,10 +33,11 @@ def _inputs(**kw):
     return [inp[x].float().numpy() for x in ("q", "k", "v")]
 
 
-def test_one_range_is_the_rounded_forward():
+@pytest.mark.parametrize("v_dtype", ["fp8", "fp16"])
+def test_one_range_is_the_rounded_forward(v_dtype):
     q, k, v = _inputs(B=1, Hq=2, Hkv=1, Nq=9, Nk=700, d=96)
-    s = oracle.reference_forward_splitkv(q, k, v, dtype="fp16", n_splits=1, gran="per_warp")
-    r = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_warp", v_dtype="fp8")
+    s = oracle.reference_forward_splitkv(q, k, v, dtype="fp16", n_splits=1, gran="per_warp", v_dtype=v_dtype)
+    r = oracle.reference_forward(q, k, v, dtype="fp16", gran="per_warp", v_dtype=v_dtype)
     want = oracle.round_half(r["out"][0].astype(np.float32), "fp16")
     np.testing.assert_array_equal(s["out"][0], want)
     np.testing.assert_array_equal(s["lse"][0], r["lse"][0])
