@@ -33,6 +33,7 @@ CASES = [
     (2, 1, 1, 1, 1, "fp16", "NHD"),
     (16, 1, 2, 300, 64, "bf16", "NHD"),
     (64, 1, 1, 40, 128, "fp16", "HND"),      # the largest number of parts the call accepts
+    (2, 1, 2, 5, 1024, "bf16", "HND"),       # the largest head size the call accepts
 ]
 
 

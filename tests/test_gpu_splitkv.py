@@ -95,7 +95,7 @@ def test_decode_shape_close_to_exact_attention():
     assert np.abs(lse.cpu().numpy()[0] - ex["lse"][0]).max() < 0.05
 
 
-@pytest.mark.parametrize("nq", [1, 16, 100])
+@pytest.mark.parametrize("nq", [1, 16, 100, 128])
 def test_packed_gqa_rows_equal_repeated_kv(nq):
     """Few queries with grouped K/V heads run with the rows of a group packed
     into one workgroup; every row's arithmetic is unchanged, so the result is
