@@ -16,6 +16,9 @@ combining two partial results of the workload's output shape; `vs_torch_sdpa`
 times sageattn against torch's scaled_dot_product_attention on the WSL page's
 comparison shape and on the benchmark workload; `splitkv` compares the plain
 kernel with the split-KV forward on a 16-query, 32 768-key GQA shape.
+
+`--sweep` prints, instead, attention-kernel TOPS over sequence lengths
+1K-32K (non-causal and causal) beside torch SDPA.
 """
 from __future__ import annotations
 
@@ -265,6 +268,76 @@ def time_vs_sdpa(w, warmup: int = 10, iters: int = 100) -> dict:
     return rec
 
 
+SWEEP_N = (1024, 2048, 4096, 8192, 16384, 32768)
+SWEEP_TOKENS = 32768                    # batch * N, the same number of query tokens at every length
+SWEEP_H, SWEEP_D, SWEEP_SEED = 32, 128, 8
+
+
+def time_sweep(warmup: int = 5, iters: int = 20, sdpa: bool = True) -> dict:
+    """Attention-kernel TOPS over sequence lengths 1K-32K, non-causal and
+    causal, the sweep the deployment guide's benchmark scripts run (section
+    6).  The guide gives no batch, head count or head dimension; this sweep
+    holds H=32, d=128, fp16, HND and batch * N = 32768 tokens, with per_warp
+    INT8 Q/K and smooth_k.  Each length is timed with FP8 V and with fp16 V
+    (the guide's INT8 QK + FP16 PV script), and torch's fused SDPA
+    (flash or memory-efficient backend) is timed on the same inputs in
+    place of the guide's FlashAttention baseline.  Quantization runs once
+    per configuration, outside the timed calls, as in the pages' kernel-only
+    TOPS."""
+    import numpy as np
+    import torch
+    import quantized_attention_smooth_amd as sage
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    import workloads
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    # one draw of standard normals (the workload recipe), viewed as (B, H, N, d) for each length
+    rng = np.random.default_rng(SWEEP_SEED)
+    shape = (SWEEP_TOKENS * SWEEP_H, SWEEP_D)
+    flat = [workloads.round_to(rng.standard_normal(shape, dtype=np.float32), "fp16").to(dev) for _ in range(3)]
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    rows = []
+    for causal in (False, True):
+        for n in SWEEP_N:
+            b = SWEEP_TOKENS // n
+            q, k, v = (t.view(b, SWEEP_H, n, SWEEP_D) for t in flat)
+            ops = 4.0 * b * SWEEP_H * n * n * SWEEP_D / (2.0 if causal else 1.0)
+            row = {"N": n, "B": b, "causal": causal}
+            for vd, acc in (("fp8", "fp16+fp32"), ("fp16", "fp32")):
+                qk, qv = sage.sage_quant_qkv(q, k, v, qk_quant_gran="per_warp", smooth_k=True, v_dtype=vd)
+                ms = timed(lambda: sage.sage_attn_fwd(qk, qv, is_causal=causal, pv_accum_dtype=acc))
+                row[f"sage_{vd}v_ms"] = round(ms, 4)
+                row[f"sage_{vd}v_tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
+                del qk, qv
+            if sdpa:
+                try:
+                    with sdpa_kernel([SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION]):
+                        ms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(q, k, v,
+                                                                                            is_causal=causal))
+                    row["sdpa_ms"] = round(ms, 4)
+                    row["sdpa_tops"] = round(ops / (ms * 1e-3) / 1e12, 1)
+                except RuntimeError as e:      # no fused SDPA kernel for this shape
+                    row["sdpa_error"] = str(e)[:200]
+            print(f"[sweep] {row}", file=sys.stderr, flush=True)
+            rows.append(row)
+    return {"shape": f"H{SWEEP_H} d{SWEEP_D} fp16 HND, B*N = {SWEEP_TOKENS}, per_warp, smooth_k",
+            "warmup": warmup, "iters": iters, "tops": "4*B*H*N*N*d per call (halved for causal) / kernel time",
+            "rows": rows}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +353,9 @@ def main() -> int:
     ap.add_argument("--secondary", default="video_dit_n17550",
                     help="a second workload whose attention-kernel TOPS is reported beside the main line "
                          "('none' to skip); the metric is quoted at sequence 4096 and 17.5k")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step line, print one JSON line with attention-kernel TOPS over sequence "
+                         "lengths 1K-32K, non-causal and causal, against torch SDPA")
     ap.add_argument("--traffic-calibration", action="store_true",
                     help="before the steps, run a plain 1 GiB -> 1 GiB fp32 elementwise copy three times, so "
                          "that hardware byte counters of the attention kernel can be scaled by what the same "
@@ -290,6 +366,10 @@ def main() -> int:
         print("bench.py measures one GPU only: the quantized attention forward here runs on a single "
               "MI355X (--gpus 1); multi-GPU sharding is not part of this build.", file=sys.stderr)
         return 2
+
+    if args.sweep:
+        print(json.dumps({"sweep": time_sweep(sdpa=not args.no_sdpa)}), flush=True)
+        return 0
 
     import workloads
 
