@@ -197,7 +197,9 @@ void oracle_quant_v_fp8(const float* v, int n, int dp, uint8_t* codes, float* sc
  *           (tau = 0 is the textbook update), and the running sums are
  *           rescaled by 2^(m_old - m_new);
  *   P       the exponent is formed in fp32, in the order the GPU kernel uses:
- *           with B = 1.5 * 2^23 (so that B + S_ij is exact in fp32),
+ *           with B = 10680707 = 2^23 + 0x22F983 (the integer the GPU's
+ *           accumulator bias, the bits of fp32 1/(2 pi), stands for; B + S_ij
+ *           is exact in fp32 and stays in [2^23, 2^24) for |S_ij| <= 2064512),
  *           c_ij = fl32(nb_i - B f_ij) and x_ij = fl32((B + S_ij) f_ij + c_ij),
  *           each with one rounding (fused multiply-adds), nb_i = fl32(L - m_i);
  *           p_ij = fl32(2^x_ij).  On the FP8 path L = fl32(log2 448) - tau,
@@ -308,7 +310,7 @@ int oracle_attn_rows(int nq, int nk, int dp,
                 m = mt;
             }
             volatile float nb = L - m;
-            const float B = 12582912.0f;                  /* 1.5 * 2^23 */
+            const float B = 10680707.0f;                  /* 2^23 + 0x22F983 */
             for (int j = t0; j <= t1; ++j) {
                 float cj = fmaf(-B, f[j], nb);                   /* one rounding */
                 float x = fmaf(B + (float)S[j], f[j], cj);       /* B + S exact; one rounding */

@@ -267,6 +267,19 @@ __device__ __forceinline__ void load_kfrag_kb(const uint8_t* ks, int n, int hh, 
 // S^T of one row block: S[kb][i] = bias + S(query n of the block,
 // key 32*kb + 8*(i/4) + 4*hh + i%4).  Two accumulation chains over the
 // channel blocks; the first MFMA of each takes the bias vector as input.
+// First MFMA of a score chain: K.Q^T of one channel block plus the
+// accumulator bias, which enters as the inline constant 1/(2 pi) (the bits
+// kAccBiasBits) and so needs no registers.  It is inline assembly because
+// the compiler hoists a constant accumulator operand out of the key loop into
+// registers instead of encoding it.  The destination is early-clobber: an
+// MFMA may not write registers it is still reading.
+static_assert(kAccBiasBits == 0x3E22F983, "the inline constant below is these bits");
+__device__ __forceinline__ v16i mfma_i8_biased(const v4i& a, const v4i& b) {
+    v16i d;
+    asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, 0.15915494" : "=&v"(d) : "v"(a), "v"(b));
+    return d;
+}
+
 template <int DP>
 __device__ __forceinline__ void qk_half(const v4i (&kf)[2][DP / 32], const v4i (&qf)[DP / 32], const v16i& biasv,
                                         v16i (&S)[2]) {
@@ -775,7 +788,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
             for (int cb = 0; cb < NCB; ++cb) qf[j][cb] = v4i{0, 0, 0, 0};
             qscale[j] = 0.f;
         }
-        cq[j] = (qscale[j] * a.sm_scale) * kLog2e;      // log2-domain factor of this row
+        cq[j] = ((qscale[j] * a.sm_scale) * kLog2e) * kAccScale;   // log2-domain factor of this row, times 2^26
     }
 
     const int64_t khead = (int64_t)b * a.Hkv + hk;
@@ -1149,7 +1162,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) qf[cb] = v4i{0, 0, 0, 0};
     }
-    const float cq = (qscale * a.sm_scale) * kLog2e;
+    const float cq = ((qscale * a.sm_scale) * kLog2e) * kAccScale;   // times 2^26, exact
 
     const int64_t khead = (int64_t)b * a.Hkv + hk;
     const int8_t* kbase = a.k8 + khead * a.nk_pad * DP + (int64_t)kb0 * DP;
@@ -1165,12 +1178,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i) o[cb][i] = 0.f;
     v4f ls = v4f{0.f, 0.f, 0.f, 0.f};
     float m_ref = -INFINITY, m_prev;
-    v16i biasv;
+    v16i biasv;                                         // for the one-at-a-time tiles after the pipelined loop
 #pragma unroll
     for (int i = 0; i < 16; ++i) biasv[i] = kAccBiasBits;
-    // d = 64 has registers to spare: keep the bias in 16 VGPRs for the whole
-    // loop instead of rebuilding it before every QK^T
-    if constexpr (DP == 64) asm volatile("" : "+v"(biasv));
     Ones<PV> ones;
     make_ones<PV>(ones, rowsum_parity(lane));
 
@@ -1251,7 +1261,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
                 constexpr int k = decltype(kc)::value;
                 if constexpr (k < NQK) {
                     constexpr int kb = k & 1, cb = k >> 1;
-                    S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[cb], cb == 0 ? biasv : S[kb], 0, 0, 0);
+                    if constexpr (cb == 0) S[kb] = mfma_i8_biased(kf[kb][cb], qf[cb]);
+                    else S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[cb], S[kb], 0, 0, 0);
                 } else if constexpr (k < NQK + NPV) {
                     pv8_job<DP, k - NQK>(va, P, o);
                 } else {

@@ -19,11 +19,16 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 
 // MFMA accumulator bias: the int32 QK^T accumulators start at the bit pattern
-// of 1.5 * 2^23, so that for |S| < 2^22 the accumulated integer, read as an
-// fp32, is exactly 1.5 * 2^23 + S (no int -> float conversion needed).
-// |S| <= 128 * 127 * 127 = 2064512 < 2^22 for head_dim <= 128.
-constexpr int kAccBiasBits = 0x4B400000;
-constexpr float kAccBias = 12582912.0f;
+// of fp32 1/(2 pi), 0x3E22F983, whose mantissa field is M = 0x22F983.  For
+// -M <= S < 2^23 - M the accumulated integer stays in the binade [1/8, 1/4),
+// so read as an fp32 it is exactly (K + S) * 2^-26 with K = 2^23 + M =
+// 10680707: no int -> float conversion is needed, and the row factor carries
+// the 2^26 (kAccScale).  |S| <= 128 * 127 * 127 = 2064512 < M for
+// head_dim <= 128.  gfx950 encodes 1/(2 pi) as an inline constant, so the
+// first MFMA of a score chain takes the bias without a register.
+constexpr int kAccBiasBits = 0x3E22F983;
+constexpr float kAccBias = 0x1.45F306p-3f;              // the same bits as an fp32 (K * 2^-26)
+constexpr float kAccScale = 0x1p26f;
 constexpr int kNegInfBits = (int)0xFF800000u;   // -inf; smallest signed int32 of any score
 
 __device__ __forceinline__ float bits_f(int x) { return __int_as_float(x); }
