@@ -264,9 +264,6 @@ __device__ __forceinline__ void load_kfrag_kb(const uint8_t* ks, int n, int hh, 
     kf[kb][cb] = *reinterpret_cast<const v4i*>(ks + row * DP + swz<DP>(row, cb * 2 + hh) * 16);
 }
 
-// S^T of one row block: S[kb][i] = bias + S(query n of the block,
-// key 32*kb + 8*(i/4) + 4*hh + i%4).  Two accumulation chains over the
-// channel blocks; the first MFMA of each takes the bias vector as input.
 // First MFMA of a score chain: K.Q^T of one channel block plus the
 // accumulator bias, which enters as the inline constant 1/(2 pi) (the bits
 // kAccBiasBits) and so needs no registers.  It is inline assembly because
@@ -280,14 +277,18 @@ __device__ __forceinline__ v16i mfma_i8_biased(const v4i& a, const v4i& b) {
     return d;
 }
 
+// S^T of one row block: S[kb][i] = bias + S(query n of the block,
+// key 32*kb + 8*(i/4) + 4*hh + i%4).  Two accumulation chains over the
+// channel blocks; the first MFMA of each adds the accumulator bias.
 template <int DP>
-__device__ __forceinline__ void qk_half(const v4i (&kf)[2][DP / 32], const v4i (&qf)[DP / 32], const v16i& biasv,
-                                        v16i (&S)[2]) {
+__device__ __forceinline__ void qk_half(const v4i (&kf)[2][DP / 32], const v4i (&qf)[DP / 32], v16i (&S)[2]) {
 #pragma unroll
-    for (int cb = 0; cb < DP / 32; ++cb)
+    for (int kb = 0; kb < 2; ++kb) S[kb] = mfma_i8_biased(kf[kb][0], qf[0]);
+#pragma unroll
+    for (int cb = 1; cb < DP / 32; ++cb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
-            S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[cb], cb == 0 ? biasv : S[kb], 0, 0, 0);
+            S[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[cb], S[kb], 0, 0, 0);
 }
 
 // V^T operand of P.V for one tile.  FP8: a[cb] = the 32 bytes of channel row cb*32 + n for the keys of
@@ -809,9 +810,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         ls[j] = v4f{0.f, 0.f, 0.f, 0.f};
     }
     float m_ref[2] = {-INFINITY, -INFINITY}, m_prev[2];
-    v16i biasv;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) biasv[i] = kAccBiasBits;
     Ones<PV> ones;
     make_ones<PV>(ones, rowsum_parity(lane));
 
@@ -868,7 +866,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         load_kfrag<DP>(stage_of(0), n, hh, kf);
         ks_of(stage_of(0), ksv);
         load_va<DP, PV>(stage_of(0) + C::KT_BYTES, n, hh, va);
-        qk_half<DP>(kf, qf[0], biasv, S[0]);
+        qk_half<DP>(kf, qf[0], S[0]);
     }
     auto pv_region_job = [&](auto kc, const PHalf<PV>& Pj, v16f (&oj)[NCB], v4f& lsj) {
         constexpr int k = decltype(kc)::value;
@@ -900,8 +898,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                 [&](auto kc) {
                     constexpr int k = decltype(kc)::value;
                     constexpr int cb = k >> 1, kb = k & 1;
-                    S[1][kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[1][cb], cb == 0 ? biasv : S[1][kb],
-                                                                     0, 0, 0);
+                    if constexpr (cb == 0) S[1][kb] = mfma_i8_biased(kf[kb][cb], qf[1][cb]);
+                    else S[1][kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[1][cb], S[1][kb], 0, 0, 0);
                     if constexpr (k == 0) load_va<DP, PV>(st + C::KT_BYTES, n, hh, va);   // V of tile t
                     if constexpr (k >= 1 && k - 1 < NDMA / 2) copier.template issue<k - 1>(st_copy, tc);
                 },
@@ -924,8 +922,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                 [&](auto kc) {
                     constexpr int k = decltype(kc)::value;
                     constexpr int cb = k >> 1, kb = k & 1;
-                    S[0][kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[0][cb], cb == 0 ? biasv : S[0][kb],
-                                                                     0, 0, 0);
+                    if constexpr (cb == 0) S[0][kb] = mfma_i8_biased(kf[kb][cb], qf[0][cb]);
+                    else S[0][kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[0][cb], S[0][kb], 0, 0, 0);
                     if constexpr (k >= 1 && k - 1 < NDMA - NDMA / 2) copier.template issue<NDMA / 2 + k - 1>(st_copy, tc);
                     if constexpr (k == NQK - 1) ks_of(st_next, ksv);                     // K scales of tile t+1
                 },
@@ -955,8 +953,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
             const uint8_t* st = stage_of(t);
             ks_of(st, ksv);
             load_kfrag<DP>(st, n, hh, kf);
-            qk_half<DP>(kf, qf[0], biasv, S[0]);
-            qk_half<DP>(kf, qf[1], biasv, S[1]);
+            qk_half<DP>(kf, qf[0], S[0]);
+            qk_half<DP>(kf, qf[1], S[1]);
             const bool need_mask = (k0 + kBK > Lk) || (a.causal && k0 + kBK - 1 > wq0);
             PHalf<PV> P[2];
             bool raised[2];
@@ -1178,9 +1176,6 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i) o[cb][i] = 0.f;
     v4f ls = v4f{0.f, 0.f, 0.f, 0.f};
     float m_ref = -INFINITY, m_prev;
-    v16i biasv;                                         // for the one-at-a-time tiles after the pipelined loop
-#pragma unroll
-    for (int i = 0; i < 16; ++i) biasv[i] = kAccBiasBits;
     Ones<PV> ones;
     make_ones<PV>(ones, rowsum_parity(lane));
 
@@ -1336,7 +1331,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
             ks_of(st, ksv);
             load_kfrag<DP>(st, n, hh, kf);
             v16i Sm[2];
-                qk_half<DP>(kf, qf, biasv, Sm);
+                qk_half<DP>(kf, qf, Sm);
             const bool need_mask = (k0 + kBK > Lk) || (a.causal && k0 + kBK - 1 > wq0);
             PHalf<PV> Pm;
             bool raised;
@@ -1437,9 +1432,6 @@ __global__ __launch_bounds__(kThreads) void qk_scores_kernel(AttnArgs a) {
     const int8_t* kbase = a.k8 + ((int64_t)b * a.Hkv + hk) * a.nk_pad * DP;
     const int ntiles = (a.Nk + kBK - 1) / kBK;
     unsigned long long s1 = 0, s2 = 0;
-    v16i biasv;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) biasv[i] = kAccBiasBits;
     constexpr int KCPR = DP / 16, K_LOADS = kBK * DP / (16 * kThreads);
     for (int t = 0; t < ntiles; ++t) {
         uint4 kr[K_LOADS];
@@ -1456,7 +1448,7 @@ __global__ __launch_bounds__(kThreads) void qk_scores_kernel(AttnArgs a) {
         v4i kf[2][DP / 32];
         load_kfrag<DP>(ks, n, hh, kf);
         v16i acc[2][2];
-        qk_half<DP>(kf, qf[0], biasv, acc[0]);
+        qk_half<DP>(kf, qf[0], acc[0]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
