@@ -97,6 +97,23 @@ def test_workload_outputs(name, big_cases):
     _announce(f"{name}: cos vs oracle {c_emu:.6f}, vs exact fp64 {c_ex:.6f}")
 
 
+# ------------------------------------------------------------------ the longest sweep length
+@pytest.mark.parametrize("causal", [False, True])
+def test_sequence_32k_outputs(causal):
+    """N = 32 768, the longest length of the benchmark sweep (1K-32K): two
+    heads of the sweep's shape (d = 128, fp16, HND, per_warp, FP8 V, smooth_k),
+    quantization bit-exact and sampled rows (tile edges, the middle, the last
+    rows) against the oracle."""
+    w = dataclasses.replace(workloads.WORKLOADS["b2h8n4096d128"], name="n32768_h2", B=1, Hq=2, Hkv=2, Nq=32768,
+                            Nk=32768, causal=causal, return_lse=True, seed=9)
+    _announce(f"{w.name}: B1 H2 N32768 d128 fp16 HND causal={causal} per_warp V=fp8 seed 9")
+    c = Case(w, workloads.make_inputs(w)).run_gpu(return_lse=True)
+    c.run_oracle(rows=sample_rows(w.seed, 24), exact=True)
+    c.check_quantized_bitexact()
+    c_emu, c_ex = c.check_outputs(lse=True)
+    _announce(f"{w.name} causal={causal}: cos vs oracle {c_emu:.6f}, vs exact fp64 {c_ex:.6f}")
+
+
 # ------------------------------------------------------------------ edge-case matrix
 SMALL = [
     # (Nq, Nk, d): ragged tails, Nq != Nk, padded head dims
