@@ -70,8 +70,8 @@ struct AttnCfg {
     static constexpr int VE = PV == 0 ? 1 : 2;          // V element bytes
     static constexpr int VROW = kBK * VE;               // V^T tile row (one channel) bytes
     static constexpr int VT_BYTES = DP * VROW;
-    static constexpr int SC_OFF = KT_BYTES + VT_BYTES;  // the tile's K scales, one 256-byte slot per reading wavefront
-    static constexpr int STAGE = KT_BYTES + VT_BYTES + NR * 256;
+    static constexpr int SC_BYTES = NR * 256;           // the tile's K scales, one 256-byte slot per reading wavefront
+    static constexpr int STAGE = KT_BYTES + VT_BYTES + SC_BYTES;
     static constexpr int NI = (KT_BYTES + VT_BYTES) / (16 * 64 * NW);   // tile DMA instructions per copying wavefront
     static constexpr int NSC = NR / NW;                 // scale copies per copying wavefront
     static_assert(NI * 16 * 64 * NW == KT_BYTES + VT_BYTES, "tile must fill whole copy rounds");
@@ -80,10 +80,34 @@ struct AttnCfg {
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
+// One stage of the LDS ring of NST stages.  The ring keeps its K tiles, its
+// V^T tiles and its K-scale slots in three regions (all K tiles first, then
+// all V^T tiles, then all scale slots), so that within each region every
+// stage is a constant offset below 64 KB from one base address.
+struct StagePtrs {
+    uint8_t* k;                                         // K tile
+    uint8_t* v;                                         // V^T tile
+    uint8_t* s;                                         // K-scale slots
+};
+template <class C, int NST>
+__device__ __forceinline__ StagePtrs ring_stage(uint8_t* smem, int u) {
+    return {smem + u * C::KT_BYTES, smem + NST * C::KT_BYTES + u * C::VT_BYTES,
+            smem + NST * (C::KT_BYTES + C::VT_BYTES) + u * C::SC_BYTES};
+}
+// The 4-wave kernel's ring keeps each stage's K tile, V^T tile and scale
+// slots together, in that order.
+template <class C>
+__device__ __forceinline__ StagePtrs ring_stage_packed(uint8_t* smem, int u) {
+    uint8_t* st = smem + u * C::STAGE;
+    return {st, st + C::KT_BYTES, st + C::KT_BYTES + C::VT_BYTES};
+}
+
 // Direct global -> LDS copy of one key tile into one stage of the ring, as
 // NI + NSC instructions per copying wavefront that the key loop can place one
 // by one.  Instruction i < NI of copying wavefront w (of NW) fills the 1 KB of
-// granules [(NW*i + w) * 64, +64); lane L writes granule (NW*i + w) * 64 + L.
+// granules [(NW*i + w) * 64, +64) of the tile (K granules first, then V^T
+// granules, each in its own region of the stage); lane L writes granule
+// (NW*i + w) * 64 + L.
 // The granule at (row, physical chunk c) receives logical chunk swz(row, c)
 // (the swizzle is an involution), so readers address logical chunk c at
 // swz(row, c).  Instruction NI + j copies the tile's K scales into the 256-byte
@@ -102,7 +126,7 @@ struct TileCopy {
     int wave, lane;                                     // wave is wave-uniform (an SGPR)
 
     template <int I>
-    __device__ __forceinline__ void issue(uint8_t* stage, int t) const {
+    __device__ __forceinline__ void issue(const StagePtrs& stage, int t) const {
         using C = AttnCfg<DP, PV, NW, NR>;
         constexpr int KG = C::KT_BYTES / 16, KCPR = DP / 16, VCPR = C::VROW / 16;
         static_assert(KG % 64 == 0, "K tile must fill whole wavefront chunks");
@@ -118,17 +142,19 @@ struct TileCopy {
                 return vbase + row * vrow_stride + (int64_t)t * C::VROW + ch * 16;
             };
             const uint8_t* src;
-            if constexpr ((I + 1) * NW * 64 <= KG) src = k_src();
-            else if constexpr (I * NW * 64 >= KG) src = v_src();
-            else src = gbase < KG ? k_src() : v_src();
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + gbase * 16), 16, 0, 0);
+            uint8_t* dst;
+            if constexpr ((I + 1) * NW * 64 <= KG) src = k_src(), dst = stage.k + gbase * 16;
+            else if constexpr (I * NW * 64 >= KG) src = v_src(), dst = stage.v + (gbase - KG) * 16;
+            else if (gbase < KG) src = k_src(), dst = stage.k + gbase * 16;
+            else src = v_src(), dst = stage.v + (gbase - KG) * 16;
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)dst, 16, 0, 0);
         } else {
             const float* src = ks16 ? ksbase + 4 * t + (lane & 3) : ksbase + t;
             const int slot = wave + NW * (I - C::NI);
-            __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage + C::SC_OFF + slot * 256), 4, 0, 0);
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(stage.s + slot * 256), 4, 0, 0);
         }
     }
-    __device__ __forceinline__ void issue_all(uint8_t* stage, int t) const {
+    __device__ __forceinline__ void issue_all(const StagePtrs& stage, int t) const {
         using C = AttnCfg<DP, PV, NW, NR>;
         static_for<0, C::NI + C::NSC>([&](auto i) { issue<decltype(i)::value>(stage, t); });
     }
@@ -170,27 +196,28 @@ struct TileCopyBuf {
     }
 
     template <int I>
-    __device__ __forceinline__ void issue(uint8_t* stage, int t) const {
+    __device__ __forceinline__ void issue(const StagePtrs& stage, int t) const {
         constexpr int KG = C::KT_BYTES / 16;
         if constexpr (I < C::NI) {
             const int gbase = (NW * I + wave) * 64;
-            lds_ptr_t dst = (lds_ptr_t)(stage + gbase * 16);
+            lds_ptr_t kdst = (lds_ptr_t)(stage.k + gbase * 16);
+            lds_ptr_t vdst = (lds_ptr_t)(stage.v + (gbase - KG) * 16);
             if constexpr ((I + 1) * NW * 64 <= KG) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, voff[I], (uint32_t)t * C::KT_BYTES, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, voff[I], (uint32_t)t * C::KT_BYTES, 0, 0);
             } else if constexpr (I * NW * 64 >= KG) {
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, voff[I], (uint32_t)t * C::VROW, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, voff[I], (uint32_t)t * C::VROW, 0, 0);
             } else {
-                if (gbase < KG) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, voff[I], (uint32_t)t * C::KT_BYTES, 0, 0);
-                else __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, voff[I], (uint32_t)t * C::VROW, 0, 0);
+                if (gbase < KG) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, kdst, 16, voff[I], (uint32_t)t * C::KT_BYTES, 0, 0);
+                else __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, vdst, 16, voff[I], (uint32_t)t * C::VROW, 0, 0);
             }
         } else {
             const int slot = wave + NW * (I - C::NI);
-            lds_ptr_t dst = (lds_ptr_t)(stage + C::SC_OFF + slot * 256);
+            lds_ptr_t dst = (lds_ptr_t)(stage.s + slot * 256);
             const uint32_t so = ks16 ? (uint32_t)t * 16u : (uint32_t)t * 4u;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 4, voff[C::NI], so, 0, 0);
         }
     }
-    __device__ __forceinline__ void issue_all(uint8_t* stage, int t) const {
+    __device__ __forceinline__ void issue_all(const StagePtrs& stage, int t) const {
         static_for<0, C::NI + C::NSC>([&](auto i) { issue<decltype(i)::value>(stage, t); });
     }
 };
@@ -201,8 +228,8 @@ template <int DP, int PV, int NW, int NR>
 struct TileCopyBuf {
     __device__ TileCopyBuf(const int8_t*, const uint8_t*, uint32_t, const float*, uint32_t, uint32_t, uint32_t, bool,
                            int, int) {}
-    template <int I> __device__ void issue(uint8_t*, int) const {}
-    __device__ void issue_all(uint8_t*, int) const {}
+    template <int I> __device__ void issue(const StagePtrs&, int) const {}
+    __device__ void issue_all(const StagePtrs&, int) const {}
 };
 #endif
 
@@ -247,33 +274,21 @@ __device__ __forceinline__ void load_kfrag(const uint8_t* ks, int n, int hh, v4i
     }
 }
 
-// The K fragments of one 32-channel block (both 32-key halves).
-template <int DP>
-__device__ __forceinline__ void load_kfrag_cb(const uint8_t* ks, int n, int hh, int cb, v4i (&kf)[2][DP / 32]) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-        const int row = kb * 32 + n;
-        kf[kb][cb] = *reinterpret_cast<const v4i*>(ks + row * DP + swz<DP>(row, cb * 2 + hh) * 16);
-    }
-}
-
-// One K fragment: keys 32*kb .. +31, channel block cb.
-template <int DP>
-__device__ __forceinline__ void load_kfrag_kb(const uint8_t* ks, int n, int hh, int kb, int cb, v4i (&kf)[2][DP / 32]) {
-    const int row = kb * 32 + n;
-    kf[kb][cb] = *reinterpret_cast<const v4i*>(ks + row * DP + swz<DP>(row, cb * 2 + hh) * 16);
-}
-
 // First MFMA of a score chain: K.Q^T of one channel block plus the
 // accumulator bias, which enters as the inline constant 1/(2 pi) (the bits
 // kAccBiasBits) and so needs no registers.  It is inline assembly because
 // the compiler hoists a constant accumulator operand out of the key loop into
 // registers instead of encoding it.  The destination is early-clobber: an
-// MFMA may not write registers it is still reading.
+// MFMA may not write registers it is still reading.  The compiler's hazard
+// checks do not look inside inline assembly, so the statement brings its own
+// two wait states for a VALU instruction that writes a or b just before it
+// (the compiler places such copies, e.g. from AGPRs).  Its result is read
+// only by the next MFMA of the same chain, as the accumulator of the same
+// opcode, which the hardware forwards.
 static_assert(kAccBiasBits == 0x3E22F983, "the inline constant below is these bits");
 __device__ __forceinline__ v16i mfma_i8_biased(const v4i& a, const v4i& b) {
     v16i d;
-    asm("v_mfma_i32_32x32x32_i8 %0, %1, %2, 0.15915494" : "=&v"(d) : "v"(a), "v"(b));
+    asm("s_nop 1\n\tv_mfma_i32_32x32x32_i8 %0, %1, %2, 0.15915494" : "=&v"(d) : "v"(a), "v"(b));
     return d;
 }
 
@@ -314,17 +329,6 @@ __device__ __forceinline__ void load_va(const uint8_t* vs, int n, int hh, VA<DP,
             for (int u = 0; u < 4; ++u) va.a[cb][u] = *reinterpret_cast<const v4i*>(r + swz<C::VROW>(row, 4 * hh + u) * 16);
         }
     }
-}
-
-// The FP8 V^T operand of one 32-channel block.
-template <int DP>
-__device__ __forceinline__ void load_va_cb(const uint8_t* vs, int n, int hh, int cb, VA<DP, 0>& va) {
-    constexpr int VROW = kBK;
-    const int row = cb * 32 + n;
-    const uint8_t* r = vs + row * VROW;
-    const v4i lo = *reinterpret_cast<const v4i*>(r + swz<VROW>(row, 2 * hh) * 16);
-    const v4i hi = *reinterpret_cast<const v4i*>(r + swz<VROW>(row, 2 * hh + 1) * 16);
-    va.a[cb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
 // P of one tile for one row block, as the P.V B operand.  FP8: w holds the
@@ -813,9 +817,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     Ones<PV> ones;
     make_ones<PV>(ones, rowsum_parity(lane));
 
-    auto stage_of = [&](int t) { return smem + (t % NST) * C::STAGE; };
-    auto ks_of = [&](const uint8_t* st, float (&ksv)[4]) {
-        const v4f k4 = *reinterpret_cast<const v4f*>(st + C::SC_OFF + wave * 256);
+    auto stage_of = [&](int t) { return ring_stage_packed<C>(smem, t % NST); };
+    auto ks_of = [&](const StagePtrs& st, float (&ksv)[4]) {
+        const v4f k4 = *reinterpret_cast<const v4f*>(st.s + wave * 256);
 #pragma unroll
         for (int g = 0; g < 4; ++g) ksv[g] = k4[g];
     };
@@ -863,9 +867,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     float ksv[4];
     VA<DP, PV> va;
     if (n_main > 0 && live) {
-        load_kfrag<DP>(stage_of(0), n, hh, kf);
+        load_kfrag<DP>(stage_of(0).k, n, hh, kf);
         ks_of(stage_of(0), ksv);
-        load_va<DP, PV>(stage_of(0) + C::KT_BYTES, n, hh, va);
+        load_va<DP, PV>(stage_of(0).v, n, hh, va);
         qk_half<DP>(kf, qf[0], S[0]);
     }
     auto pv_region_job = [&](auto kc, const PHalf<PV>& Pj, v16f (&oj)[NCB], v4f& lsj) {
@@ -879,10 +883,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     };
     for (int t = 0; t < n_main; ++t) {
         const int tc = min(t + AHEAD, ntiles - 1);      // tile copied in this step (clamped)
-        uint8_t* st_copy = stage_of(t + AHEAD);
+        const StagePtrs st_copy = stage_of(t + AHEAD);
         if (live) {
-            const uint8_t* st = stage_of(t);
-            const uint8_t* st_next = stage_of(t + 1);
+            const StagePtrs st = stage_of(t);
+            const StagePtrs st_next = stage_of(t + 1);
             // H0
             SoftmaxPieces<PV> s0;
             interleave<NPV + NRS, 4>([&](auto kc) { pv_region_job(kc, P[1], o[1], ls[1]); },
@@ -900,7 +904,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                     constexpr int cb = k >> 1, kb = k & 1;
                     if constexpr (cb == 0) S[1][kb] = mfma_i8_biased(kf[kb][cb], qf[1][cb]);
                     else S[1][kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[kb][cb], qf[1][cb], S[1][kb], 0, 0, 0);
-                    if constexpr (k == 0) load_va<DP, PV>(st + C::KT_BYTES, n, hh, va);   // V of tile t
+                    if constexpr (k == 0) load_va<DP, PV>(st.v, n, hh, va);   // V of tile t
                     if constexpr (k >= 1 && k - 1 < NDMA / 2) copier.template issue<k - 1>(st_copy, tc);
                 },
                 [&](auto ec) { s0.template piece<decltype(ec)::value>(S[0], P[0]); });
@@ -909,7 +913,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
             interleave<NPV + NRS, 4>(
                 [&](auto kc) {
                     pv_region_job(kc, P[0], o[0], ls[0]);
-                    if constexpr (decltype(kc)::value == 0) load_kfrag<DP>(st_next, n, hh, kf);   // K of tile t+1
+                    if constexpr (decltype(kc)::value == 0) load_kfrag<DP>(st_next.k, n, hh, kf);   // K of tile t+1
                 },
                 [&](auto hc) { s1.template head<decltype(hc)::value>(S[1], ksv, cq[1], m_ref[1], m_prev[1]); });
             if (__any(s1.raise)) {
@@ -950,9 +954,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         issue(t + AHEAD);
         const int k0 = t * kBK;
         if (live && (!a.causal || k0 <= wq0 + 63)) {
-            const uint8_t* st = stage_of(t);
+            const StagePtrs st = stage_of(t);
             ks_of(st, ksv);
-            load_kfrag<DP>(st, n, hh, kf);
+            load_kfrag<DP>(st.k, n, hh, kf);
             qk_half<DP>(kf, qf[0], S[0]);
             qk_half<DP>(kf, qf[1], S[1]);
             const bool need_mask = (k0 + kBK > Lk) || (a.causal && k0 + kBK - 1 > wq0);
@@ -976,7 +980,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                 o_guard<DP>(o[1]);
             }
             VA<DP, PV> va;
-            load_va<DP, PV>(st + C::KT_BYTES, n, hh, va);
+            load_va<DP, PV>(st.v, n, hh, va);
             pv_all<DP, PV>(va, P[0], ones, o[0], ls[0]);
             pv_all<DP, PV>(va, P[1], ones, o[1], ls[1]);
         }
@@ -1179,12 +1183,37 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     Ones<PV> ones;
     make_ones<PV>(ones, rowsum_parity(lane));
 
-    auto stage_of = [&](int t) { return smem + (t % NST) * C::STAGE; };
-    auto ks_of = [&](const uint8_t* st, float (&ksv)[4]) {
-        const v4f k4 = *reinterpret_cast<const v4f*>(st + C::SC_OFF + wave * 256);
+    auto stage_of = [&](int t) { return ring_stage<C, NST>(smem, t % NST); };
+    auto ks_of = [&](const StagePtrs& st, float (&ksv)[4]) {
+        const v4f k4 = *reinterpret_cast<const v4f*>(st.s + wave * 256);
 #pragma unroll
         for (int g = 0; g < 4; ++g) ksv[g] = k4[g];
     };
+    // This lane's LDS addresses in ring stage 0, held in registers for the
+    // whole loop: the K fragments of each channel block, the two 16-byte
+    // halves of its V^T operand, and its wavefront's K-scale slot.  A read of
+    // stage u in the pipelined loop adds only a constant below 64 KB (u times
+    // the region's bytes per stage, plus the key or channel block), which the
+    // LDS instruction takes as its immediate offset.  The empty asm statements
+    // keep the compiler from recombining the bases with those constants, which
+    // costs an add per read.
+    typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+    typedef __attribute__((address_space(3))) const v4i lds_v4i;
+    typedef __attribute__((address_space(3))) const v4f lds_v4f;
+    lds_u8* kp[NCB];
+    lds_u8* vp[2];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+        kp[cb] = (lds_u8*)(smem + n * DP + swz<DP>(n, cb * 2 + hh) * 16);
+        asm volatile("" : "+v"(kp[cb]));
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        vp[e] = (lds_u8*)(smem + NST * C::KT_BYTES + n * C::VROW + swz<C::VROW>(n, 2 * hh + e) * 16);
+        asm volatile("" : "+v"(vp[e]));
+    }
+    lds_u8* sp_slot = (lds_u8*)(smem + NST * (C::KT_BYTES + C::VT_BYTES) + wave * 256);
+    asm volatile("" : "+v"(sp_slot));
     const TileCopyBuf<DP, PV, NW, NW> copier(kbase, vbase, (uint32_t)vrow_stride, ksbase,
                                                   (uint32_t)(a.nk_pad - kb0) * DP, (uint32_t)(a.nk_pad * DP - kb0),
                                                   (uint32_t)((a.nk_pad - kb0) >> a.gk_shift) * 4u, ks16, wave, lane);
@@ -1237,9 +1266,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     float ksv[4];
     VA<DP, PV> va;
     if (n_main > 0 && live) {
-        load_kfrag<DP>(stage_of(0), n, hh, kf);
+        load_kfrag<DP>(stage_of(0).k, n, hh, kf);
         ks_of(stage_of(0), ksv);
-        load_va<DP, PV>(stage_of(0) + C::KT_BYTES, n, hh, va);
+        load_va<DP, PV>(stage_of(0).v, n, hh, va);
     }
     constexpr int NH = NQK + NPV + NRS;                 // matrix-core jobs of H
     static_assert(NPV + NRS >= 3, "room for the group maxima");
@@ -1248,10 +1277,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     auto regionH = [&](auto u, int t, SoftmaxPieces<PV, KS16>& sp) {
         constexpr int U = decltype(u)::value;
         const int tc = min(t + AHEAD, ntiles - 1);
-        uint8_t* st_copy = smem + ((U + AHEAD) % NST) * C::STAGE;
+        constexpr int UN = (U + 1) % NST;               // stage of tile t+1
+        const StagePtrs st_copy = ring_stage<C, NST>(smem, (U + AHEAD) % NST);
         if (live) {
-            const uint8_t* st = smem + U * C::STAGE;
-            const uint8_t* st_next = smem + ((U + 1) % NST) * C::STAGE;
             static_for<0, NH>([&](auto kc) {
                 constexpr int k = decltype(kc)::value;
                 if constexpr (k < NQK) {
@@ -1267,18 +1295,24 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
                 if constexpr (k == 0) sp.prep(ksv, cq);
                 if constexpr (k == NQK - 1) {           // K of tile t+1 (kf is free once the last QK^T MFMA issued)
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) {
-                        load_kfrag_kb<DP>(st_next, n, hh, 0, cb, kf);
-                        load_kfrag_kb<DP>(st_next, n, hh, 1, cb, kf);
-                    }
+                    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                        for (int kb = 0; kb < 2; ++kb)
+                            kf[kb][cb] = *(lds_v4i*)(kp[cb] + UN * C::KT_BYTES + kb * 32 * DP);
                 }
                 // group maxima of tile t, one or two per P.V MFMA
                 if constexpr (k == NQK + 1) { sp.gmax(S[0], 0); sp.gmax(S[0], 1); }
                 if constexpr (k == NQK + 2) { sp.gmax(S[1], 2); sp.gmax(S[1], 3); }
                 if constexpr (k == NH - 1) {            // V of tile t (va is free once the last P.V MFMA issued)
-                    ks_of(st_next, ksv);
+                    const v4f k4 = *(lds_v4f*)(sp_slot + UN * C::SC_BYTES);
 #pragma unroll
-                    for (int cb = 0; cb < NCB; ++cb) load_va_cb<DP>(st + C::KT_BYTES, n, hh, cb, va);
+                    for (int g = 0; g < 4; ++g) ksv[g] = k4[g];
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) {
+                        const int off = U * C::VT_BYTES + cb * 32 * C::VROW;
+                        const v4i lo = *(lds_v4i*)(vp[0] + off), hi = *(lds_v4i*)(vp[1] + off);
+                        va.a[cb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    }
                 }
                 sched_fence();
             });
@@ -1327,9 +1361,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         issue(t + AHEAD);
         const int k0 = t * kBK;
         if (live && (!a.causal || k0 <= wq0 + 31)) {
-            const uint8_t* st = stage_of(t);
+            const StagePtrs st = stage_of(t);
             ks_of(st, ksv);
-            load_kfrag<DP>(st, n, hh, kf);
+            load_kfrag<DP>(st.k, n, hh, kf);
             v16i Sm[2];
                 qk_half<DP>(kf, qf, Sm);
             const bool need_mask = (k0 + kBK > Lk) || (a.causal && k0 + kBK - 1 > wq0);
@@ -1341,7 +1375,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
                 raised = softmax_half<PV, false>(Sm, ksv, cq, m_ref, m_prev, Pm, k0, Lk, a.causal, qrow, hh);
             if (__any(raised)) rescale_half<DP>(m_ref, m_prev, o, ls);
             VA<DP, PV> vam;
-            load_va<DP, PV>(st + C::KT_BYTES, n, hh, vam);
+            load_va<DP, PV>(st.v, n, hh, vam);
             pv8_all<DP>(vam, Pm, ones, o, ls);
         }
         step_end(t);
