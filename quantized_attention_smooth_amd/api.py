@@ -247,13 +247,17 @@ def sage_attn_fwd(qk: QuantQK, qv: QuantV, *, tensor_layout: str = "HND", is_cau
 
 
 PACK_MAX_NQ = 128       # the library packs the query heads of a K/V head together up to this many queries
+MI355X_CUS = 256        # compute units of one MI355X
 
 
-def splitkv_plan(B: int, Hq: int, Nq: int, Nk: int, n_splits: Optional[int] = None, Hkv: Optional[int] = None) -> int:
-    """Number of key ranges to ask for: enough workgroups to fill the GPU
-    (about 512, two per compute unit) with ranges of at least 256 keys.  With
-    grouped K/V heads and few queries, the library runs the rows of all query
-    heads of a K/V head in one workgroup, so there are fewer row tiles."""
+def splitkv_plan(B: int, Hq: int, Nq: int, Nk: int, n_splits: Optional[int] = None, Hkv: Optional[int] = None,
+                 cus: int = MI355X_CUS) -> int:
+    """Number of key ranges to ask for: as many as fit one round of
+    workgroups, one per compute unit (an attention workgroup takes a whole
+    CU), with ranges of at least 256 keys and at most 64 ranges.  A second,
+    partial round would leave most CUs idle while it runs.  With grouped K/V
+    heads and few queries, the library runs the rows of all query heads of a
+    K/V head in one workgroup, so there are fewer row tiles."""
     if n_splits is not None:
         return int(n_splits)
     Hkv = Hq if Hkv is None else Hkv
@@ -261,7 +265,7 @@ def splitkv_plan(B: int, Hq: int, Nq: int, Nk: int, n_splits: Optional[int] = No
         tiles = B * Hkv * ((Hq // Hkv * Nq + 255) // 256)
     else:
         tiles = B * Hq * ((Nq + 255) // 256)
-    return max(1, min(64, -(-512 // tiles), Nk // 256))
+    return max(1, min(64, cus // tiles, Nk // 256))
 
 
 def sage_attn_fwd_splitkv(qk: QuantQK, qv: QuantV, *, n_splits: Optional[int] = None, tensor_layout: str = "HND",

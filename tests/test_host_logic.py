@@ -37,16 +37,20 @@ def test_merge_rejects_before_any_call(case):
 def test_splitkv_plan():
     # explicit request is passed through
     assert sage.splitkv_plan(1, 8, 16, 4096, n_splits=7) == 7
-    # enough ranges to fill ~512 workgroups, ranges of at least 256 keys, at most 64
-    assert sage.splitkv_plan(1, 8, 16, 32768, Hkv=8) == 64
+    # as many ranges as fit one round of 256 workgroups, ranges of at least 256 keys, at most 64
+    assert sage.splitkv_plan(1, 8, 16, 32768, Hkv=8) == 32
     assert sage.splitkv_plan(1, 8, 16, 1024, Hkv=8) == 4
     assert sage.splitkv_plan(4, 32, 2048, 32768, Hkv=32) == 1
+    assert sage.splitkv_plan(1, 1, 16, 1 << 20) == 64
+    assert sage.splitkv_plan(1, 3, 16, 1 << 20) == 64          # 3 tiles x 64 ranges = 192 workgroups
+    assert sage.splitkv_plan(1, 5, 16, 1 << 20) == 51          # 5 x 51 = 255 <= 256
     # packed GQA rows: the 4 query heads of a K/V head share one row tile
-    assert sage.splitkv_plan(4, 32, 16, 32768, Hkv=8) == 16
-    assert sage.splitkv_plan(4, 32, 200, 32768, Hkv=8) == 4       # 200 > 128 queries: not packed
+    assert sage.splitkv_plan(4, 32, 16, 32768, Hkv=8) == 8
+    assert sage.splitkv_plan(4, 32, 200, 32768, Hkv=8) == 2       # 200 > 128 queries: not packed
     for B, Hq, Hkv, Nq, Nk in [(1, 1, 1, 1, 1), (2, 64, 8, 33, 100000), (16, 16, 16, 4096, 4096)]:
         n = sage.splitkv_plan(B, Hq, Nq, Nk, Hkv=Hkv)
         assert 1 <= n <= 64
+        assert n == 1 or n * (B * Hkv if Hq > Hkv and Nq <= 128 else B * Hq) <= 256
         assert len(oracle.splitkv_ranges(Nk, n)) <= n
 
 
