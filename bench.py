@@ -3,7 +3,11 @@
 
 One step = one pass of the whole hot path over one batch already resident in
 HBM: sage_quant_qkv (K mean and V statistics, INT8 Q/K, FP8 V^T, in two
-launches) and sage_attn_fwd (INT8 QK^T, online softmax, FP8 P.V).  The default workload
+launches) and sage_attn_fwd (INT8 QK^T, online softmax, FP8 P.V).  The step
+rate (`value`) comes from replaying the step captured in a HIP graph, which
+removes the Python launch overhead between the kernels (`--eager` times eager
+launches instead; `ms_per_step_eager` always reports them); kernel times come
+from HIP events around eager launches.  The default workload
 is B=2, H=8, N=4096, head_dim=128, fp16, per_warp INT8 Q/K, FP8 V.
 
 Prints ONE JSON line.  `value` is whole-step TOPS (4*B*H*Nq*Nk*d per step,
@@ -144,6 +148,49 @@ def time_workload(w, steps: int, warmup: int, calibrate: bool = False):
     quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / steps
     attn_ms = sum(e[1].elapsed_time(e[2]) for e in events) / steps
     return inp, ms_per_step, quant_ms, attn_ms
+
+
+def time_step_graph(w, inp, steps: int, warmup: int):
+    """The same step (fused quantize + attention on the resident inputs),
+    captured once into a HIP graph and replayed: the three kernels run
+    unchanged, without the Python launch overhead between them.  Returns
+    (ms per step from the host clock, output of the last replay, output of one
+    eager step for comparison)."""
+    import torch
+    import quantized_attention_smooth_amd as sage
+
+    dev = torch.device("cuda:0")
+    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    ws_k = torch.empty(sage.workspace_bytes(w.B, w.Hkv, w.Nk, w.d), dtype=torch.uint8, device=dev)
+    ws_v = torch.empty_like(ws_k)
+
+    def step():
+        qk, qv = sage.sage_quant_qkv(q, k, v, tensor_layout=w.layout, qk_quant_gran=w.gran, smooth_k=w.smooth_k,
+                                     v_dtype=w.v_dtype, smooth_v=w.smooth_v, workspace_k=ws_k, workspace_v=ws_v)
+        return sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, is_causal=w.causal,
+                                  return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            eager = step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    eager = eager[0].clone() if isinstance(eager, tuple) else eager.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    out = out[0] if isinstance(out, tuple) else out
+    return (t1 - t0) * 1e3 / steps, out, eager
 
 
 def time_merge(w, parts: int = 2, iters: int = 50) -> dict:
@@ -353,6 +400,9 @@ def main() -> int:
     ap.add_argument("--secondary", default="video_dit_n17550",
                     help="a second workload whose attention-kernel TOPS is reported beside the main line "
                          "('none' to skip); the metric is quoted at sequence 4096 and 17.5k")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the step from eager launches only (by default the step rate comes from replaying "
+                         "the step captured in a HIP graph; kernel times always come from the eager launches)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step line, print one JSON line with attention-kernel TOPS over sequence "
                          "lengths 1K-32K, non-causal and causal, against torch SDPA")
@@ -374,7 +424,14 @@ def main() -> int:
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
-    inp, ms_per_step, quant_ms, attn_ms = time_workload(w, args.steps, args.warmup, args.traffic_calibration)
+    inp, ms_eager, quant_ms, attn_ms = time_workload(w, args.steps, args.warmup, args.traffic_calibration)
+    ms_per_step, launch = ms_eager, "eager"
+    if not args.eager:
+        import torch
+        ms_graph, out_g, out_e = time_step_graph(w, inp, args.steps, args.warmup)
+        if not torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)):
+            raise SystemExit("graph replay output differs from the eager step")
+        ms_per_step, launch = ms_graph, "hip_graph"
 
     ops = workloads.attention_ops(w)
     value = ops / (ms_per_step * 1e-3) / 1e12
@@ -392,6 +449,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "step_launch": launch,
+        "ms_per_step_eager": round(ms_eager, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
