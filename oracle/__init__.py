@@ -42,10 +42,9 @@ _LIB_OVERRIDE = os.environ.get("SAGE_ORACLE_LIB")
 Q_GROUP = {"per_block": 128, "per_warp": 32, "per_thread": 1}
 K_GROUP = {"per_block": 64, "per_warp": 64, "per_thread": 16}
 
-# key tile of the online softmax and the lazy-rescale threshold used by the
-# HIP kernel's schedule (see oracle_attn_rows in sage_oracle.c)
+# key tile of the online softmax (keys per block of the FlashAttention-style
+# update; see oracle_attn_rows in sage_oracle.c)
 DEFAULT_BK = 64
-DEFAULT_TAU = 3
 
 
 def build(force: bool = False) -> str:
@@ -84,8 +83,9 @@ def lib():
         L.oracle_quant_int8_rows.restype = None
         L.oracle_quant_v_fp8.argtypes = [P, i, i, P, P]
         L.oracle_quant_v_fp8.restype = None
-        L.oracle_attn_rows.argtypes = [i, i, i, P, P, P, P, P, P, P, P, ctypes.c_float, i, i, i, i, i,
-                                       i, P, P, P, P, P, P]
+        d_ = ctypes.c_double
+        L.oracle_attn_rows.argtypes = [i, i, i, P, P, P, P, P, P, P, P, ctypes.c_float, i, i, i, i, d_, d_,
+                                       i, P, P, P, P, P, P, P, P]
         L.oracle_attn_rows.restype = i
         L.oracle_attn_exact.argtypes = [i, i, i, P, P, P, ctypes.c_double, i, i, i, P, P, P]
         L.oracle_attn_exact.restype = i
@@ -187,7 +187,8 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
                       v_dtype: str = "fp8", smooth_k: bool = True, smooth_v: bool = False,
                       cu_seqlens_q: Optional[np.ndarray] = None, cu_seqlens_k: Optional[np.ndarray] = None,
                       rows: Optional[Callable[[int, int], np.ndarray]] = None, want_scores: bool = False,
-                      attention: bool = True, bk: int = DEFAULT_BK, tau: int = DEFAULT_TAU) -> dict:
+                      attention: bool = True, bk: int = DEFAULT_BK, exp_band=(0.0, 0.0),
+                      want_p: bool = False) -> dict:
     """Run every step of the quantized forward on the CPU.
 
     q, k, v: float32 arrays holding exact fp16/bf16 values, in the caller's
@@ -200,10 +201,13 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
       v8[b] (Hkv, Nk_b, Dp) uint8 codes (FP8) or v16[b] (Hkv, Nk_b, Dp) float32,
       v_scale[b] (Hkv, Dp), v_mean[b] (Hkv, Dp),
       rows[b], out[b] (Hq, nrows, d) float64, lse[b] (Hq, nrows), scores[b]
-      (Hq, nrows, Nk_b) int32 if want_scores, allow[b] (Hq, nrows, d): bound on
-      how far a 2-ulp difference in an exp2 evaluation can move each output
-      through P's rounding (see oracle_attn_rows), lse_pq[b] (Hq, nrows): the
-      share of lse due to rounding P to its operand format.
+      (Hq, nrows, Nk_b) int32 if want_scores, allow[b] (Hq, nrows, d): the most
+      that P operands formed from exponents within exp_band = (band_f, band_x)
+      of this evaluation's could move each output (see oracle_attn_rows;
+      zero for the default band), lse_pq[b] (Hq, nrows): the share of lse due
+      to rounding P to its operand format; with want_p, p[b] (Hq, nrows, Nk_b)
+      the P operand of every key at its tile's reference maximum and mref[b]
+      (Hq, nrows, Nk_b) float32 that maximum.
     """
     varlen = cu_seqlens_q is not None
     if varlen and cu_seqlens_k is None:
@@ -222,7 +226,8 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
         raise ValueError("Hq must be divisible by Hkv")
     grp = hq // hkv
     res = {k_: [] for k_ in ("q8", "q_scale", "k8", "k_scale", "k_mean", "v8", "v16", "v_scale", "v_mean",
-                             "rows", "out", "lse", "scores", "allow", "lse_pq")}
+                             "rows", "out", "lse", "scores", "allow", "lse_pq", "p", "mref")}
+    band_f, band_x = (float(exp_band[0]), float(exp_band[1]))
     L = lib()
     for (b, qb), (_, kb), (_, vb) in zip(qp, kp, vp):
         nq, nk = qb.shape[1], kb.shape[1]
@@ -265,7 +270,7 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
             continue
         r = np.arange(nq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows(b, nq), dtype=np.int32)
         res["rows"].append(r)
-        outs, lses, scs, alws, lpqs = [], [], [], [], []
+        outs, lses, scs, alws, lpqs, pds, mds = [], [], [], [], [], [], []
         p_mode = 0 if v_dtype == "fp8" else (2 if dtype == "bf16" else 1)
         for h in range(hq):
             hk = h // grp
@@ -276,21 +281,27 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
             sd = np.zeros((len(r), nk), dtype=np.int32) if want_scores else None
             al = np.zeros((len(r), dp), dtype=np.float64)
             lpq = np.zeros(len(r), dtype=np.float64)
+            pd = np.zeros((len(r), nk), dtype=np.float64) if want_p else None
+            md = np.zeros((len(r), nk), dtype=np.float32) if want_p else None
             vsc = vss[hk] if v_dtype == "fp8" else None
             rc = L.oracle_attn_rows(nq, nk, dp, _p(q8s[h]), _p(qs_row), _p(k8s[hk]), _p(ks_key),
                                     _p(np.ascontiguousarray(vvals[hk], dtype=np.float32)), _p(vsc),
                                     _p(vms[hk] if smooth_v else None), _p(kms[hk] if smooth_k else None),
-                                    sm32, int(causal), 0, bk, tau, p_mode, len(r), _p(r), _p(o), _p(ls), _p(sd),
-                                    _p(al), _p(lpq))
+                                    sm32, int(causal), 0, bk, p_mode, band_f, band_x, len(r), _p(r), _p(o), _p(ls),
+                                    _p(sd), _p(al), _p(lpq), _p(pd), _p(md))
             if rc != 0:
                 raise RuntimeError(f"oracle_attn_rows failed ({rc})")
             outs.append(o[:, :d]); lses.append(ls); alws.append(al[:, :d]); lpqs.append(lpq)
             if want_scores:
                 scs.append(sd)
+            if want_p:
+                pds.append(pd); mds.append(md)
         res["out"].append(np.stack(outs)); res["lse"].append(np.stack(lses)); res["allow"].append(np.stack(alws))
         res["lse_pq"].append(np.stack(lpqs))
         if want_scores:
             res["scores"].append(np.stack(scs))
+        if want_p:
+            res["p"].append(np.stack(pds)); res["mref"].append(np.stack(mds))
     return res
 
 
@@ -369,7 +380,7 @@ def splitkv_ranges(nk: int, n_splits: int):
 def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str, n_splits: int,
                               layout: str = "HND", sm_scale: Optional[float] = None, gran: str = "per_thread",
                               smooth_k: bool = True, smooth_v: bool = False, v_dtype: str = "fp8",
-                              rows: Optional[Callable[[int, int], np.ndarray]] = None) -> dict:
+                              rows: Optional[Callable[[int, int], np.ndarray]] = None, exp_band=(0.0, 0.0)) -> dict:
     """The split-KV forward (few queries against many keys; non-causal)
     step by step: quantize Q, K, V over the whole sequence as
     reference_forward does; for each key range (splitkv_ranges) run the
@@ -423,8 +434,8 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
                                         _p(np.ascontiguousarray(vval[a0:a1], dtype=np.float32)),
                                         _p(vs[hk] if v_dtype == "fp8" else None),
                                         _p(vm[hk] if smooth_v else None), _p(km[hk] if smooth_k else None),
-                                        sm32, 0, 0, DEFAULT_BK, DEFAULT_TAU, p_mode, len(r), _p(r), _p(o), _p(ls),
-                                        None, _p(al), None)
+                                        sm32, 0, 0, DEFAULT_BK, p_mode, float(exp_band[0]), float(exp_band[1]),
+                                        len(r), _p(r), _p(o), _p(ls), None, _p(al), None, None, None)
                 if rc != 0:
                     raise RuntimeError(f"oracle_attn_rows failed ({rc})")
                 # the range's output, rounded to the output dtype as it is stored

@@ -24,9 +24,10 @@
  * follows the readings listed in the repository's design notes; each function
  * says which.
  *
- * Precision: the quantization decisions (INT8 codes, FP8 codes of V and P) are
- * taken in fp32, the precision of the GPU kernels, so that codes can be
- * compared; every accumulation that decides no code is carried in fp64.
+ * Precision: every value that is rounded to a code (INT8 codes of Q and K, FP8
+ * codes of V and P) is formed in fp32, with one rounding per arithmetic step
+ * as written, so that codes are defined to the bit and can be compared; every
+ * accumulation that decides no code (means, P.V, row sums) is carried in fp64.
  *
  * Build: gcc -O2 -fopenmp -ffp-contract=off -fPIC -shared (no fast-math).
  */
@@ -189,44 +190,49 @@ void oracle_quant_v_fp8(const float* v, int n, int dp, uint8_t* codes, float* sc
  * following the method's steps in order:
  *   scores  S_ij = sum_c q8_ic k8_jc in exact integer arithmetic
  *           ([guide] sec. 1: QK^T by 8-bit integer multiplication);
- *   dequant f_ij = fl32(c_i * kscale_j), c_i = fl32(fl32(qscale_i * sm_scale)
- *           * log2(e)), s_ij = fl32(S_ij * f_ij)  (log2 domain);
- *   online softmax over key tiles of `bk` keys in ascending order
- *           ([amd-9070] sec. 2: blockwise like FlashAttention): the reference
- *           maximum m moves to the tile maximum when that exceeds m + tau
- *           (tau = 0 is the textbook update), and the running sums are
- *           rescaled by 2^(m_old - m_new);
- *   P       the exponent is formed in fp32, in the order the GPU kernel uses:
- *           with B = 10680707 = 2^23 + 0x22F983 (the integer the GPU's
- *           accumulator bias, the bits of fp32 1/(2 pi), stands for; B + S_ij
- *           is exact in fp32 and stays in [2^23, 2^24) for |S_ij| <= 2064512),
- *           c_ij = fl32(nb_i - B f_ij) and x_ij = fl32((B + S_ij) f_ij + c_ij),
- *           each with one rounding (fused multiply-adds), nb_i = fl32(L - m_i);
- *           p_ij = fl32(2^x_ij).  On the FP8 path L = fl32(log2 448) - tau,
- *           so p already carries P's static scale 448 / 2^tau, and the P.V
- *           operand is P_ij = E4M3FN(min(p, 448)); on the FP16 path L = 0 and
- *           P_ij is p rounded to fp16 (bf16 for bf16 inputs) ([guide] sec. 1:
- *           V in FP8 or FP16);
- *   sums    l = sum_j P_ij and acc_c = sum_j P_ij * V_jc, both over the same
- *           rounded P and in fp64, so the weights P_ij / l sum to one;
+ *   dequant c_i = fl32(fl32(qscale_i * sm_scale) * log2(e)) and
+ *           s_ij = fl32(fl32(S_ij * kscale_j) * c_i), the score in log2 units;
+ *   online softmax over key tiles of `bk` keys in ascending order, as in
+ *           FlashAttention ([amd-9070] sec. 2: the softmax is computed block
+ *           by block, each block with its own value range):
+ *             m' = max(m, largest visible s_ij of the tile),
+ *             the running sums are rescaled by alpha = 2^(m - m') when the
+ *             maximum moves (the first tile starts from zero sums),
+ *             x_ij = fl32(s_ij - m'),  p_ij = fl32(2^x_ij) <= 1;
+ *   P       the P.V operand: on the FP8 path P_ij = E4M3FN(fl32(p_ij * 448)),
+ *           P's static scale 448 putting p in [0, 1] at the top of the
+ *           format's range; on the FP16 path P_ij = fl16(p_ij) (bf16 for bf16
+ *           inputs) ([guide] sec. 1: V in FP8 or FP16);
+ *   sums    acc_c = sum_j P_ij V_jc and l = sum_j P_ij over the same rounded
+ *           P, in fp64: the normaliser sums the weights that multiply V, so
+ *           the normalised weights P_ij / l of a row sum to one and every
+ *           output is a convex combination of the rows of V;
  *   output  out_ic = acc_c * vscale_c / l + vmean_c (FP8 path; P's scale
  *           cancels between acc and l) or acc_c / l + vmean_c (FP16 path)
  *           ([guide] sec. 4.2: smooth_v adds back the mean it subtracted);
- *   lse     (m - L + log2 l) ln 2, plus sm_scale * sum_c q8_ic qscale_i kmean_c
- *           when K was smoothed, so that it is the log-sum-exp of the
- *           unsmoothed scores ([guide] sec. 4.1: return_lse).
+ *   lse     (m - log2(Pscale) + log2 l) ln 2, plus sm_scale * sum_c q8_ic
+ *           qscale_i kmean_c when K was smoothed, so that it is the
+ *           log-sum-exp of the unsmoothed scores ([guide] sec. 4.1:
+ *           return_lse); Pscale is 448 on the FP8 path and 1 otherwise.
  *
  * Causal masking keeps keys j <= i + causal_shift (top-left alignment when the
  * shift is 0); keys j >= nk do not exist.  Tiles with no visible key are
  * skipped.
  *
- * Rounding fragility: 2^x is evaluated here to the correctly rounded fp32
- * value; an implementation whose exp2 is accurate to 1 ulp may return a p up
- * to 2 ulps away, and that can move P across an FP8/fp16 rounding midpoint.
- * A change d of one P_ij moves out_i by d (V_jc - out_ic) / l, at most
- * |d| (|V_jc| + max_k |V_kc|) / l.  For every P whose code would change within
- * p (1 -+ 2^-22), `allow` (if not NULL) accumulates that bound (rescaled like
- * acc and normalised like out).
+ * Rounding sensitivity ("allowance").  Another evaluation of the same steps
+ * may form the exponent with a different rounding order; if its value of P_ij
+ * before the operand rounding lies within a factor 2^(+-delta_ij) of this
+ * one, with
+ *     delta_ij = band_f * f_ij + band_x * (|s_ij| + |m'| + 8),
+ *     f_ij = c_i * kscale_j (one integer score unit, in log2 units),
+ * its operand can differ from P_ij only where the interval
+ * [P 2^-delta, P 2^delta] contains a rounding boundary of the operand format.
+ * Changing the operands of a row by dP_j moves its output by
+ * sum_j dP_j (V_jc - out_c) / (l + sum_j dP_j), so for every such key the
+ * width of the operand interval is recorded, and `allow` (if not NULL)
+ * receives  sum_j |dP_j| |V_jc - out_c| / (l - sum_j |dP_j|)  in output units
+ * (each dP_j carried to the final reference maximum like acc).  With
+ * band_f = band_x = 0 the allowance is 0.
  *
  * q8: nq x dp; qscale: nq (per row, expanded from its group); k8: nk x dp;
  * kscale: nk (per key, expanded); vval: nk x dp values of the PV operand
@@ -236,7 +242,10 @@ void oracle_quant_v_fp8(const float* v, int n, int dp, uint8_t* codes, float* sc
  * rows: nrows query indices to compute; out: nrows x dp; lse: nrows or NULL;
  * sdump: nrows x nk int32 scores or NULL; allow: nrows x dp or NULL;
  * lse_pq: nrows or NULL, the part of lse that comes from rounding P to its
- * operand format: |ln(sum of rounded P) - ln(sum of unrounded P)|.          */
+ * operand format: |ln(sum of rounded P) - ln(sum of unrounded P)|;
+ * pdump: nrows x nk or NULL, the operand value P_ij of each key at its own
+ * tile's reference maximum (0 for keys the row does not see); mdump:
+ * nrows x nk or NULL, that reference maximum m' (-inf for unseen keys).       */
 static double p_operand(double p, int p_mode) {
     if (p_mode == 0) return e4m3_value(p < E4M3_MAX ? p : E4M3_MAX);
     return fmt_rne(p, p_mode == 2 ? 7 : 10, p_mode == 2 ? -126 : -14);
@@ -247,23 +256,25 @@ int oracle_attn_rows(int nq, int nk, int dp,
                      const int8_t* k8, const float* kscale,
                      const float* vval, const float* vscale, const float* vmean,
                      const float* kmean, float sm_scale, int causal, int causal_shift,
-                     int bk, int tau, int p_mode,
+                     int bk, int p_mode, double band_f, double band_x,
                      int nrows, const int32_t* rows,
-                     double* out, double* lse, int32_t* sdump, double* allow, double* lse_pq) {
+                     double* out, double* lse, int32_t* sdump, double* allow, double* lse_pq,
+                     double* pdump, float* mdump) {
     if (bk <= 0 || dp <= 0 || nk <= 0) return -1;
     const float LOG2E = 1.4426950408889634f;
-    const float L = p_mode == 0 ? (float)log2(E4M3_MAX) - (float)tau : 0.0f;
+    const double pscale = p_mode == 0 ? E4M3_MAX : 1.0;
     int err = 0;
 #pragma omp parallel for schedule(dynamic, 4)
     for (int ri = 0; ri < nrows; ++ri) {
         int i = rows[ri];
         if (i < 0 || i >= nq) { err = -2; continue; }
         int32_t* S = (int32_t*)malloc(sizeof(int32_t) * (size_t)nk);
-        float* f = (float*)malloc(sizeof(float) * (size_t)nk);
         float* s = (float*)malloc(sizeof(float) * (size_t)nk);
         double* acc = (double*)calloc((size_t)dp, sizeof(double));
-        double* alw = (double*)calloc((size_t)dp, sizeof(double));
-        double* vmax = (double*)calloc((size_t)dp, sizeof(double));
+        int* fj = (int*)malloc(sizeof(int) * (size_t)nk);           /* keys whose operand may differ */
+        double* fd = (double*)malloc(sizeof(double) * (size_t)nk);  /* their operand interval widths */
+        float* fm = (float*)malloc(sizeof(float) * (size_t)nk);     /* their tile's reference maximum */
+        int nflip = 0;
         const int8_t* qi = q8 + (size_t)i * dp;
         for (int j = 0; j < nk; ++j) {
             int64_t dot = 0;
@@ -275,9 +286,8 @@ int oracle_attn_rows(int nq, int nk, int dp,
         volatile float ci = qscale[i] * sm_scale;
         volatile float ci2 = ci * LOG2E;
         for (int j = 0; j < nk; ++j) {
-            volatile float fj = ci2 * kscale[j];
-            volatile float sj = (float)S[j] * fj;
-            f[j] = fj;
+            volatile float t = (float)S[j] * kscale[j];              /* fp32 products, one rounding each */
+            volatile float sj = t * ci2;
             s[j] = sj;
         }
         int last = nk - 1;
@@ -285,13 +295,10 @@ int oracle_attn_rows(int nq, int nk, int dp,
             long lim = (long)i + causal_shift;
             if (lim < last) last = (int)lim;
         }
-        /* largest |V| per channel, for the fragility bound */
-        for (int c = 0; c < dp; ++c) vmax[c] = 0.0;
-        for (int j = 0; j < nk; ++j)
-            for (int c = 0; c < dp; ++c) {
-                double a = fabs((double)vval[(size_t)j * dp + c]);
-                if (a > vmax[c]) vmax[c] = a;
-            }
+        if (pdump)
+            for (int j = 0; j < nk; ++j) pdump[(size_t)ri * nk + j] = 0.0;
+        if (mdump)
+            for (int j = 0; j < nk; ++j) mdump[(size_t)ri * nk + j] = -INFINITY;
         float m = -INFINITY;
         double l = 0.0, lu = 0.0;                          /* sums of rounded / unrounded P */
         for (int t0 = 0; t0 <= last; t0 += bk) {
@@ -299,41 +306,49 @@ int oracle_attn_rows(int nq, int nk, int dp,
             if (t1 > last) t1 = last;
             float mt = -INFINITY;
             for (int j = t0; j <= t1; ++j) if (s[j] > mt) mt = s[j];
-            volatile float thresh = m + (float)tau;     /* the decision is taken in fp32 */
-            if (m == -INFINITY || mt > thresh) {
-                if (m != -INFINITY) {
-                    float alpha = (float)exp2((double)m - (double)mt);
-                    l *= alpha;
-                    lu *= alpha;
-                    for (int c = 0; c < dp; ++c) { acc[c] *= alpha; alw[c] *= alpha; }
-                }
-                m = mt;
+            float mn = mt > m ? mt : m;                     /* m' = max(m, tile maximum) */
+            if (mn > m && m != -INFINITY) {
+                double alpha = exp2((double)m - (double)mn);
+                l *= alpha;
+                lu *= alpha;
+                for (int c = 0; c < dp; ++c) acc[c] *= alpha;
             }
-            volatile float nb = L - m;
-            const float B = 10680707.0f;                  /* 2^23 + 0x22F983 */
+            m = mn;
             for (int j = t0; j <= t1; ++j) {
-                float cj = fmaf(-B, f[j], nb);                   /* one rounding */
-                float x = fmaf(B + (float)S[j], f[j], cj);       /* B + S exact; one rounding */
-                float p = (float)exp2((double)x);
-                double pq = p_operand(p, p_mode);
+                volatile float x = s[j] - m;                 /* fp32 subtraction, x <= 0 */
+                float p = (float)exp2((double)x);            /* fp64 exp2 rounded to fp32 */
+                volatile float pp = (float)((double)p * pscale);   /* fl32(p * Pscale); exact when Pscale = 1 */
+                double pq = p_operand(pp, p_mode);
                 l += pq;
-                lu += (double)p;
-                double lo = p_operand((double)p * (1.0 - 0x1p-22), p_mode);
-                double hi = p_operand((double)p * (1.0 + 0x1p-22), p_mode);
-                double flip = fabs(hi - lo);
+                lu += (double)pp;
                 const float* vj = vval + (size_t)j * dp;
-                for (int c = 0; c < dp; ++c) {
-                    acc[c] += pq * (double)vj[c];
-                    if (flip > 0.0) alw[c] += flip * (fabs((double)vj[c]) + vmax[c]);
+                for (int c = 0; c < dp; ++c) acc[c] += pq * (double)vj[c];
+                if (pdump) pdump[(size_t)ri * nk + j] = pq;
+                if (mdump) mdump[(size_t)ri * nk + j] = m;
+                double delta = band_f * (double)ci2 * (double)kscale[j] +
+                               band_x * (fabs((double)s[j]) + fabs((double)m) + 8.0);
+                if (delta > 0.0) {
+                    double lo = p_operand((double)pp * exp2(-delta), p_mode);
+                    double hi = p_operand((double)pp * exp2(delta), p_mode);
+                    if (hi > lo) { fj[nflip] = j; fd[nflip] = hi - lo; fm[nflip] = m; ++nflip; }
                 }
             }
         }
+        double sum_dp = 0.0;                               /* interval widths at the final reference */
+        for (int k = 0; k < nflip; ++k) {
+            fd[k] *= exp2((double)fm[k] - (double)m);
+            sum_dp += fd[k];
+        }
         for (int c = 0; c < dp; ++c) {
-            double sc = p_mode == 0 ? (double)vscale[c] / l : 1.0 / l;
-            double o = acc[c] * sc;
-            if (vmean) o += vmean[c];
-            out[(size_t)ri * dp + c] = o;
-            if (allow) allow[(size_t)ri * dp + c] = alw[c] * sc;
+            double sc = p_mode == 0 ? (double)vscale[c] : 1.0;
+            double o = acc[c] / l;                          /* operand units */
+            out[(size_t)ri * dp + c] = o * sc + (vmean ? (double)vmean[c] : 0.0);
+            if (allow) {
+                double a = 0.0;
+                for (int k = 0; k < nflip; ++k) a += fd[k] * fabs((double)vval[(size_t)fj[k] * dp + c] - o);
+                double den = l - sum_dp;
+                allow[(size_t)ri * dp + c] = nflip == 0 ? 0.0 : (den > 0.0 ? a * sc / den : INFINITY);
+            }
         }
         if (lse) {
             double corr = 0.0;
@@ -341,10 +356,10 @@ int oracle_attn_rows(int nq, int nk, int dp,
                 for (int c = 0; c < dp; ++c) corr += (double)qi[c] * (double)qscale[i] * (double)kmean[c];
                 corr *= (double)sm_scale;
             }
-            lse[ri] = ((double)m - (double)L + log2(l)) * M_LN2 + corr;
+            lse[ri] = ((double)m - log2(pscale) + log2(l)) * M_LN2 + corr;
         }
         if (lse_pq) lse_pq[ri] = l > 0.0 ? fabs(log(l) - log(lu)) : 0.0;
-        free(S); free(f); free(s); free(acc); free(alw); free(vmax);
+        free(S); free(s); free(acc); free(fj); free(fd); free(fm);
     }
     return err;
 }

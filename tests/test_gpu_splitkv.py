@@ -16,7 +16,7 @@ import torch
 import oracle
 import workloads
 import quantized_attention_smooth_amd as sage
-from parity_utils import COS_EMU, COS_EXACT, cosine, out_ulp
+from parity_utils import COS_EMU, COS_EXACT, EXP_BAND, cosine, out_ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -52,7 +52,7 @@ def test_splitkv_matches_oracle(case):
     torch.cuda.synchronize()
     ref = oracle.reference_forward_splitkv(*(inp[x].float().numpy() for x in ("q", "k", "v")), dtype=dtype,
                                            n_splits=ns, layout=layout, gran=gran, smooth_v=smooth_v,
-                                           v_dtype=v_dtype)
+                                           v_dtype=v_dtype, exp_band=EXP_BAND)
     got = out.float().cpu().numpy()
     if layout == "NHD":
         got = got.transpose(0, 2, 1, 3)
@@ -131,7 +131,7 @@ def test_sageattn_kv_splits_matches_oracle():
     ns = sage.splitkv_plan(2, 8, 8, 5000, Hkv=8)
     assert ns > 1
     ref = oracle.reference_forward_splitkv(*(inp[x].float().numpy() for x in ("q", "k", "v")), dtype="fp16",
-                                           n_splits=ns)
+                                           n_splits=ns, exp_band=EXP_BAND)
     got = out.float().cpu().numpy()
     for b in range(2):
         r = ref["out"][b]

@@ -16,18 +16,28 @@ PINS = ["tests/test_oracle_codecs.py", "tests/test_oracle_quant.py", "tests/test
 
 MUTATIONS = {
     "online softmax: running sum not rescaled": ("l *= alpha;", ""),
-    "online softmax: accumulator not rescaled": ("{ acc[c] *= alpha; alw[c] *= alpha; }", "{ alw[c] *= alpha; }"),
-    "dequant: wrong key-group scale": ("volatile float fj = ci2 * kscale[j];",
-                                       "volatile float fj = ci2 * kscale[j + 1 < nk ? j + 1 : j];"),
-    "P scale 256 instead of 448": ("const float L = p_mode == 0 ? (float)log2(E4M3_MAX) - (float)tau : 0.0f;",
-                                   "const float L = p_mode == 0 ? (float)log2(256.0) - (float)tau : 0.0f;"),
-    "lse: smoothing correction sign": ("lse[ri] = ((double)m - (double)L + log2(l)) * M_LN2 + corr;",
-                                       "lse[ri] = ((double)m - (double)L + log2(l)) * M_LN2 - corr;"),
+    "online softmax: accumulator not rescaled": ("for (int c = 0; c < dp; ++c) acc[c] *= alpha;", ""),
+    # the reference maximum kept until a tile exceeds it by 3 (a lazy update)
+    "online softmax: lazy maximum (threshold 3)": ("float mn = mt > m ? mt : m;",
+                                                   "float mn = (m == -INFINITY || mt > m + 3.0f) ? mt : m;"),
+    # the exponent formed as (B + S) f + (-B f - m') with a large integer bias B
+    "exponent: biased fused form": ("volatile float x = s[j] - m;",
+                                    "volatile float x = fmaf(10680707.0f + (float)S[j], kscale[j] * ci2, "
+                                    "fmaf(-10680707.0f, kscale[j] * ci2, -m));"),
+    "row sum over unrounded P": ("l += pq;", "l += (double)pp;"),
+    "dequant: wrong key-group scale": ("volatile float t = (float)S[j] * kscale[j];",
+                                       "volatile float t = (float)S[j] * kscale[j + 1 < nk ? j + 1 : j];"),
+    "P scale 256 instead of 448": ("const double pscale = p_mode == 0 ? E4M3_MAX : 1.0;",
+                                   "const double pscale = p_mode == 0 ? 256.0 : 1.0;"),
+    "lse: smoothing correction sign": ("lse[ri] = ((double)m - log2(pscale) + log2(l)) * M_LN2 + corr;",
+                                       "lse[ri] = ((double)m - log2(pscale) + log2(l)) * M_LN2 - corr;"),
     "causal: diagonal masked": ("long lim = (long)i + causal_shift;\n            if (lim < last) last = (int)lim;",
                                 "long lim = (long)i + causal_shift - 1;\n            if (lim < last) last = (int)lim;"),
-    "epilogue: V scale dropped": ("double sc = p_mode == 0 ? (double)vscale[c] / l : 1.0 / l;",
-                                  "double sc = p_mode == 0 ? 1.0 / (448.0 * l) : 1.0 / l;"),
-    "epilogue: V mean not added back": ("if (vmean) o += vmean[c];", ""),
+    "epilogue: V scale dropped": ("double sc = p_mode == 0 ? (double)vscale[c] : 1.0;",
+                                  "double sc = p_mode == 0 ? 1.0 / 448.0 : 1.0;"),
+    "epilogue: V mean not added back": ("out[(size_t)ri * dp + c] = o * sc + (vmean ? (double)vmean[c] : 0.0);",
+                                        "out[(size_t)ri * dp + c] = o * sc;"),
+    "allowance: exponent band ignored": ("if (delta > 0.0) {", "if (delta < 0.0) {"),
     "INT8: truncation instead of rounding": ("float q = nearbyintf(t);", "float q = truncf(t);"),
     "INT8: scale amax/128": ("volatile float scale = amax / 127.0f;", "volatile float scale = amax / 128.0f;"),
     "tile max over one key": ("for (int j = t0; j <= t1; ++j) if (s[j] > mt) mt = s[j];",
