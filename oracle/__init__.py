@@ -85,7 +85,7 @@ def lib():
         L.oracle_quant_v_fp8.restype = None
         d_ = ctypes.c_double
         L.oracle_attn_rows.argtypes = [i, i, i, P, P, P, P, P, P, P, P, ctypes.c_float, i, i, i, i, d_, d_,
-                                       i, P, P, P, P, P, P, P, P]
+                                       i, P, P, P, P, P, P, P, P, P]
         L.oracle_attn_rows.restype = i
         L.oracle_attn_exact.argtypes = [i, i, i, P, P, P, ctypes.c_double, i, i, i, P, P, P]
         L.oracle_attn_exact.restype = i
@@ -205,7 +205,8 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
       that P operands formed from exponents within exp_band = (band_f, band_x)
       of this evaluation's could move each output (see oracle_attn_rows;
       zero for the default band), lse_pq[b] (Hq, nrows): the share of lse due
-      to rounding P to its operand format; with want_p, p[b] (Hq, nrows, Nk_b)
+      to rounding P to its operand format, lse_allow[b] (Hq, nrows): the most
+      those operand changes could move lse; with want_p, p[b] (Hq, nrows, Nk_b)
       the P operand of every key at its tile's reference maximum and mref[b]
       (Hq, nrows, Nk_b) float32 that maximum.
     """
@@ -226,7 +227,7 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
         raise ValueError("Hq must be divisible by Hkv")
     grp = hq // hkv
     res = {k_: [] for k_ in ("q8", "q_scale", "k8", "k_scale", "k_mean", "v8", "v16", "v_scale", "v_mean",
-                             "rows", "out", "lse", "scores", "allow", "lse_pq", "p", "mref")}
+                             "rows", "out", "lse", "scores", "allow", "lse_pq", "p", "mref", "lse_allow")}
     band_f, band_x = (float(exp_band[0]), float(exp_band[1]))
     L = lib()
     for (b, qb), (_, kb), (_, vb) in zip(qp, kp, vp):
@@ -270,7 +271,7 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
             continue
         r = np.arange(nq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows(b, nq), dtype=np.int32)
         res["rows"].append(r)
-        outs, lses, scs, alws, lpqs, pds, mds = [], [], [], [], [], [], []
+        outs, lses, scs, alws, lpqs, pds, mds, las = [], [], [], [], [], [], [], []
         p_mode = 0 if v_dtype == "fp8" else (2 if dtype == "bf16" else 1)
         for h in range(hq):
             hk = h // grp
@@ -281,6 +282,7 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
             sd = np.zeros((len(r), nk), dtype=np.int32) if want_scores else None
             al = np.zeros((len(r), dp), dtype=np.float64)
             lpq = np.zeros(len(r), dtype=np.float64)
+            la = np.zeros(len(r), dtype=np.float64)
             pd = np.zeros((len(r), nk), dtype=np.float64) if want_p else None
             md = np.zeros((len(r), nk), dtype=np.float32) if want_p else None
             vsc = vss[hk] if v_dtype == "fp8" else None
@@ -288,16 +290,16 @@ def reference_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dtype: str
                                     _p(np.ascontiguousarray(vvals[hk], dtype=np.float32)), _p(vsc),
                                     _p(vms[hk] if smooth_v else None), _p(kms[hk] if smooth_k else None),
                                     sm32, int(causal), 0, bk, p_mode, band_f, band_x, len(r), _p(r), _p(o), _p(ls),
-                                    _p(sd), _p(al), _p(lpq), _p(pd), _p(md))
+                                    _p(sd), _p(al), _p(lpq), _p(pd), _p(md), _p(la))
             if rc != 0:
                 raise RuntimeError(f"oracle_attn_rows failed ({rc})")
-            outs.append(o[:, :d]); lses.append(ls); alws.append(al[:, :d]); lpqs.append(lpq)
+            outs.append(o[:, :d]); lses.append(ls); alws.append(al[:, :d]); lpqs.append(lpq); las.append(la)
             if want_scores:
                 scs.append(sd)
             if want_p:
                 pds.append(pd); mds.append(md)
         res["out"].append(np.stack(outs)); res["lse"].append(np.stack(lses)); res["allow"].append(np.stack(alws))
-        res["lse_pq"].append(np.stack(lpqs))
+        res["lse_pq"].append(np.stack(lpqs)); res["lse_allow"].append(np.stack(las))
         if want_scores:
             res["scores"].append(np.stack(scs))
         if want_p:
@@ -391,9 +393,14 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
 
     Returns per sequence b: out[b] (Hq, nrows, d) fp64 merged output before
     its final rounding, lse[b] (Hq, nrows), allow[b] (Hq, nrows, d): the
-    per-range flip allowances plus one output ulp of each rounded range
-    output, weighted as in the merge; parts_scale[b] (Hq, nrows): the largest
-    |range output| of the row; rows[b]."""
+    per-range rounding allowances plus one output ulp of each rounded range
+    output, weighted as in the merge, plus what the ranges' LSE allowances
+    can move the merge weights (a change of at most e of every L_s moves the
+    normalised weights by factors within e^(+-2e)); lse_allow[b]
+    (Hq, nrows): the largest LSE allowance of the row's ranges (the merged
+    log-sum-exp moves by at most the largest change of its terms);
+    parts_scale[b] (Hq, nrows): the largest |range output| of the row;
+    rows[b]."""
     d = q.shape[-1]
     dp = padded_head_dim(d)
     if sm_scale is None:
@@ -405,7 +412,7 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
     p_mode = 0 if v_dtype == "fp8" else (2 if dtype == "bf16" else 1)
     mbits, emin = (7, -126) if dtype == "bf16" else (10, -14)
     L = lib()
-    res = {"out": [], "lse": [], "allow": [], "parts_scale": [], "rows": []}
+    res = {"out": [], "lse": [], "allow": [], "lse_allow": [], "parts_scale": [], "rows": []}
     for b in range(len(qz["q8"])):
         q8, qs = qz["q8"][b], qz["q_scale"][b]
         k8, ks, km = qz["k8"][b], qz["k_scale"][b], qz["k_mean"][b]
@@ -417,17 +424,18 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
         grp = hq // hkv
         r = np.arange(nq, dtype=np.int32) if rows is None else np.ascontiguousarray(rows(b, nq), dtype=np.int32)
         res["rows"].append(r)
-        outs, lses, alws, scs = [], [], [], []
+        outs, lses, alws, scs, las = [], [], [], [], []
         for h in range(hq):
             hk = h // grp
             qs_row = np.ascontiguousarray(np.repeat(qs[h], gq)[:nq], dtype=np.float32)
             ks_key = np.repeat(ks[hk], gk)[:nk]
             vval = e4m3_decode(v8[hk]) if v_dtype == "fp8" else qz["v16"][b][hk]
-            po, pl, pa = [], [], []
+            po, pl, pa, pla = [], [], [], []
             for a0, a1 in splitkv_ranges(nk, n_splits):
                 o = np.zeros((len(r), dp), dtype=np.float64)
                 ls = np.zeros(len(r), dtype=np.float64)
                 al = np.zeros((len(r), dp), dtype=np.float64)
+                la = np.zeros(len(r), dtype=np.float64)
                 rc = L.oracle_attn_rows(nq, a1 - a0, dp, _p(q8[h]), _p(qs_row),
                                         _p(np.ascontiguousarray(k8[hk][a0:a1])),
                                         _p(np.ascontiguousarray(ks_key[a0:a1], dtype=np.float32)),
@@ -435,22 +443,26 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
                                         _p(vs[hk] if v_dtype == "fp8" else None),
                                         _p(vm[hk] if smooth_v else None), _p(km[hk] if smooth_k else None),
                                         sm32, 0, 0, DEFAULT_BK, p_mode, float(exp_band[0]), float(exp_band[1]),
-                                        len(r), _p(r), _p(o), _p(ls), None, _p(al), None, None, None)
+                                        len(r), _p(r), _p(o), _p(ls), None, _p(al), None, None, None, _p(la))
                 if rc != 0:
                     raise RuntimeError(f"oracle_attn_rows failed ({rc})")
                 # the range's output, rounded to the output dtype as it is stored
                 po.append(round_half(o[:, :d].astype(np.float32), dtype).astype(np.float64))
                 pl.append(ls)
+                pla.append(la)
                 a = np.maximum(np.abs(o[:, :d]), 2.0 ** emin)
                 pa.append(al[:, :d] + np.exp2(np.floor(np.log2(a)) - mbits))
-            po, pl, pa = np.stack(po), np.stack(pl), np.stack(pa)
+            po, pl, pa, pla = np.stack(po), np.stack(pl), np.stack(pa), np.stack(pla)
             mo, ml = merge_states(po, pl)
             m = pl.max(axis=0)
             w = np.exp(pl - np.where(np.isneginf(m), 0.0, m)[None, :])
             w = w / np.maximum(w.sum(axis=0), 1e-300)[None, :]
-            outs.append(mo); lses.append(ml)
-            alws.append(np.einsum("sr,srd->rd", w, pa))
+            eps = pla.max(axis=0)
+            spread = np.einsum("sr,srd->rd", w, np.abs(po - mo[None]))
+            outs.append(mo); lses.append(ml); las.append(eps)
+            alws.append(np.einsum("sr,srd->rd", w, pa) + np.expm1(2.0 * eps)[:, None] * spread)
             scs.append(np.abs(po).max(axis=(0, 2)))
         res["out"].append(np.stack(outs)); res["lse"].append(np.stack(lses))
         res["allow"].append(np.stack(alws)); res["parts_scale"].append(np.stack(scs))
+        res["lse_allow"].append(np.stack(las))
     return res

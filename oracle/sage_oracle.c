@@ -231,8 +231,10 @@ void oracle_quant_v_fp8(const float* v, int n, int dp, uint8_t* codes, float* sc
  * sum_j dP_j (V_jc - out_c) / (l + sum_j dP_j), so for every such key the
  * width of the operand interval is recorded, and `allow` (if not NULL)
  * receives  sum_j |dP_j| |V_jc - out_c| / (l - sum_j |dP_j|)  in output units
- * (each dP_j carried to the final reference maximum like acc).  With
- * band_f = band_x = 0 the allowance is 0.
+ * (each dP_j carried to the final reference maximum like acc), and
+ * `lse_allow` (if not NULL) receives -ln(1 - sum_j |dP_j| / l), the most
+ * those changes can move ln l and so the log-sum-exp.  With
+ * band_f = band_x = 0 both allowances are 0.
  *
  * q8: nq x dp; qscale: nq (per row, expanded from its group); k8: nk x dp;
  * kscale: nk (per key, expanded); vval: nk x dp values of the PV operand
@@ -245,7 +247,8 @@ void oracle_quant_v_fp8(const float* v, int n, int dp, uint8_t* codes, float* sc
  * operand format: |ln(sum of rounded P) - ln(sum of unrounded P)|;
  * pdump: nrows x nk or NULL, the operand value P_ij of each key at its own
  * tile's reference maximum (0 for keys the row does not see); mdump:
- * nrows x nk or NULL, that reference maximum m' (-inf for unseen keys).       */
+ * nrows x nk or NULL, that reference maximum m' (-inf for unseen keys);
+ * lse_allow: nrows or NULL (see above).                                       */
 static double p_operand(double p, int p_mode) {
     if (p_mode == 0) return e4m3_value(p < E4M3_MAX ? p : E4M3_MAX);
     return fmt_rne(p, p_mode == 2 ? 7 : 10, p_mode == 2 ? -126 : -14);
@@ -259,7 +262,7 @@ int oracle_attn_rows(int nq, int nk, int dp,
                      int bk, int p_mode, double band_f, double band_x,
                      int nrows, const int32_t* rows,
                      double* out, double* lse, int32_t* sdump, double* allow, double* lse_pq,
-                     double* pdump, float* mdump) {
+                     double* pdump, float* mdump, double* lse_allow) {
     if (bk <= 0 || dp <= 0 || nk <= 0) return -1;
     const float LOG2E = 1.4426950408889634f;
     const double pscale = p_mode == 0 ? E4M3_MAX : 1.0;
@@ -359,6 +362,7 @@ int oracle_attn_rows(int nq, int nk, int dp,
             lse[ri] = ((double)m - log2(pscale) + log2(l)) * M_LN2 + corr;
         }
         if (lse_pq) lse_pq[ri] = l > 0.0 ? fabs(log(l) - log(lu)) : 0.0;
+        if (lse_allow) lse_allow[ri] = sum_dp <= 0.0 ? 0.0 : (sum_dp < l ? -log1p(-sum_dp / l) : INFINITY);
         free(S); free(s); free(acc); free(fj); free(fd); free(fm);
     }
     return err;

@@ -35,8 +35,10 @@
 //    cores run QK^T of tile t+1 and P.V of tile t-1; the scheduler is told to
 //    interleave the two streams instruction by instruction, which is what
 //    lets one wavefront keep the MFMA pipe and the VALU busy together.
-//  * O^T (fp32) is rescaled only when some row of the wavefront raised its
-//    running maximum (lazy rescaling with threshold kTau).
+//  * the running maximum follows the plain online-softmax update: a row's
+//    reference maximum becomes max(m, tile maximum) and O^T (fp32) and the
+//    row sums are rescaled by 2^(m - m') whenever some row of the wavefront
+//    moved it.
 #include <type_traits>
 
 #include "sage_device.h"
@@ -46,10 +48,10 @@ namespace sage {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2_448 = 8.807354922057604f;   // log2 of the FP8 P scale (448)
-// Lazy rescaling: a row's reference maximum only moves when a tile's maximum
-// exceeds it by more than kTau (log2 units), so P can reach 2^kTau and its
-// FP8 scale is 448 / 2^kTau.  Most tiles then skip the O rescale.
-constexpr int kTau = 3;
+// log2 of P's static scale: 448 puts p = 2^(s - m') <= 1 at the top of the FP8
+// range; the fp16/bf16 operand takes p itself
+template <int PV>
+constexpr float kPLog2Scale = PV == 0 ? kLog2_448 : 0.f;
 
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
@@ -472,10 +474,11 @@ __device__ __forceinline__ void pv_all(const VA<DP, PV>& va, const PHalf<PV>& P,
 //   f = (q_scale * sm_scale * log2 e) * k_scale per key-scale group g
 //   (g = 2*kb + i/8 covers keys 16g .. 16g+15; a 64-key group fills all four),
 //   tile max  mt = max over keys of fl32(S * f),
-//   raise     iff mt > fl32(m + kTau)  (then m = mt),
+//   raise     iff mt > m  (then m = mt: m' = max(m, mt)),
 //   P         = 2^x,  x = fl32((B + S) * f + fl32(nb - B * f)),
-//             nb = log2(P scale) - m,
-// exactly as the oracle orders these roundings.  MASKED hides the keys a
+//             nb = log2(P scale) - m, with B + S the score accumulator
+//             read as a float (its bias B < 2^24, so B + S is exact).
+// MASKED hides the keys a
 // row may not see (past the sequence end, or after the row when causal).
 // Returns, per lane, whether its row raised its maximum; m_prev then holds
 // the maximum before this tile.  (Used by the masked tiles; the pipelined
@@ -484,7 +487,7 @@ template <int PV, bool MASKED>
 __device__ __forceinline__ bool softmax_half(const v16i (&S)[2], const float (&ksv)[4], float cq, float& m_ref,
                                              float& m_prev, PHalf<PV>& P, int k0, int Lk, bool causal, int row,
                                              int hh) {
-    constexpr float p_log2_scale = PV == 0 ? kLog2_448 - (float)kTau : 0.f;
+    constexpr float p_log2_scale = kPLog2Scale<PV>;
     bool vis[2][16];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -513,7 +516,7 @@ __device__ __forceinline__ bool softmax_half(const v16i (&S)[2], const float (&k
     }
     smax = swap_half_max(smax);
     m_prev = m_ref;
-    const bool raise = smax > m_ref + (float)kTau;
+    const bool raise = smax > m_ref;
     m_ref = raise ? smax : m_ref;
     // a row that has seen no key keeps m = -inf; its P is 0 below
     const float m_use = MASKED ? (m_ref == -INFINITY ? 0.f : m_ref) : m_ref;
@@ -565,7 +568,7 @@ __device__ __forceinline__ bool softmax_half(const v16i (&S)[2], const float (&k
 // integer maximum equals the maximum of the scaled groups).
 template <int PV, bool KS16 = true>
 struct SoftmaxPieces {
-    static constexpr float p_log2_scale = PV == 0 ? kLog2_448 - (float)kTau : 0.f;
+    static constexpr float p_log2_scale = kPLog2Scale<PV>;
     float f[4], cg[4], smax;
     int mi[4];
     int word[8];                                        // FP8: bytes 0-1 of word w between its two chunks
@@ -594,19 +597,17 @@ struct SoftmaxPieces {
         } else {
             smax = swap_half_max(smax);
             m_prev = m_ref;
-            raise = smax > m_ref + (float)kTau;
+            raise = smax > m_ref;
             m_ref = raise ? smax : m_ref;
             const float nb = p_log2_scale - m_ref;
 #pragma unroll
             for (int g = 0; g < 4; ++g) cg[g] = __builtin_fmaf(-kAccBias, f[g], nb);
         }
     }
-    // The same head split for a loop that computes P speculatively with the
-    // reference maximum it has before the tile: prep() and gmax() need only
-    // the scores, spec() gives the exponent offsets for the current maximum,
-    // decide() the raise decision and the new maximum (same roundings as
-    // head<>()).  A row that does not raise keeps its maximum, so its
-    // speculative P is exact; a wavefront with a raising row redoes P.
+    // The same head split into calls that the 8-wavefront loop places
+    // itself: prep() and gmax() need only the scores, decide() takes the
+    // raise decision and the new maximum, spec() gives the exponent offsets
+    // for a maximum (same roundings as head<>()).
     __device__ __forceinline__ void prep(const float (&ksv)[4], float cq) {
         if constexpr (KS16) {
 #pragma unroll
@@ -640,7 +641,7 @@ struct SoftmaxPieces {
         }
         smax = swap_half_max(smax);
         m_prev = m_ref;
-        raise = smax > m_ref + (float)kTau;
+        raise = smax > m_ref;
         m_ref = raise ? smax : m_ref;
     }
 
@@ -1031,7 +1032,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                 }
         }
         if (a.lse) {
-            constexpr float p_log2_scale = PV == 0 ? kLog2_448 - (float)kTau : 0.f;
+            constexpr float p_log2_scale = kPLog2Scale<PV>;
             float part = 0.f;
             if (a.kmean) {
                 const float* km = a.kmean + khead * DP;
@@ -1238,12 +1239,13 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     constexpr int NDMA = LPT;
     // Step t is two regions:
     //   H(t): QK^T of tile t, then P.V of tile t-1 and the row sums, with the
-    //         group maxima of tile t between the P.V MFMAs, the copy of tile
-    //         t+AHEAD, and the K and V^T fragments of the next step
+    //         group maxima of tile t and the raise decision (the new
+    //         reference maximum of every row) between the P.V MFMAs, the copy
+    //         of tile t+AHEAD, and the K and V^T fragments of the next step
     //         (matrix-core work);
-    //   E(t): P of tile t, computed with the reference maximum from before
-    //         the tile while the raise decision completes; if a row raises,
-    //         O is rescaled and P recomputed (VALU work).
+    //   E(t): P of tile t against the new maximum; then, if some row of the
+    //         wavefront moved its maximum, O and the row sums (complete up to
+    //         tile t-1 by now) are rescaled (VALU work).
     // One workgroup barrier per step: wavefronts 0-3 pass barrier t right
     // after their H(t), wavefronts 4-7 right before theirs, so between
     // barriers t and t+1 the leading group runs E(t) then H(t+1) while the
@@ -1300,9 +1302,11 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
                         for (int kb = 0; kb < 2; ++kb)
                             kf[kb][cb] = *(lds_v4i*)(kp[cb] + UN * C::KT_BYTES + kb * 32 * DP);
                 }
-                // group maxima of tile t, one or two per P.V MFMA
+                // group maxima of tile t, one or two per P.V MFMA, then the
+                // raise decision
                 if constexpr (k == NQK + 1) { sp.gmax(S[0], 0); sp.gmax(S[0], 1); }
                 if constexpr (k == NQK + 2) { sp.gmax(S[1], 2); sp.gmax(S[1], 3); }
+                if constexpr (k == NH - 1) sp.decide(m_ref, m_prev);
                 if constexpr (k == NH - 1) {            // V of tile t (va is free once the last P.V MFMA issued)
                     const v4f k4 = *(lds_v4f*)(sp_slot + UN * C::SC_BYTES);
 #pragma unroll
@@ -1324,17 +1328,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     auto regionE = [&](SoftmaxPieces<PV, KS16>& sp) {
         if (!live) return;
         sp.spec(m_ref);
-        static_for<0, SoftmaxPieces<PV, KS16>::NPIECE>([&](auto ec) {
-            constexpr int e = decltype(ec)::value;
-            sp.template piece<e>(S, P);
-            if constexpr (e == 1) sp.decide(m_ref, m_prev);
-        });
-        if (__any(sp.raise)) {                          // rare: some row raised its maximum
-            rescale_half<DP>(m_ref, m_prev, o, ls);
-            sp.spec(m_ref);
-            static_for<0, SoftmaxPieces<PV, KS16>::NPIECE>([&](auto ec) { sp.template piece<decltype(ec)::value>(S, P); });
-        }
+        static_for<0, SoftmaxPieces<PV, KS16>::NPIECE>([&](auto ec) { sp.template piece<decltype(ec)::value>(S, P); });
         keep_here<PV>(P);
+        if (__any(sp.raise)) rescale_half<DP>(m_ref, m_prev, o, ls);   // some row moved its maximum
     };
     // both groups pass one barrier per step (see above); a last barrier
     // after the loop orders every wavefront's final waits before the tail
@@ -1418,7 +1414,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
             }
     }
     if (a.lse) {
-        constexpr float p_log2_scale = kLog2_448 - (float)kTau;
+        constexpr float p_log2_scale = kPLog2Scale<0>;
         float part = 0.f;
         if (a.kmean) {
             const float* km = a.kmean + khead * DP;

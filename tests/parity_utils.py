@@ -22,10 +22,12 @@ one integer score unit in log2 units plus a relative term.  The oracle's
 allowance bounds how far operands formed anywhere in that band can move each
 output (it is zero for elements whose P operands cannot change).
 
-LSE: within 1e-3 of the oracle's; against exact fp64 attention within
-max_j |s_hat_ij - s_ij| + 1e-3, where s_hat are the dequantized (unsmoothed)
-scores and s the exact ones -- log-sum-exp moves by at most the largest
-change of its arguments.
+LSE: within 1e-3 + the oracle's LSE allowance (what P operands formed within
+the exponent band can move ln l: -ln(1 - sum |dP| / l), which matters on rows
+with few keys) of the oracle's; against exact fp64 attention within
+max_j |s_hat_ij - s_ij| + 1e-3 + that allowance, where s_hat are the
+dequantized (unsmoothed) scores and s the exact ones -- log-sum-exp moves by
+at most the largest change of its arguments.
 """
 from __future__ import annotations
 
@@ -254,11 +256,15 @@ class Case:
                 es.append(self.exact["out"][b].ravel())
             if lse:
                 gl = self.gpu_lse_rows(b, rows)
-                assert np.max(np.abs(gl - self.ref["lse"][b])) <= LSE_TOL_EMU
+                lerr = np.abs(gl - self.ref["lse"][b])
+                ltol = LSE_TOL_EMU + self.ref["lse_allow"][b]
+                assert np.all(lerr <= ltol), (f"seq {b}: lse off by {lerr.max():.3g} at "
+                                              f"{np.unravel_index(lerr.argmax(), lerr.shape)}")
                 if self.exact is not None and self.w.smooth_k:
                     # score error of the INT8 Q/K, plus what rounding P to its
                     # operand format moved the row sum, plus the emulation slack
-                    bound = self.lse_exact_bound(b, rows, sm) + self.ref["lse_pq"][b] + LSE_TOL_EMU + 1e-4
+                    bound = (self.lse_exact_bound(b, rows, sm) + self.ref["lse_pq"][b] + LSE_TOL_EMU + 1e-4 +
+                             self.ref["lse_allow"][b])
                     assert np.all(np.abs(gl - self.exact["lse"][b]) <= bound)
         g, r = np.concatenate(gs), np.concatenate(rs)
         c_emu = cosine(g, r)

@@ -63,7 +63,7 @@ def test_splitkv_matches_oracle(case):
         assert (diff <= tol).all(), f"batch {b}: {(diff > tol).sum()} outputs off, worst {diff.max():.3g}"
         assert cosine(got[b], r) >= COS_EMU
         if want_lse:
-            assert np.abs(lse[b].cpu().numpy() - ref["lse"][b]).max() <= 2e-3
+            assert np.all(np.abs(lse[b].cpu().numpy() - ref["lse"][b]) <= 2e-3 + ref["lse_allow"][b])
 
 
 def test_one_range_is_bit_identical_to_attn_fwd():

@@ -121,7 +121,8 @@ def test_fp16_path_matches_exact_on_dequantized(gran, causal):
 LOG2E32 = np.float32(1.4426950408889634)
 
 
-def _closed_form(r, b, h, hk, gran, sm, causal, bk=64, v_dtype="fp8", dtype="fp16", pp_factor=None):
+def _closed_form(r, b, h, hk, gran, sm, causal, bk=64, v_dtype="fp8", dtype="fp16", pp_factor=None,
+                 want_l=False):
     """The FlashAttention-style online softmax written in closed form instead
     of as a loop: with m_t the running maximum after key tile t (a cumulative
     maximum of the tile maxima), every key j of tile t gets the operand
@@ -131,7 +132,8 @@ def _closed_form(r, b, h, hk, gran, sm, causal, bk=64, v_dtype="fp8", dtype="fp1
     arithmetic (one rounding per operation), Q is torch's float8_e4m3fn or
     fp16/bf16 cast.  pp_factor (nq, nk), if given, multiplies the value
     before the operand rounding (an evaluation with a different exponent).
-    Returns P (nq, nk), m_t per key (nq, nk), out (nq, d) in fp64."""
+    Returns P (nq, nk), m_t per key (nq, nk), out (nq, d) in fp64 and, with
+    want_l, also l (nq,), the sum of the weights at the final maximum."""
     gq, gk = oracle.Q_GROUP[gran], oracle.K_GROUP[gran]
     q8 = r["q8"][b][h].astype(np.int64)
     k8 = r["k8"][b][hk].astype(np.int64)
@@ -172,6 +174,8 @@ def _closed_form(r, b, h, hk, gran, sm, causal, bk=64, v_dtype="fp8", dtype="fp1
     w = P * np.exp2(m_key.astype(np.float64) - mfin)
     w = np.where(vis, w, 0.0)
     out = (w @ vv) / w.sum(axis=1, keepdims=True) * vsc[None, :] + r["v_mean"][b][hk].astype(np.float64)[None, :]
+    if want_l:
+        return P, np.where(vis, m_key, np.float32(-np.inf)), out, w.sum(axis=1)
     return P, np.where(vis, m_key, np.float32(-np.inf)), out
 
 
@@ -277,15 +281,20 @@ def test_allowance_bounds_a_perturbed_evaluation(v_dtype, dtype):
     mref = r["mref"][0][0].astype(np.float64)
     delta = band[0] * c.astype(np.float64)[:, None] * ks.astype(np.float64)[None, :] + \
         band[1] * (np.abs(s.astype(np.float64)) + np.abs(mref) + 8.0)
+    _, _, _, l0 = _closed_form(r, 0, 0, 0, "per_warp", 1 / math.sqrt(d), False, v_dtype=v_dtype, dtype=dtype,
+                               want_l=True)
     moved = 0
     for trial in range(4):
         u = rng.uniform(-1.0, 1.0, size=(nq, nk)) if trial else np.sign(rng.uniform(-1, 1, size=(nq, nk)))
         fac = np.exp2(0.999 * u * delta)
-        P2, _, out2 = _closed_form(r, 0, 0, 0, "per_warp", 1 / math.sqrt(d), False, v_dtype=v_dtype, dtype=dtype,
-                                   pp_factor=fac)
+        P2, _, out2, l2 = _closed_form(r, 0, 0, 0, "per_warp", 1 / math.sqrt(d), False, v_dtype=v_dtype,
+                                       dtype=dtype, pp_factor=fac, want_l=True)
         moved += int((P2 != r["p"][0][0]).sum())
         assert np.all(np.abs(out2 - r["out"][0][0]) <= r["allow"][0][0] + 1e-12)
-    assert moved > 100 and r["allow"][0][0].max() > 0
+        # the log-sum-exp moves with ln l
+        assert np.all(np.abs(np.log(l2) - np.log(l0)) <= r["lse_allow"][0][0] + 1e-12)
+    assert moved > 100 and r["allow"][0][0].max() > 0 and r["lse_allow"][0][0].max() > 0
+    assert np.all(z["lse_allow"][0] == 0.0)
 
 
 def test_fp8_schedule_without_max_updates_equals_single_tile():
