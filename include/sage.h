@@ -20,7 +20,8 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers owned by the caller.  The library
- *   allocates nothing and keeps no state between calls.
+ *   allocates nothing and keeps no state between calls, apart from the static
+ *   scratch array of sage_quant_qkv_noalloc (see there).
  * - Every call is asynchronous on the caller's HIP stream (`stream`, a
  *   hipStream_t; NULL = the legacy default stream) and on the current HIP
  *   device.  Nothing is synchronised on the host.
@@ -172,6 +173,30 @@ int sage_quant_v(const sage_quant_v_params* p, void* stream);
  * overlapping workspaces; nothing is launched then.
  * ------------------------------------------------------------------------- */
 int sage_quant_qkv(const sage_quant_qk_params* qk, const sage_quant_v_params* v, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * sage_quant_qkv_noalloc: sage_quant_qkv for callers that cannot allocate
+ * device memory -- code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same parameters, checks, kernels and
+ * results (bit for bit) as sage_quant_qkv, except that the workspace fields of
+ * both parameter blocks are ignored: the exact-sum partials live in a static
+ * device array of SAGE_QUANT_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on until the process ends.  The call allocates nothing; its
+ * first call on a device looks up that array's device address there.
+ * Limit: the call needs sage_quant_qkv_noalloc_scratch_size(B, Hkv, Nk, d)
+ * bytes of the array (0 for invalid sizes); beyond SAGE_QUANT_SCRATCH_BYTES
+ * it returns SAGE_EINVAL and launches nothing (with the 16 MiB array: about
+ * 500 sequence-heads of K/V at head_dim 128, any length).
+ * Concurrency: every call on one GPU uses the same array, which keeps the last
+ * call's partials (nothing in it needs to start at zero).  Calls whose work
+ * overlaps on one GPU (different streams, or several host threads without
+ * ordering) race on it; order them on one stream.
+ * Errors: as sage_quant_qkv; SAGE_EHIP if the array's address cannot be
+ * obtained.
+ * ------------------------------------------------------------------------- */
+#define SAGE_QUANT_SCRATCH_BYTES ((size_t)16 << 20)
+size_t sage_quant_qkv_noalloc_scratch_size(int B, int Hkv, int Nk, int d);
+int sage_quant_qkv_noalloc(const sage_quant_qk_params* qk, const sage_quant_v_params* v, void* stream);
 
 /* ---------------------------------------------------------------------------
  * sage_attn_fwd: the fused attention forward on quantized operands.

@@ -18,6 +18,7 @@ SAGE_HND, SAGE_NHD = 0, 1
 SAGE_PER_BLOCK, SAGE_PER_WARP, SAGE_PER_THREAD = 0, 1, 2
 SAGE_V_FP8, SAGE_V_FP16 = 0, 1
 SAGE_ACC_FP32, SAGE_ACC_FP16, SAGE_ACC_FP16_FP32, SAGE_ACC_FP32_FP32 = 0, 1, 2, 3
+SAGE_QUANT_SCRATCH_BYTES = 16 << 20
 
 VP = ctypes.c_void_p
 I = ctypes.c_int
@@ -70,7 +71,8 @@ class MergeParams(ctypes.Structure):
     ]
 
 
-EXPORTS = ["sage_quant_qk", "sage_quant_workspace_size", "sage_quant_v", "sage_quant_qkv", "sage_attn_fwd",
+EXPORTS = ["sage_quant_qk", "sage_quant_workspace_size", "sage_quant_v", "sage_quant_qkv",
+           "sage_quant_qkv_noalloc_scratch_size", "sage_quant_qkv_noalloc", "sage_attn_fwd",
            "sage_attn_varlen_fwd", "sage_debug_qk_scores", "sage_merge_states", "sage_attn_splitkv_workspace_size",
            "sage_attn_fwd_splitkv", "sage_last_error", "sage_version"]
 
@@ -96,6 +98,10 @@ def load(path: str = LIB_PATH):
     L.sage_quant_v.restype = I
     L.sage_quant_qkv.argtypes = [ctypes.POINTER(QuantQKParams), ctypes.POINTER(QuantVParams), VP]
     L.sage_quant_qkv.restype = I
+    L.sage_quant_qkv_noalloc.argtypes = [ctypes.POINTER(QuantQKParams), ctypes.POINTER(QuantVParams), VP]
+    L.sage_quant_qkv_noalloc.restype = I
+    L.sage_quant_qkv_noalloc_scratch_size.argtypes = [I, I, I, I]
+    L.sage_quant_qkv_noalloc_scratch_size.restype = SZ
     L.sage_attn_fwd.argtypes = [ctypes.POINTER(AttnParams), VP]
     L.sage_attn_fwd.restype = I
     L.sage_attn_varlen_fwd.argtypes = [ctypes.POINTER(AttnVarlenParams), VP]

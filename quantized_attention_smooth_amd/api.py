@@ -109,7 +109,7 @@ def workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 
 def _quant_qk_params(q: torch.Tensor, k: torch.Tensor, tensor_layout: str, qk_quant_gran: str, smooth_k: bool,
-                     cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, workspace):
+                     cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, workspace, alloc_workspace=True):
     if qk_quant_gran not in _GRAN:
         raise ValueError(f"qk_quant_gran must be one of {sorted(_GRAN)}")
     if q.dtype != k.dtype or q.device != k.device:
@@ -126,7 +126,7 @@ def _quant_qk_params(q: torch.Tensor, k: torch.Tensor, tensor_layout: str, qk_qu
     k8 = torch.empty((gk.B, gk.H, nk_pad, dp), dtype=torch.int8, device=dev)
     ks = torch.empty((gk.B, gk.H, nk_pad // _KG[qk_quant_gran]), dtype=torch.float32, device=dev)
     km = torch.empty((gk.B, gk.H, dp), dtype=torch.float32, device=dev) if smooth_k else None
-    if smooth_k and workspace is None:
+    if smooth_k and workspace is None and alloc_workspace:
         workspace = torch.empty(workspace_bytes(gk.B, gk.H, gk.N, gk.d), dtype=torch.uint8, device=dev)
     p = A.QuantQKParams()
     p.struct_size = ctypes.sizeof(A.QuantQKParams)
@@ -144,7 +144,7 @@ def _quant_qk_params(q: torch.Tensor, k: torch.Tensor, tensor_layout: str, qk_qu
 
 
 def _quant_v_params(v: torch.Tensor, tensor_layout: str, v_dtype: str, smooth_v: bool, cu_seqlens_k, max_seqlen_k,
-                    workspace):
+                    workspace, alloc_workspace=True):
     if v_dtype not in ("fp8", "fp16"):
         raise ValueError("v_dtype must be 'fp8' or 'fp16' (the input's 16-bit type)")
     g = _geometry(v, tensor_layout, cu_seqlens_k, max_seqlen_k)
@@ -155,7 +155,7 @@ def _quant_v_params(v: torch.Tensor, tensor_layout: str, v_dtype: str, smooth_v:
     vt = torch.empty((g.B, g.H, dp, nk_pad), dtype=torch.uint8 if fp8 else v.dtype, device=dev)
     vs = torch.empty((g.B, g.H, dp), dtype=torch.float32, device=dev) if fp8 else None
     vm = torch.empty((g.B, g.H, dp), dtype=torch.float32, device=dev) if smooth_v else None
-    if (fp8 or smooth_v) and workspace is None:
+    if (fp8 or smooth_v) and workspace is None and alloc_workspace:
         workspace = torch.empty(workspace_bytes(g.B, g.H, g.N, g.d), dtype=torch.uint8, device=dev)
     p = A.QuantVParams()
     p.struct_size = ctypes.sizeof(A.QuantVParams)
@@ -207,6 +207,26 @@ def sage_quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, tensor_
                                   max_seqlen_q, max_seqlen_k, workspace_k)
     pv, rv, _ = _quant_v_params(v, tensor_layout, v_dtype, smooth_v, cu_seqlens_k, max_seqlen_k, workspace_v)
     A.check(L.sage_quant_qkv(ctypes.byref(pk), ctypes.byref(pv), _stream()))
+    return rqk, rv
+
+
+def sage_quant_qkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, tensor_layout: str = "HND",
+                           qk_quant_gran: str = "per_thread", smooth_k: bool = True, v_dtype: str = "fp8",
+                           smooth_v: bool = False, cu_seqlens_q: Optional[torch.Tensor] = None,
+                           cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
+                           max_seqlen_k: Optional[int] = None):
+    """sage_quant_qkv with the statistics partials in the library's static
+    device array instead of a workspace (for callers that cannot allocate;
+    calls that overlap on one GPU race on that array).  The outputs are
+    allocated here, as for the other calls."""
+    L = A.load()
+    if v.dtype != k.dtype or v.device != k.device:
+        raise ValueError("k and v must share dtype and device")
+    pk, rqk, _ = _quant_qk_params(q, k, tensor_layout, qk_quant_gran, smooth_k, cu_seqlens_q, cu_seqlens_k,
+                                  max_seqlen_q, max_seqlen_k, None, alloc_workspace=False)
+    pv, rv, _ = _quant_v_params(v, tensor_layout, v_dtype, smooth_v, cu_seqlens_k, max_seqlen_k, None,
+                                alloc_workspace=False)
+    A.check(L.sage_quant_qkv_noalloc(ctypes.byref(pk), ctypes.byref(pv), _stream()))
     return rqk, rv
 
 

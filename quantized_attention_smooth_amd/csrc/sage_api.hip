@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "sage.h"
@@ -102,18 +103,38 @@ struct QKPrep {
     sage::QuantRowsArgs qa, ka;
     sage::StatsArgs st;
     bool smooth, bf16, vec;
+    WsLayout wl;
     const void* ws;
-    size_t ws_used;
+    size_t ws_used;                     // bytes of workspace the call uses (0: none)
 };
 struct VPrep {
     sage::QuantVArgs va;
     sage::StatsArgs st;
     bool need_stats, smooth, bf16, fp8, vec;
+    WsLayout wl;
     const void* ws;
     size_t ws_used;
 };
 
-int prepare_qk(const sage_quant_qk_params* p, QKPrep& o) {
+// Point the statistics partials of a prepared call at workspace `base`
+// (NULL: no workspace bound yet).
+void bind_qk_ws(QKPrep& o, uint8_t* base) {
+    o.ws = o.ws_used ? base : nullptr;
+    if (o.smooth) o.st.part_sum = base ? base + o.wl.sum_off : nullptr;
+}
+void bind_v_ws(VPrep& o, uint8_t* base) {
+    o.ws = o.ws_used ? base : nullptr;
+    if (o.need_stats) {
+        o.st.part_sum = base ? base + o.wl.sum_off : nullptr;
+        o.st.part_min = base ? reinterpret_cast<float*>(base + o.wl.min_off) : nullptr;
+        o.st.part_max = base ? reinterpret_cast<float*>(base + o.wl.max_off) : nullptr;
+    }
+}
+
+// Validate a Q/K quantize call and build its launch arguments.  With
+// own_ws = false the caller's workspace fields are ignored (and not checked);
+// the partials are bound later with bind_qk_ws.
+int prepare_qk(const sage_quant_qk_params* p, QKPrep& o, bool own_ws = true) {
     if (!p) return fail(SAGE_EINVAL, "params is NULL");
     if (p->struct_size < sizeof(sage_quant_qk_params)) return fail(SAGE_EINVAL, "struct_size too small");
     if (!valid_dtype(p->dtype)) return fail(SAGE_EINVAL, "unknown dtype %d", p->dtype);
@@ -132,7 +153,7 @@ int prepare_qk(const sage_quant_qk_params* p, QKPrep& o) {
         p->q_stride_b < 0 || p->k_stride_b < 0)
         return fail(SAGE_EINVAL, "negative or zero token stride");
     const WsLayout ws = ws_layout(p->B, p->Hkv, p->Nk, p->d);
-    if (p->smooth_k) {
+    if (p->smooth_k && own_ws) {
         if (!p->workspace || !aligned(p->workspace, 16)) return fail(SAGE_EINVAL, "workspace NULL or misaligned");
         if (p->workspace_bytes < ws.total)
             return fail(SAGE_EINVAL, "workspace too small: %zu < %zu bytes", p->workspace_bytes, ws.total);
@@ -140,15 +161,11 @@ int prepare_qk(const sage_quant_qk_params* p, QKPrep& o) {
     const bool bf16 = p->dtype == SAGE_BF16;
     const int dp = dp_of(p->d);
     const int nq_pad = (int)round_up(p->Nq, sage::kPad), nk_pad = (int)round_up(p->Nk, sage::kPad);
-    uint8_t* wsb = reinterpret_cast<uint8_t*>(p->workspace);
     sage::StatsArgs st{};
     st.x = p->k; st.sb = p->k_stride_b; st.sh = p->k_stride_h; st.sn = p->k_stride_n;
     st.cu = p->cu_seqlens_k; st.B = p->B; st.H = p->Hkv; st.N = p->Nk; st.d = p->d; st.dp = dp;
     st.chunks = ws.chunks; st.chunk_len = ws.chunk_len; st.want_minmax = 0;
-    if (p->smooth_k) {
-        st.part_sum = wsb + ws.sum_off;
-        st.out_mean = p->k_mean;
-    }
+    if (p->smooth_k) st.out_mean = p->k_mean;
     auto vec_ok = [&](const void* x, int64_t sb, int64_t sh, int64_t sn) {
         return aligned(x, 16) && p->d % 8 == 0 && sb % 8 == 0 && sh % 8 == 0 && sn % 8 == 0;
     };
@@ -168,12 +185,14 @@ int prepare_qk(const sage_quant_qk_params* p, QKPrep& o) {
     o.smooth = p->smooth_k != 0;
     o.bf16 = bf16;
     o.vec = vec;
-    o.ws = p->smooth_k ? p->workspace : nullptr;
+    o.wl = ws;
     o.ws_used = p->smooth_k ? ws.total : 0;
+    bind_qk_ws(o, own_ws ? reinterpret_cast<uint8_t*>(p->workspace) : nullptr);
     return 0;
 }
 
-int prepare_v(const sage_quant_v_params* p, VPrep& o) {
+// As prepare_qk, for a V quantize call.
+int prepare_v(const sage_quant_v_params* p, VPrep& o, bool own_ws = true) {
     if (!p) return fail(SAGE_EINVAL, "params is NULL");
     if (p->struct_size < sizeof(sage_quant_v_params)) return fail(SAGE_EINVAL, "struct_size too small");
     if (!valid_dtype(p->dtype)) return fail(SAGE_EINVAL, "unknown dtype %d", p->dtype);
@@ -191,7 +210,7 @@ int prepare_v(const sage_quant_v_params* p, VPrep& o) {
         return fail(SAGE_EINVAL, "negative or zero token stride");
     const bool need_stats = fp8 || p->smooth_v;
     const WsLayout ws = ws_layout(p->B, p->Hkv, p->Nk, p->d);
-    if (need_stats) {
+    if (need_stats && own_ws) {
         if (!p->workspace || !aligned(p->workspace, 16)) return fail(SAGE_EINVAL, "workspace NULL or misaligned");
         if (p->workspace_bytes < ws.total)
             return fail(SAGE_EINVAL, "workspace too small: %zu < %zu bytes", p->workspace_bytes, ws.total);
@@ -199,15 +218,11 @@ int prepare_v(const sage_quant_v_params* p, VPrep& o) {
     const bool bf16 = p->dtype == SAGE_BF16;
     const int dp = dp_of(p->d);
     const int nk_pad = (int)round_up(p->Nk, sage::kPad);
-    uint8_t* wsb = reinterpret_cast<uint8_t*>(p->workspace);
     sage::StatsArgs st{};
     st.x = p->v; st.sb = p->v_stride_b; st.sh = p->v_stride_h; st.sn = p->v_stride_n;
     st.cu = p->cu_seqlens_k; st.B = p->B; st.H = p->Hkv; st.N = p->Nk; st.d = p->d; st.dp = dp;
     st.chunks = ws.chunks; st.chunk_len = ws.chunk_len; st.want_minmax = fp8 ? 1 : 0;
     if (need_stats) {
-        st.part_sum = wsb + ws.sum_off;
-        st.part_min = reinterpret_cast<float*>(wsb + ws.min_off);
-        st.part_max = reinterpret_cast<float*>(wsb + ws.max_off);
         st.smooth = p->smooth_v ? 1 : 0;
         st.out_mean = p->smooth_v ? p->v_mean : nullptr;
         st.out_scale = fp8 ? p->v_scale : nullptr;
@@ -224,9 +239,18 @@ int prepare_v(const sage_quant_v_params* p, VPrep& o) {
     o.bf16 = bf16;
     o.fp8 = fp8;
     o.vec = vec;
-    o.ws = need_stats ? p->workspace : nullptr;
+    o.wl = ws;
     o.ws_used = need_stats ? ws.total : 0;
+    bind_v_ws(o, own_ws ? reinterpret_cast<uint8_t*>(p->workspace) : nullptr);
     return 0;
+}
+
+// Both parameter blocks of a fused call must describe the same K/V geometry.
+int check_qkv_pair(const sage_quant_qk_params* qk, const sage_quant_v_params* v) {
+    if (qk->dtype != v->dtype || qk->B != v->B || qk->Hkv != v->Hkv || qk->Nk != v->Nk || qk->d != v->d ||
+        qk->cu_seqlens_k != v->cu_seqlens_k)
+        return fail(SAGE_EINVAL, "K and V must share dtype, B, Hkv, Nk, head_dim and cu_seqlens_k");
+    return SAGE_OK;
 }
 }  // namespace
 
@@ -254,9 +278,7 @@ int sage_quant_qkv(const sage_quant_qk_params* qk, const sage_quant_v_params* v,
     VPrep b;
     if (int r = prepare_qk(qk, a)) return r;
     if (int r = prepare_v(v, b)) return r;
-    if (qk->dtype != v->dtype || qk->B != v->B || qk->Hkv != v->Hkv || qk->Nk != v->Nk || qk->d != v->d ||
-        qk->cu_seqlens_k != v->cu_seqlens_k)
-        return fail(SAGE_EINVAL, "K and V must share dtype, B, Hkv, Nk, head_dim and cu_seqlens_k");
+    if (int r = check_qkv_pair(qk, v)) return r;
     if (a.ws_used && b.ws_used) {
         const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.ws), b0 = reinterpret_cast<uintptr_t>(b.ws);
         if (a0 < b0 + b.ws_used && b0 < a0 + a.ws_used)
@@ -266,6 +288,76 @@ int sage_quant_qkv(const sage_quant_qk_params* qk, const sage_quant_v_params* v,
     if (int r = hip_status(sage::launch_quant_qkv(a.qa, a.ka, a.st, a.smooth, b.va, b.st, b.need_stats, a.bf16, b.fp8,
                                                   a.vec && b.vec, s),
                            "Q/K/V quantize launch"))
+        return r;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// The fused quantize call for callers that cannot allocate device memory.  Its
+// statistics partials live in `scratch`, a file-scope device array that every
+// GPU the library runs on holds for the life of the process.  In host code
+// `scratch` names a host-side stand-in, not the device array: its device
+// address comes from hipGetSymbolAddress, looked up once per device with that
+// device current, and only that address is passed to kernels.
+namespace {
+constexpr size_t kScratchBytes = size_t(16) << 20;       // SAGE_QUANT_SCRATCH_BYTES in sage.h
+static_assert(kScratchBytes == SAGE_QUANT_SCRATCH_BYTES, "scratch size and its public constant differ");
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_dev[kMaxDevices];                      // device address of `scratch`, per device
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+// Device address of `scratch` on the current device (looked up on the first
+// call there).
+int scratch_address(uint8_t** out) {
+    int dev = -1;
+    if (int r = hip_status(hipGetDevice(&dev), "hipGetDevice")) return r;
+    if (dev < 0 || dev >= kMaxDevices) return fail(SAGE_EHIP, "device id %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* ptr = nullptr;
+        if (int r = hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"))
+            return r;
+        if (!ptr || !aligned(ptr, 256)) return fail(SAGE_EHIP, "scratch address %p unusable", ptr);
+        g_scratch_dev[dev] = static_cast<uint8_t*>(ptr);
+    }
+    *out = g_scratch_dev[dev];
+    return SAGE_OK;
+}
+}  // namespace
+
+size_t sage_quant_qkv_noalloc_scratch_size(int B, int Hkv, int Nk, int d) {
+    if (B < 1 || Hkv < 1 || Nk < 1 || d < 1 || d > 128) return 0;
+    const size_t one = ws_layout(B, Hkv, Nk, d).total;  // a multiple of 256
+    return 2 * one;
+}
+
+int sage_quant_qkv_noalloc(const sage_quant_qk_params* qk, const sage_quant_v_params* v, void* stream) {
+    QKPrep a;
+    VPrep b;
+    if (int r = prepare_qk(qk, a, false)) return r;
+    if (int r = prepare_v(v, b, false)) return r;
+    if (int r = check_qkv_pair(qk, v)) return r;
+    const size_t koff = 0, voff = a.ws_used;            // K partials, then V partials (256-byte multiples)
+    const size_t need = a.ws_used + b.ws_used;
+    if (need > kScratchBytes)
+        return fail(SAGE_EINVAL,
+                    "problem too large for the no-alloc call: its statistics need %zu bytes, the static scratch "
+                    "holds %zu (use sage_quant_qkv with a workspace)",
+                    need, kScratchBytes);
+    uint8_t* base = nullptr;
+    if (need) {
+        if (int r = scratch_address(&base)) return r;
+    }
+    bind_qk_ws(a, base ? base + koff : nullptr);
+    bind_v_ws(b, base ? base + voff : nullptr);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (int r = hip_status(sage::launch_quant_qkv(a.qa, a.ka, a.st, a.smooth, b.va, b.st, b.need_stats, a.bf16, b.fp8,
+                                                  a.vec && b.vec, s),
+                           "Q/K/V quantize launch (no-alloc)"))
         return r;
     return ok();
 }

@@ -330,3 +330,45 @@ def test_splitkv_workspace_size(lib):
     rows = 4 * 2 * 3 * 10
     want = -(-(rows * 64 * 2) // 256) * 256 + -(-(rows * 4) // 256) * 256
     assert lib.sage_attn_splitkv_workspace_size(2, 3, 10, 1000, 64, 7) == want
+
+
+# ---------------------------------------------------------------- the no-alloc quantize call (host checks)
+def _pair_valid(B=2, Hkv=2, Nk=300, d=128):
+    qk, v = _qk_valid(), _v_valid()
+    qk.dtype = v.dtype = A.SAGE_BF16
+    qk.B = v.B = B
+    qk.Hkv = v.Hkv = Hkv
+    qk.Hq = 2 * Hkv
+    qk.Nk = v.Nk = Nk
+    qk.d = v.d = d
+    qk.workspace, qk.workspace_bytes = None, 0           # ignored by the no-alloc call
+    v.workspace, v.workspace_bytes = None, 0
+    return qk, v
+
+
+def test_noalloc_scratch_size(lib):
+    for B, H, N, d in ((1, 2, 300, 64), (2, 8, 4096, 128), (1, 48, 17550, 64), (4, 8, 32768, 128)):
+        assert lib.sage_quant_qkv_noalloc_scratch_size(B, H, N, d) == 2 * lib.sage_quant_workspace_size(B, H, N, d)
+    assert lib.sage_quant_qkv_noalloc_scratch_size(0, 2, 300, 64) == 0
+    assert lib.sage_quant_qkv_noalloc_scratch_size(1, 2, 300, 129) == 0
+    # the workloads of the benchmark fit the static array
+    assert lib.sage_quant_qkv_noalloc_scratch_size(1, 48, 17550, 64) <= A.SAGE_QUANT_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_too_large_before_any_hip_call(lib):
+    """Beyond the static array the call fails with SAGE_EINVAL on the host
+    (no GPU is touched: this runs without one)."""
+    qk, v = _pair_valid(B=64, Hkv=32, Nk=100000, d=128)
+    assert lib.sage_quant_qkv_noalloc_scratch_size(64, 32, 100000, 128) > A.SAGE_QUANT_SCRATCH_BYTES
+    assert lib.sage_quant_qkv_noalloc(ctypes.byref(qk), ctypes.byref(v), None) == A.SAGE_EINVAL
+    assert b"too large for the no-alloc call" in lib.sage_last_error()
+
+
+@pytest.mark.parametrize("case", ["dtype", "head_dim 129", "Hq not multiple of Hkv", "null k8", "q8 misaligned"])
+def test_noalloc_rejects_invalid(lib, case):
+    qk, v = _pair_valid()
+    QK_BREAKS[case](qk)
+    assert lib.sage_quant_qkv_noalloc(ctypes.byref(qk), ctypes.byref(v), None) == A.SAGE_EINVAL
+    qk, v = _pair_valid()
+    v.Nk = 301                                           # K and V disagree
+    assert lib.sage_quant_qkv_noalloc(ctypes.byref(qk), ctypes.byref(v), None) == A.SAGE_EINVAL
