@@ -247,7 +247,10 @@ int sage_attn_fwd(const sage_attn_params* p, void* stream);
  * sage_attn_varlen_fwd: as sage_attn_fwd for a packed batch of sequences
  * (deployment guide sec. 4.2, sageattn_varlen with cu_seqlens_q/k).  The
  * quantized operands use the layouts above with B = number of sequences and
- * Nq/Nk = max_seqlen_q/k.  Causal masking is per sequence.  out is packed
+ * Nq/Nk = max_seqlen_q/k.  Causal masking is per sequence.  A sequence longer
+ * than max_seqlen (here and in the quantize calls) is cut to its first
+ * max_seqlen tokens, all that its padded slot holds: later keys are ignored
+ * and the outputs and LSEs of later queries are not written.  out is packed
  * token-major: token (cu_seqlens_q[b] + n), head h, channel c at
  * out + (cu_seqlens_q[b] + n)*o_stride_n + h*o_stride_h + c.
  * lse (optional): fp32 [Hq][total_q], total_q = cu_seqlens_q[B].
@@ -279,13 +282,14 @@ int sage_debug_qk_scores(const sage_attn_params* p, int mode, void* scores, void
  * shorter; ranges that would be empty are dropped, so S = ceil(Nk /
  * split_len) <= n_splits).  Each range runs the same online softmax as
  * sage_attn_fwd, starting afresh at its first key; its normalised output is
- * rounded to out_dtype and stored with its log-sum-exp in the workspace, and
- * the S partial results are then combined as sage_merge_states does.  With
- * S = 1 the result is bit-identical to sage_attn_fwd.
+ * stored in fp32 with its log-sum-exp in the workspace, and the S partial
+ * results are then combined as sage_merge_states does (in fp32, one rounding
+ * to out_dtype at the end).  With S = 1 the result is bit-identical to
+ * sage_attn_fwd.
  * Same parameters and layouts as sage_attn_fwd; non-causal only.
  * workspace: device memory, 256-byte aligned, of at least
  * sage_attn_splitkv_workspace_size(B, Hq, Nq, Nk, d, n_splits) bytes (0 for
- * invalid sizes); it holds S x [B][Hq][Nq][d] outputs and S x [B][Hq][Nq]
+ * invalid sizes); it holds S x [B][Hq][Nq][d] fp32 outputs and S x [B][Hq][Nq]
  * fp32 LSEs and need not be initialised.
  * Errors: as sage_attn_fwd; SAGE_EINVAL for n_splits outside 1..64 or a
  * missing, misaligned or too small workspace; SAGE_EUNSUPPORTED for

@@ -387,14 +387,14 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
     step by step: quantize Q, K, V over the whole sequence as
     reference_forward does; for each key range (splitkv_ranges) run the
     online-softmax attention of that range alone, starting afresh at its first
-    key ([guide] sec. 4.1: q and k/v lengths may differ), and round its
-    normalised output to the input dtype; combine the ranges with merge_states
-    (the return_lse merge of [guide] sec. 4.1).
+    key ([guide] sec. 4.1: q and k/v lengths may differ), keeping its
+    normalised output unrounded; combine the ranges with merge_states (the
+    return_lse merge of [guide] sec. 4.1).
 
     Returns per sequence b: out[b] (Hq, nrows, d) fp64 merged output before
     its final rounding, lse[b] (Hq, nrows), allow[b] (Hq, nrows, d): the
-    per-range rounding allowances plus one output ulp of each rounded range
-    output, weighted as in the merge, plus what the ranges' LSE allowances
+    per-range rounding allowances, weighted as in the merge, plus what the
+    ranges' LSE allowances
     can move the merge weights (a change of at most e of every L_s moves the
     normalised weights by factors within e^(+-2e)); lse_allow[b]
     (Hq, nrows): the largest LSE allowance of the row's ranges (the merged
@@ -410,7 +410,6 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
     qz = reference_forward(q, k, v, dtype=dtype, layout=layout, gran=gran, v_dtype=v_dtype, smooth_k=smooth_k,
                            smooth_v=smooth_v, attention=False)
     p_mode = 0 if v_dtype == "fp8" else (2 if dtype == "bf16" else 1)
-    mbits, emin = (7, -126) if dtype == "bf16" else (10, -14)
     L = lib()
     res = {"out": [], "lse": [], "allow": [], "lse_allow": [], "parts_scale": [], "rows": []}
     for b in range(len(qz["q8"])):
@@ -446,12 +445,10 @@ def reference_forward_splitkv(q: np.ndarray, k: np.ndarray, v: np.ndarray, *, dt
                                         len(r), _p(r), _p(o), _p(ls), None, _p(al), None, None, None, _p(la))
                 if rc != 0:
                     raise RuntimeError(f"oracle_attn_rows failed ({rc})")
-                # the range's output, rounded to the output dtype as it is stored
-                po.append(round_half(o[:, :d].astype(np.float32), dtype).astype(np.float64))
+                po.append(o[:, :d])
                 pl.append(ls)
                 pla.append(la)
-                a = np.maximum(np.abs(o[:, :d]), 2.0 ** emin)
-                pa.append(al[:, :d] + np.exp2(np.floor(np.log2(a)) - mbits))
+                pa.append(al[:, :d])
             po, pl, pa, pla = np.stack(po), np.stack(pl), np.stack(pa), np.stack(pla)
             mo, ml = merge_states(po, pl)
             m = pl.max(axis=0)

@@ -79,6 +79,20 @@ def _geometry(x: torch.Tensor, layout: str, cu: Optional[torch.Tensor], max_seql
     raise ValueError(f"tensor_layout must be 'HND' or 'NHD', not {layout!r}")
 
 
+def _check_out(out: torch.Tensor, shape, device: torch.device, name: str = "out") -> None:
+    """A caller-supplied output must have exactly the extent the kernels write
+    (the C ABI sees only its pointer and strides), a 16-bit float dtype, the
+    inputs' device and a contiguous last dimension."""
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(out.shape)}, expected {tuple(shape)}")
+    if out.dtype not in _DT:
+        raise ValueError(f"{name} dtype {out.dtype} unsupported: fp16 or bf16")
+    if out.device != device:
+        raise ValueError(f"{name} is on {out.device}, the inputs on {device}")
+    if out.stride(-1) != 1:
+        raise ValueError(f"the last dimension of {name} must be contiguous")
+
+
 @dataclasses.dataclass
 class QuantQK:
     q8: torch.Tensor
@@ -256,9 +270,13 @@ def sage_attn_fwd(qk: QuantQK, qv: QuantV, *, tensor_layout: str = "HND", is_cau
                   out: Optional[torch.Tensor] = None):
     L = A.load()
     dev = qk.q8.device
+    if tensor_layout not in ("HND", "NHD"):
+        raise ValueError(f"tensor_layout must be 'HND' or 'NHD', not {tensor_layout!r}")
+    shape = (qk.B, qk.Hq, qk.Nq, qk.d) if tensor_layout == "HND" else (qk.B, qk.Nq, qk.Hq, qk.d)
     if out is None:
-        shape = (qk.B, qk.Hq, qk.Nq, qk.d) if tensor_layout == "HND" else (qk.B, qk.Nq, qk.Hq, qk.d)
         out = torch.empty(shape, dtype=qk.dtype, device=dev)
+    else:
+        _check_out(out, shape, dev)
     g = _geometry(out, tensor_layout, None, None)
     lse = torch.empty((qk.B, qk.Hq, qk.Nq), dtype=torch.float32, device=dev) if return_lse else None
     p = _attn_params(qk, qv, out, lse, is_causal, sm_scale, pv_accum_dtype, (g.sb, g.sh, g.sn))
@@ -296,9 +314,13 @@ def sage_attn_fwd_splitkv(qk: QuantQK, qv: QuantV, *, n_splits: Optional[int] = 
     merged by their log-sum-exp (few queries, many keys; non-causal)."""
     L = A.load()
     dev = qk.q8.device
+    if tensor_layout not in ("HND", "NHD"):
+        raise ValueError(f"tensor_layout must be 'HND' or 'NHD', not {tensor_layout!r}")
+    shape = (qk.B, qk.Hq, qk.Nq, qk.d) if tensor_layout == "HND" else (qk.B, qk.Nq, qk.Hq, qk.d)
     if out is None:
-        shape = (qk.B, qk.Hq, qk.Nq, qk.d) if tensor_layout == "HND" else (qk.B, qk.Nq, qk.Hq, qk.d)
         out = torch.empty(shape, dtype=qk.dtype, device=dev)
+    else:
+        _check_out(out, shape, dev)
     g = _geometry(out, tensor_layout, None, None)
     lse = torch.empty((qk.B, qk.Hq, qk.Nq), dtype=torch.float32, device=dev) if return_lse else None
     ns = splitkv_plan(qk.B, qk.Hq, qk.Nq, qk.Nk, n_splits, qk.Hkv)
@@ -318,6 +340,8 @@ def sage_attn_varlen_fwd(qk: QuantQK, qv: QuantV, cu_seqlens_q: torch.Tensor, cu
     dev = qk.q8.device
     if out is None:
         out = torch.empty((total_q, qk.Hq, qk.d), dtype=qk.dtype, device=dev)
+    else:
+        _check_out(out, (total_q, qk.Hq, qk.d), dev)
     lse = torch.empty((qk.Hq, total_q), dtype=torch.float32, device=dev) if return_lse else None
     vp = A.AttnVarlenParams()
     vp.base = _attn_params(qk, qv, out, lse, is_causal, sm_scale, pv_accum_dtype, (0, out.stride(1), out.stride(0)))
@@ -376,8 +400,10 @@ def sage_merge_states(out_parts: torch.Tensor, lse_parts: torch.Tensor, *, tenso
         raise ValueError(f"lse_parts shape {tuple(lse_parts.shape)} != {(S, B, H, N)}")
     if out is None:
         out = torch.empty(out_parts.shape[1:], dtype=out_parts.dtype, device=out_parts.device)
-    if out.stride(-1) != 1:
-        raise ValueError("the last dimension of out must be contiguous")
+    else:
+        _check_out(out, out_parts.shape[1:], out_parts.device)
+        if out.dtype != out_parts.dtype:
+            raise ValueError(f"out dtype {out.dtype} differs from the parts' {out_parts.dtype}")
     os_ = (out.stride(0), out.stride(1), out.stride(2)) if tensor_layout == "HND" else \
         (out.stride(0), out.stride(2), out.stride(1))
     lse = torch.empty((B, H, N), dtype=torch.float32, device=out_parts.device) if return_lse else None

@@ -250,6 +250,39 @@ __device__ __forceinline__ void block_sync() {
     asm volatile("" ::: "memory");
 }
 
+// Stores channels c0 .. c0+3 (those below d) of one output row at element
+// offset `row_off` of out: fp32 values (split-KV partial results) or values
+// rounded to fp16/bf16, as one 8-byte (16-byte for fp32) write when vec4.
+template <bool OUT_BF16>
+__device__ __forceinline__ void store_out4(void* out, bool out_f32, bool vec4, int64_t row_off, int c0, int d,
+                                           const float (&val)[4]) {
+    if (out_f32) {
+        float* o = reinterpret_cast<float*>(out) + row_off + c0;
+        if (vec4 && c0 + 3 < d) {
+            *reinterpret_cast<float4*>(o) = make_float4(val[0], val[1], val[2], val[3]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (c0 + e < d) o[e] = val[e];
+        }
+        return;
+    }
+    uint16_t hv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hv[e] = Half<OUT_BF16>::from_f(val[e]);
+    uint16_t* o = reinterpret_cast<uint16_t*>(out) + row_off + c0;
+    if (vec4 && c0 + 3 < d) {
+        uint2 w;
+        w.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+        w.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+        *reinterpret_cast<uint2*>(o) = w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (c0 + e < d) o[e] = hv[e];
+    }
+}
+
 // Row sums of P with one small MFMA: the lane's P values are the B operand of
 // a 16x16xK MFMA whose K blocks come from the four 16-lane groups.  Groups 0/2
 // hold queries 0..15 (lane halves 0/1), groups 1/3 queries 16..31, so an A
@@ -760,10 +793,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     const int bh = lpt ? wg % nbh : wg / a.n_qtiles, h = bh % a.Hq, b = bh / a.Hq;
     if (a.causal) qt = a.n_qtiles - 1 - qt;             // longest rows first
     int Lq = a.Nq, Lk = a.Nk, qoff = 0;
-    if (a.cu_q) {
+    if (a.cu_q) {                                       // a sequence longer than max_seqlen is cut to it
         qoff = a.cu_q[b];
-        Lq = a.cu_q[b + 1] - qoff;
-        Lk = a.cu_k[b + 1] - a.cu_k[b];
+        Lq = min(max(a.cu_q[b + 1] - qoff, 0), a.Nq);
+        Lk = min(max(a.cu_k[b + 1] - a.cu_k[b], 0), a.Nk);
     }
     const int kb0 = split * a.split_len;                // first key of this workgroup's range
     if (a.n_splits > 1) Lk = min(Lk - kb0, a.split_len);
@@ -1000,35 +1033,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         const float l_tot = ls[j][0];                   // the row-sum MFMA covers both lane halves
         const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
         if (qrow < Lq) {
-            uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + split * a.split_out +
-                             (a.cu_q ? (int64_t)(qoff + qrow) * a.on + (int64_t)h * a.oh
-                                     : (int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)qrow * a.on);
+            const int64_t row_off = split * a.split_out +
+                                    (a.cu_q ? (int64_t)(qoff + qrow) * a.on + (int64_t)h * a.oh
+                                            : (int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)qrow * a.on);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4) {
                     const int c0 = cb * 32 + 8 * r4 + 4 * hh;
                     if (c0 >= a.d) continue;
-                    uint16_t hv[4];
+                    float val[4];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const int c = c0 + e;
-                        float val = o[j][cb][4 * r4 + e];
-                        if constexpr (PV == 0) val *= vsc[c] * inv_l;
-                        else val *= inv_l;
-                        if (vmu) val += vmu[c];
-                        hv[e] = Half<OUT_BF16>::from_f(val);
+                        const int c = min(c0 + e, a.d - 1);
+                        val[e] = o[j][cb][4 * r4 + e];
+                        if constexpr (PV == 0) val[e] *= vsc[c] * inv_l;
+                        else val[e] *= inv_l;
+                        if (vmu) val[e] += vmu[c];
                     }
-                    if (a.out_vec4 && c0 + 3 < a.d) {
-                        uint2 w;
-                        w.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-                        w.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-                        *reinterpret_cast<uint2*>(orow + c0) = w;
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (c0 + e < a.d) orow[c0 + e] = hv[e];
-                    }
+                    store_out4<OUT_BF16>(a.out, a.out_f32, a.out_vec4, row_off, c0, a.d, val);
                 }
         }
         if (a.lse) {
@@ -1122,10 +1145,10 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const int h0 = pack ? (bh % a.Hkv) * grp : bh % a.Hq;
     if (a.causal) qt = a.n_qtiles - 1 - qt;
     int Lq = a.Nq, Lk = a.Nk, qoff = 0;
-    if (a.cu_q) {
+    if (a.cu_q) {                                       // a sequence longer than max_seqlen is cut to it
         qoff = a.cu_q[b];
-        Lq = a.cu_q[b + 1] - qoff;
-        Lk = a.cu_k[b + 1] - a.cu_k[b];
+        Lq = min(max(a.cu_q[b + 1] - qoff, 0), a.Nq);
+        Lk = min(max(a.cu_k[b + 1] - a.cu_k[b], 0), a.Nk);
     }
     const int kb0 = split * a.split_len;                // first key of this workgroup's range
     if (a.n_splits > 1) Lk = min(Lk - kb0, a.split_len);
@@ -1384,33 +1407,23 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const float l_tot = ls[0];
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (lane_ok) {
-        uint16_t* orow = reinterpret_cast<uint16_t*>(a.out) + split * a.split_out +
-                         (a.cu_q ? (int64_t)(qoff + qrow) * a.on + (int64_t)h * a.oh
-                                 : (int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)qrow * a.on);
+        const int64_t row_off = split * a.split_out +
+                                (a.cu_q ? (int64_t)(qoff + qrow) * a.on + (int64_t)h * a.oh
+                                        : (int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)qrow * a.on);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int c0 = cb * 32 + 8 * r4 + 4 * hh;
                 if (c0 >= a.d) continue;
-                uint16_t hv[4];
+                float val[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int c = c0 + e;
-                    float val = o[cb][4 * r4 + e] * (vsc[c] * inv_l);
-                    if (vmu) val += vmu[c];
-                    hv[e] = Half<OUT_BF16>::from_f(val);
+                    const int c = min(c0 + e, a.d - 1);
+                    val[e] = o[cb][4 * r4 + e] * (vsc[c] * inv_l);
+                    if (vmu) val[e] += vmu[c];
                 }
-                if (a.out_vec4 && c0 + 3 < a.d) {
-                    uint2 w;
-                    w.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-                    w.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-                    *reinterpret_cast<uint2*>(orow + c0) = w;
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (c0 + e < a.d) orow[c0 + e] = hv[e];
-                }
+                store_out4<OUT_BF16>(a.out, a.out_f32, a.out_vec4, row_off, c0, a.d, val);
             }
     }
     if (a.lse) {

@@ -63,10 +63,13 @@ __device__ __forceinline__ UnitHeadB unit_head_b(int bid, int units, int H) {
     return UnitHeadB{(bid / H) % units, bid % H, bid / H / units};
 }
 
+// Tokens of sequence b: [n0, n0 + N).  A varlen sequence longer than the
+// maximum length the call was given (Ndense) is cut to its first Ndense
+// tokens, which is all its padded slot holds.
 __device__ __forceinline__ void seq_range(const int32_t* cu, int b, int Ndense, int& n0, int& N) {
     if (cu) {
         n0 = cu[b];
-        N = cu[b + 1] - n0;
+        N = min(max(cu[b + 1] - n0, 0), Ndense);
     } else {
         n0 = 0;
         N = Ndense;

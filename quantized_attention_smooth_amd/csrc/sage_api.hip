@@ -476,7 +476,7 @@ SplitPlan split_plan(int B, int Hq, int Nq, int Nk, int d, int n_splits) {
     s.split_len = (int)round_up(per, sage::kPad);
     s.splits = (int)((Nk + (int64_t)s.split_len - 1) / s.split_len);
     const size_t rows = (size_t)s.splits * B * Hq * Nq;
-    s.parts_bytes = (rows * d * 2 + 255) / 256 * 256;
+    s.parts_bytes = (rows * d * 4 + 255) / 256 * 256;     // fp32 partial outputs
     s.lse_bytes = (rows * 4 + 255) / 256 * 256;
     s.total = s.parts_bytes + s.lse_bytes;
     return s;
@@ -502,9 +502,10 @@ int sage_attn_fwd_splitkv(const sage_attn_params* p, int n_splits, void* workspa
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const int64_t d = p->d, rows = (int64_t)p->B * p->Hq * p->Nq;
-    // partial results of split s: out [B][Hq][Nq][d] and LSE [B][Hq][Nq]
+    // partial results of split s: fp32 out [B][Hq][Nq][d] and LSE [B][Hq][Nq]
     sage::AttnArgs a = attn_args(p);
     a.out = ws;
+    a.out_f32 = 1;
     a.ob = (int64_t)p->Hq * p->Nq * d;
     a.oh = (int64_t)p->Nq * d;
     a.on = d;
@@ -520,6 +521,7 @@ int sage_attn_fwd_splitkv(const sage_attn_params* p, int n_splits, void* workspa
         return r;
     sage::MergeArgs m{};
     m.parts = ws;
+    m.parts_f32 = 1;
     m.ps = rows * d;
     m.pb = a.ob;
     m.ph = a.oh;

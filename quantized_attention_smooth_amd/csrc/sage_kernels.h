@@ -72,7 +72,8 @@ struct AttnArgs {
     int causal;
     float sm_scale;
     int64_t ob, oh, on;
-    int out_vec4;                // 4 consecutive channels may be stored as one 8-byte write
+    int out_vec4;                // 4 consecutive channels may be stored as one 8-byte (16-byte fp32) write
+    int out_f32;                 // out holds fp32 values (split-KV partial results), strides in floats
     int lse_varlen;              // LSE layout [Hq][total_q] instead of [B][Hq][Nq]
     int total_q;
     int n_qtiles;                // query tiles per (b, h)
@@ -98,6 +99,7 @@ struct MergeArgs {
     int64_t ob, oh, on;
     float* lse;                  // [B][H][N] or null
     int S, B, H, N, d;
+    int parts_f32;               // parts are fp32 (split-KV partials) instead of the output dtype
 };
 
 // Launchers (defined in the kernel translation units).  Each returns the

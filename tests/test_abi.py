@@ -322,13 +322,14 @@ def test_splitkv_rejects(lib, case):
 def test_splitkv_workspace_size(lib):
     assert lib.sage_attn_splitkv_workspace_size(1, 8, 4, 4133, 128, 0) == 0
     assert lib.sage_attn_splitkv_workspace_size(1, 8, 4, 4133, 129, 5) == 0
-    # 5 requested ranges of 4133 keys: ranges of 896 keys, 5 of them
+    # 5 requested ranges of 4133 keys: ranges of 896 keys, 5 of them; fp32
+    # partial outputs and LSEs, each region rounded up to 256 bytes
     rows = 5 * 1 * 8 * 4
-    want = -(-(rows * 128 * 2) // 256) * 256 + -(-(rows * 4) // 256) * 256
+    want = -(-(rows * 128 * 4) // 256) * 256 + -(-(rows * 4) // 256) * 256
     assert lib.sage_attn_splitkv_workspace_size(1, 8, 4, 4133, 128, 5) == want
     # 7 requested ranges of 1000 keys: ranges of 256 keys, only 4 of them
     rows = 4 * 2 * 3 * 10
-    want = -(-(rows * 64 * 2) // 256) * 256 + -(-(rows * 4) // 256) * 256
+    want = -(-(rows * 64 * 4) // 256) * 256 + -(-(rows * 4) // 256) * 256
     assert lib.sage_attn_splitkv_workspace_size(2, 3, 10, 1000, 64, 7) == want
 
 

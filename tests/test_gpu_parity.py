@@ -215,6 +215,32 @@ def test_varlen_equals_per_sequence_dense():
         assert torch.equal(lse[:, s:e], lb[0]), b
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_sequence_longer_than_max_seqlen_is_cut(causal):
+    """A sequence longer than the max_seqlen the calls are given is taken as
+    its first max_seqlen tokens (all its padded slot holds): the result equals,
+    bit for bit, the same batch with that sequence cut, and the output rows
+    past the cut keep what they held."""
+    _announce(f"varlen sequence beyond max_seqlen, causal={causal}")
+    g = torch.Generator().manual_seed(12)
+    lens, max_len = [100, 300, 50], 200
+    T = sum(lens)
+    q, k, v = (torch.randn(T, 4, 128, generator=g).half().cuda() for _ in range(3))
+    cu = torch.tensor([0, 100, 400, 450], dtype=torch.int32).cuda()
+    keep = torch.tensor(list(range(0, 300)) + list(range(400, 450))).cuda()
+    cu_cut = torch.tensor([0, 100, 300, 350], dtype=torch.int32).cuda()
+    qk, qv = sage.sage_quant_qkv(q, k, v, cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=max_len,
+                                 max_seqlen_k=max_len, smooth_v=True)
+    out = torch.full((T, 4, 128), float("nan"), dtype=torch.float16, device="cuda")
+    out, lse = sage.sage_attn_varlen_fwd(qk, qv, cu, cu, T, is_causal=causal, return_lse=True, out=out)
+    ref, ref_lse = sage.sageattn_varlen(q[keep], k[keep], v[keep], cu_cut, cu_cut, max_len, max_len,
+                                        is_causal=causal, return_lse=True, smooth_v=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out[keep], ref)
+    assert torch.equal(lse[:, keep], ref_lse)
+    assert torch.isnan(out[300:400]).all()
+
+
 def test_deterministic():
     _announce("run-to-run determinism")
     g = torch.Generator().manual_seed(9)

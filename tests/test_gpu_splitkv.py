@@ -2,10 +2,12 @@
 
 sage_attn_fwd_splitkv against the oracle's split emulation
 (oracle.reference_forward_splitkv) on the same seeded inputs: per element
-|gpu - oracle| <= 2e-3 + 2 output ulps + the oracle's merged per-range
-allowance + 1e-4 * the largest range output of the row (the merge's fp32
-weights built from the ranges' LSEs, which themselves agree to 1e-3), and
-cosine >= 0.9999; the merged LSE within 2e-3.  One range is bit-identical to
+|gpu - oracle| <= 2e-3 + 1 output ulp (the dense forward's bound) + the
+oracle's merged allowance + 3e-5 * the largest range output of the row (the
+merge's fp32 weights: range LSEs of magnitude below ~50 carry fp32 rounding
+of a few 1e-6, and each weight's exp adds an ulp), and cosine >= 0.9999; the
+merged LSE within 2e-3 + the LSE allowance.  The ranges' partial outputs are
+kept in fp32, so no rounding happens before the final one.  One range is bit-identical to
 sage_attn_fwd.  On a decode-like shape (16 queries, 16 384 keys) the result is
 within the method's tolerance of exact attention (cosine >= 0.999).
 """
@@ -58,7 +60,7 @@ def test_splitkv_matches_oracle(case):
         got = got.transpose(0, 2, 1, 3)
     for b in range(B):
         r = ref["out"][b]
-        tol = 2e-3 + 2 * out_ulp(r, dtype) + ref["allow"][b] + 1e-4 * ref["parts_scale"][b][..., None]
+        tol = 2e-3 + out_ulp(r, dtype) + ref["allow"][b] + 3e-5 * ref["parts_scale"][b][..., None]
         diff = np.abs(got[b] - r)
         assert (diff <= tol).all(), f"batch {b}: {(diff > tol).sum()} outputs off, worst {diff.max():.3g}"
         assert cosine(got[b], r) >= COS_EMU
@@ -135,7 +137,7 @@ def test_sageattn_kv_splits_matches_oracle():
     got = out.float().cpu().numpy()
     for b in range(2):
         r = ref["out"][b]
-        tol = 2e-3 + 2 * out_ulp(r, "fp16") + ref["allow"][b] + 1e-4 * ref["parts_scale"][b][..., None]
+        tol = 2e-3 + out_ulp(r, "fp16") + ref["allow"][b] + 3e-5 * ref["parts_scale"][b][..., None]
         assert (np.abs(got[b] - r) <= tol).all()
     with pytest.raises(NotImplementedError):
         sage.sageattn(q, k, v, is_causal=True, kv_splits=2)

@@ -58,3 +58,48 @@ def test_sageattn_refuses_cpu_tensors():
     q = torch.zeros(1, 2, 4, 64, dtype=torch.float16)
     with pytest.raises(ValueError):                     # CPU tensors are refused first
         sage.sageattn(q, q, q, kv_splits=2)
+
+
+# ---------------------------------------------------------------- caller-supplied outputs
+def _cpu_quantized(B=1, Hq=2, Hkv=2, N=130, d=64):
+    """Quantized-operand holders with CPU tensors: the binding's output checks
+    run before any call into the library, so no GPU is needed."""
+    import torch
+    from quantized_attention_smooth_amd.api import QuantQK, QuantV
+    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt)
+    qk = QuantQK(z(B, Hq, 256, 64, dt=torch.int8), z(B, Hq, 256), z(B, Hkv, 256, 64, dt=torch.int8), z(B, Hkv, 16),
+                 z(B, Hkv, 64), "per_thread", B, Hq, Hkv, N, N, d, torch.float16)
+    qv = QuantV(z(B, Hkv, 64, 256, dt=torch.uint8), z(B, Hkv, 64), None, "fp8")
+    return qk, qv
+
+
+@pytest.mark.parametrize("bad", ["shape", "dtype", "layout"])
+def test_attn_fwd_rejects_wrong_out(bad):
+    import torch
+    import quantized_attention_smooth_amd as sage
+    qk, qv = _cpu_quantized()
+    shape, dt = (1, 2, 130, 64), torch.float16
+    if bad == "shape":
+        shape = (1, 2, 129, 64)
+    if bad == "dtype":
+        dt = torch.float32
+    out = torch.empty(shape, dtype=dt)
+    layout = "NHD" if bad == "layout" else "HND"           # HND-shaped out for an NHD call
+    with pytest.raises(ValueError):
+        sage.sage_attn_fwd(qk, qv, out=out, tensor_layout=layout)
+    with pytest.raises(ValueError):
+        sage.sage_attn_fwd_splitkv(qk, qv, out=out, tensor_layout=layout, n_splits=2)
+
+
+def test_attn_varlen_and_merge_reject_wrong_out():
+    import torch
+    import quantized_attention_smooth_amd as sage
+    qk, qv = _cpu_quantized(B=3)
+    cu = torch.tensor([0, 50, 90, 130], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        sage.sage_attn_varlen_fwd(qk, qv, cu, cu, 130, out=torch.empty((129, 2, 64), dtype=torch.float16))
+    parts = torch.zeros((2, 1, 2, 10, 64), dtype=torch.float16)
+    lse = torch.zeros((2, 1, 2, 10), dtype=torch.float32)
+    for out in (torch.empty((1, 2, 10, 32), dtype=torch.float16), torch.empty((1, 2, 10, 64), dtype=torch.bfloat16)):
+        with pytest.raises(ValueError):
+            sage.sage_merge_states(parts, lse, out=out)
