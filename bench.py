@@ -4,11 +4,14 @@
 One step = one pass of the whole hot path over one batch already resident in
 HBM: sage_quant_qkv (K mean and V statistics, INT8 Q/K, FP8 V^T, in two
 launches) and sage_attn_fwd (INT8 QK^T, online softmax, FP8 P.V).  The step
-rate (`value`) comes from replaying the step captured in a HIP graph, which
-removes the Python launch overhead between the kernels (`--eager` times eager
-launches instead; `ms_per_step_eager` always reports them); kernel times come
-from HIP events around eager launches.  The default workload
-is B=2, H=8, N=4096, head_dim=128, fp16, per_warp INT8 Q/K, FP8 V.
+rate (`value`) comes from eager launches (`--graph` replays the step captured
+in a HIP graph instead); kernel times come from HIP events around the eager
+launches.  Before any of it, untimed steps run
+for --settle-ms of wall time (the GPU clock rises over the first tens of
+milliseconds of work), then the --warmup steps.  The default workload
+is B=2, H=8, N=4096, head_dim=128, fp16, per_warp INT8 Q/K, FP8 V;
+--workload varlen16_h16 times the packed variable-length batch
+(sage_attn_varlen_fwd).
 
 Prints ONE JSON line.  `value` is whole-step TOPS (4*B*H*Nq*Nk*d per step,
 halved for causal).  `roofline` describes the attention kernel, timed with HIP
@@ -74,57 +77,109 @@ def cpu_baseline(w, inp, seconds: float) -> dict:
     ops, heads, t_total = 0.0, 0, 0.0
     grp = w.Hq // w.Hkv
     problems = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    cu = inp["cu_seqlens"].numpy() if w.varlen else None
     while t_total < seconds:
         b, h = problems[heads % len(problems)]
         hk = h // grp
-        if w.layout == "HND":
+        if w.varlen:                          # sequence b as a dense token-major problem
+            s0, s1 = int(cu[b]), int(cu[b + 1])
+            qs, ks, vs = (x[None, s0:s1, hh:hh + 1] for x, hh in ((q, h), (k, hk), (v, hk)))
+            layout, nq = "NHD", s1 - s0
+        elif w.layout == "HND":
             qs, ks, vs = q[b:b + 1, h:h + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1]
+            layout, nq = "HND", w.Nq
         else:
             qs, ks, vs = q[b:b + 1, :, h:h + 1], k[b:b + 1, :, hk:hk + 1], v[b:b + 1, :, hk:hk + 1]
+            layout, nq = "NHD", w.Nq
         t0 = time.perf_counter()
         oracle.reference_forward(np.ascontiguousarray(qs), np.ascontiguousarray(ks), np.ascontiguousarray(vs),
-                                 dtype=w.dtype, layout=w.layout, causal=w.causal, gran=w.gran,
+                                 dtype=w.dtype, layout=layout, causal=w.causal, gran=w.gran,
                                  v_dtype=w.v_dtype, smooth_k=w.smooth_k, smooth_v=w.smooth_v)
         t_total += time.perf_counter() - t0
         heads += 1
-        per = 4.0 * w.Nq * w.Nk * w.d
+        per = 4.0 * nq * (nq if w.varlen else w.Nk) * w.d
         ops += per / 2 if w.causal else per
+    unit = "(sequence, head)" if w.varlen else "(batch, head)"
     return {"value": ops / t_total / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
-            "sample": f"{heads} (batch, head) problems of {w.name} (of {w.B * w.Hq} per step, taken in order, "
-                      f"repeating if needed), all {w.Nq} query rows, "
+            "sample": f"{heads} {unit} problems of {w.name} (of {w.B * w.Hq} per step, taken in order, "
+                      f"repeating if needed), every query row, "
                       f"quantization included; {t_total:.1f} s"}
 
 
-def time_workload(w, steps: int, warmup: int, calibrate: bool = False):
-    """Run `warmup` untimed and `steps` timed steps of the hot path (fused
-    quantize + attention) on inputs resident in HBM.  Returns the inputs and
-    (ms per step from the host clock, quantize ms and attention ms from HIP
-    events recorded on the stream the kernels run on)."""
+def make_step(w, inp):
+    """The hot-path step of workload w on its inputs, moved to the GPU once:
+    sage_quant_qkv (two launches, caller workspaces) then sage_attn_fwd (or
+    sage_attn_varlen_fwd).  step(ev) records ev[0], ev[1], ev[2] before the
+    quantize call, between the calls and after the attention call, on the
+    stream the kernels run on."""
     import torch
-    import workloads
     import quantized_attention_smooth_amd as sage
 
-    if w.varlen:
-        raise SystemExit("the benchmark workload must be dense")
-    inp = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
     q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
-    ws_k = torch.empty(sage.workspace_bytes(w.B, w.Hkv, w.Nk, w.d), dtype=torch.uint8, device=dev)
+    n_max = inp["max_seqlen"] if w.varlen else w.Nk
+    ws_k = torch.empty(sage.workspace_bytes(w.B, w.Hkv, n_max, w.d), dtype=torch.uint8, device=dev)
     ws_v = torch.empty_like(ws_k)
     stream = torch.cuda.current_stream()
+    if w.varlen:
+        cu = inp["cu_seqlens"].to(dev)
+        qkw = dict(cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=n_max, max_seqlen_k=n_max)
+    else:
+        qkw = dict(tensor_layout=w.layout)
 
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        qk, qv = sage.sage_quant_qkv(q, k, v, tensor_layout=w.layout, qk_quant_gran=w.gran, smooth_k=w.smooth_k,
-                                     v_dtype=w.v_dtype, smooth_v=w.smooth_v, workspace_k=ws_k, workspace_v=ws_v)
+        qk, qv = sage.sage_quant_qkv(q, k, v, qk_quant_gran=w.gran, smooth_k=w.smooth_k, v_dtype=w.v_dtype,
+                                     smooth_v=w.smooth_v, workspace_k=ws_k, workspace_v=ws_v, **qkw)
         if ev is not None:
             ev[1].record(stream)
-        out = sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, is_causal=w.causal,
-                                 return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
+        if w.varlen:
+            out = sage.sage_attn_varlen_fwd(qk, qv, cu, cu, q.shape[0], is_causal=w.causal,
+                                            return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
+        else:
+            out = sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, is_causal=w.causal,
+                                     return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
         if ev is not None:
             ev[2].record(stream)
         return out
+
+    return step
+
+
+def settle_clock(step, settle_ms: float) -> tuple:
+    """Run untimed steps until `settle_ms` of wall time has passed: the GPU's
+    clock rises over the first tens of milliseconds of work, so timing only
+    after a fixed stretch of work (rather than a fixed number of steps)
+    measures the steady clock whatever the step's length.  Returns (ms spent,
+    steps run)."""
+    import torch
+
+    for _ in range(3):                     # one-time costs (code-object load, allocator) before the clock starts
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < settle_ms:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+        n += 8
+    return (time.perf_counter() - t0) * 1e3, n
+
+
+def time_workload(w, steps: int, warmup: int, calibrate: bool = False, settle_ms: float = 0.0):
+    """Settle the clock, then run `warmup` untimed and `steps` timed steps of
+    the hot path (fused quantize + attention) on inputs resident in HBM.
+    Returns the inputs, (ms per step from the host clock, quantize ms and
+    attention ms from HIP events recorded on the stream the kernels run on)
+    and (settle ms, settle steps)."""
+    import torch
+    import workloads
+
+    inp = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    step = make_step(w, inp)
 
     if calibrate:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -134,6 +189,7 @@ def time_workload(w, steps: int, warmup: int, calibrate: bool = False):
         torch.cuda.synchronize()
         del src, dst
 
+    settle = settle_clock(step, settle_ms)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -147,7 +203,7 @@ def time_workload(w, steps: int, warmup: int, calibrate: bool = False):
     ms_per_step = (t1 - t0) * 1e3 / steps
     quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / steps
     attn_ms = sum(e[1].elapsed_time(e[2]) for e in events) / steps
-    return inp, ms_per_step, quant_ms, attn_ms
+    return inp, (ms_per_step, quant_ms, attn_ms), settle
 
 
 def time_step_graph(w, inp, steps: int, warmup: int):
@@ -157,19 +213,8 @@ def time_step_graph(w, inp, steps: int, warmup: int):
     (ms per step from the host clock, output of the last replay, output of one
     eager step for comparison)."""
     import torch
-    import quantized_attention_smooth_amd as sage
 
-    dev = torch.device("cuda:0")
-    q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
-    ws_k = torch.empty(sage.workspace_bytes(w.B, w.Hkv, w.Nk, w.d), dtype=torch.uint8, device=dev)
-    ws_v = torch.empty_like(ws_k)
-
-    def step():
-        qk, qv = sage.sage_quant_qkv(q, k, v, tensor_layout=w.layout, qk_quant_gran=w.gran, smooth_k=w.smooth_k,
-                                     v_dtype=w.v_dtype, smooth_v=w.smooth_v, workspace_k=ws_k, workspace_v=ws_v)
-        return sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, is_causal=w.causal,
-                                  return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
-
+    step = make_step(w, inp)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -389,9 +434,10 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # the GPU's clock rises over the first tens of milliseconds of work: 300 untimed steps (~40 ms on the default
-    # workload) let the timed steps run at the steady clock
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
+    # the GPU's clock rises over the first tens of milliseconds of work: before the declared warmup, untimed steps
+    # run for this much wall time, so the timed steps see the steady clock whatever --warmup says
+    ap.add_argument("--settle-ms", type=float, default=500.0)
     ap.add_argument("--workload", default="b2h8n4096d128")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -400,9 +446,10 @@ def main() -> int:
     ap.add_argument("--secondary", default="video_dit_n17550",
                     help="a second workload whose attention-kernel TOPS is reported beside the main line "
                          "('none' to skip); the metric is quoted at sequence 4096 and 17.5k")
-    ap.add_argument("--eager", action="store_true",
-                    help="time the step from eager launches only (by default the step rate comes from replaying "
-                         "the step captured in a HIP graph; kernel times always come from the eager launches)")
+    ap.add_argument("--graph", action="store_true",
+                    help="take the step rate from replaying the step captured in a HIP graph instead of from eager "
+                         "launches (kernel times always come from the eager launches); on ROCm 7 the replays "
+                         "measured slower than eager launches")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step line, print one JSON line with attention-kernel TOPS over sequence "
                          "lengths 1K-32K, non-causal and causal, against torch SDPA")
@@ -424,23 +471,34 @@ def main() -> int:
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
-    inp, ms_eager, quant_ms, attn_ms = time_workload(w, args.steps, args.warmup, args.traffic_calibration)
+    inp, (ms_eager, quant_ms, attn_ms), (settle_ms, settle_steps) = time_workload(
+        w, args.steps, args.warmup, args.traffic_calibration, args.settle_ms)
     ms_per_step, launch = ms_eager, "eager"
-    if not args.eager:
+    if args.graph:
         import torch
         ms_graph, out_g, out_e = time_step_graph(w, inp, args.steps, args.warmup)
         if not torch.equal(out_g.view(torch.int16), out_e.view(torch.int16)):
             raise SystemExit("graph replay output differs from the eager step")
         ms_per_step, launch = ms_graph, "hip_graph"
 
-    ops = workloads.attention_ops(w)
+    lens = inp.get("lens")
+    ops = workloads.attention_ops(w, lens)
     value = ops / (ms_per_step * 1e-3) / 1e12
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_TOPS[w.v_dtype]
     # quantize-pass bytes: read Q, K, V once, K and V a second time for the
     # statistics, write INT8 Q/K and FP8 V (+ small scale arrays)
-    elem = w.B * (w.Hq * w.Nq + 2 * w.Hkv * w.Nk) * w.d
-    quant_bytes = 2 * elem + 2 * 2 * w.B * w.Hkv * w.Nk * w.d + elem
+    tok_q = int(sum(lens)) if w.varlen else w.B * w.Nq
+    tok_k = int(sum(lens)) if w.varlen else w.B * w.Nk
+    elem = (w.Hq * tok_q + 2 * w.Hkv * tok_k) * w.d
+    quant_bytes = 2 * elem + 2 * 2 * w.Hkv * tok_k * w.d + elem
+    config = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "seq_len": w.Nq, "head_dim": w.d,
+              "in_dtype": w.dtype, "layout": w.layout, "causal": w.causal, "qk_quant_gran": w.gran,
+              "v_dtype": w.v_dtype, "pv_accum_dtype": w.pv_accum, "smooth_k": w.smooth_k,
+              "smooth_v": w.smooth_v, "parallelism": "none (1 GPU)"}
+    if w.varlen:
+        config.update(layout="packed varlen", seq_len=None, n_seq=w.B, seq_lens=[int(x) for x in lens],
+                      total_tokens=tok_q, max_seqlen=int(inp["max_seqlen"]))
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -448,6 +506,8 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "clock_settle_ms": round(settle_ms, 1),
+        "clock_settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 5),
         "step_launch": launch,
         "ms_per_step_eager": round(ms_eager, 5),
@@ -456,10 +516,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "i8+fp8" if w.v_dtype == "fp8" else "i8+fp16",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "seq_len": w.Nq, "head_dim": w.d,
-                   "in_dtype": w.dtype, "layout": w.layout, "causal": w.causal, "qk_quant_gran": w.gran,
-                   "v_dtype": w.v_dtype, "pv_accum_dtype": w.pv_accum, "smooth_k": w.smooth_k,
-                   "smooth_v": w.smooth_v, "parallelism": "none (1 GPU)"},
+        "config": config,
         "attn_kernel_ms": round(attn_ms, 5),
         "attn_kernel_tops": round(attn_tops, 2),
         "attn_pct_of_peak": round(100.0 * attn_tops / peak, 2),
@@ -470,7 +527,7 @@ def main() -> int:
     }
     if args.secondary != "none" and args.secondary != w.name:
         w2 = workloads.WORKLOADS[args.secondary]
-        _, ms2, qms2, ams2 = time_workload(w2, 10, 20)
+        _, (ms2, qms2, ams2), _ = time_workload(w2, 10, 20)
         ops2 = workloads.attention_ops(w2)
         at2 = ops2 / (ams2 * 1e-3) / 1e12
         rec["secondary"] = {"workload": w2.name, "seq_len": w2.Nq, "head_dim": w2.d, "B": w2.B, "Hq": w2.Hq,

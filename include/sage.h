@@ -57,7 +57,14 @@
  * code = rint(x * fl32(127/amax)); all-zero group -> scale 0, codes 0.
  * V (FP8): per channel c over the sequence, code = E4M3FN(clamp(v' *
  * fl32(448/amax_c), +-448)), v' = fl32(v - v_mean_c) when smooth_v.
- * Means are fl32(fl64(exact sum) / N), independent of summation order.
+ * Means are fl32(fl64(exact sum) / N), independent of summation order:
+ * fp16 values are summed exactly as integers in units of 2^-24 (N < 2^23);
+ * bf16 values are summed in fp64, which is exact -- in any order -- when the
+ * column's sum of |x| is below 2^53 u, u the smallest bf16 ulp among its
+ * nonzero values (2^(floor(log2|x|) - 7), at least 2^-133): e.g. a span of
+ * about 46 - log2(N) binades between its largest and smallest magnitude.
+ * Beyond that the bf16 sum carries fp64 rounding and the mean can differ
+ * from the exactly rounded one in its last bit.
  */
 #ifndef SAGE_H
 #define SAGE_H
@@ -272,6 +279,15 @@ int sage_attn_varlen_fwd(const sage_attn_varlen_params* p, void* stream);
  * Errors: as sage_attn_fwd.
  * ------------------------------------------------------------------------- */
 int sage_debug_qk_scores(const sage_attn_params* p, int mode, void* scores, void* stream);
+
+/* sage_debug_qk_scores_varlen: the per-row checksums of mode 1 for a packed
+ * varlen batch (sage_attn_varlen_params; out, lse and the V fields are not
+ * used), from the same tile code, per sequence with the forward's lengths:
+ * checksums int64 [Hq][total_q][2] = (sum_j S_ij, sum_j (j+1) S_ij) modulo
+ * 2^64 over the keys j of row i's own sequence.
+ * Errors: SAGE_EINVAL for invalid sizes, NULL or misaligned pointers,
+ * total_q < 1. */
+int sage_debug_qk_scores_varlen(const sage_attn_varlen_params* p, void* checksums, void* stream);
 
 /* ---------------------------------------------------------------------------
  * sage_attn_fwd_splitkv: sage_attn_fwd for few queries against many keys

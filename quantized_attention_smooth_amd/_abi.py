@@ -73,7 +73,7 @@ class MergeParams(ctypes.Structure):
 
 EXPORTS = ["sage_quant_qk", "sage_quant_workspace_size", "sage_quant_v", "sage_quant_qkv",
            "sage_quant_qkv_noalloc_scratch_size", "sage_quant_qkv_noalloc", "sage_attn_fwd",
-           "sage_attn_varlen_fwd", "sage_debug_qk_scores", "sage_merge_states", "sage_attn_splitkv_workspace_size",
+           "sage_attn_varlen_fwd", "sage_debug_qk_scores", "sage_debug_qk_scores_varlen", "sage_merge_states", "sage_attn_splitkv_workspace_size",
            "sage_attn_fwd_splitkv", "sage_last_error", "sage_version"]
 
 _lib = None
@@ -108,6 +108,8 @@ def load(path: str = LIB_PATH):
     L.sage_attn_varlen_fwd.restype = I
     L.sage_debug_qk_scores.argtypes = [ctypes.POINTER(AttnParams), I, VP, VP]
     L.sage_debug_qk_scores.restype = I
+    L.sage_debug_qk_scores_varlen.argtypes = [ctypes.POINTER(AttnVarlenParams), VP, VP]
+    L.sage_debug_qk_scores_varlen.restype = I
     L.sage_attn_fwd_splitkv.argtypes = [ctypes.POINTER(AttnParams), I, VP, SZ, VP]
     L.sage_attn_fwd_splitkv.restype = I
     L.sage_attn_splitkv_workspace_size.argtypes = [I, I, I, I, I, I]

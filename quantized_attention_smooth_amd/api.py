@@ -351,11 +351,26 @@ def sage_attn_varlen_fwd(qk: QuantQK, qv: QuantV, cu_seqlens_q: torch.Tensor, cu
     return (out, lse) if return_lse else out
 
 
-def sage_debug_qk_scores(qk: QuantQK, checksums: bool = False) -> torch.Tensor:
+def sage_debug_qk_scores(qk: QuantQK, checksums: bool = False, cu_seqlens_q: Optional[torch.Tensor] = None,
+                         cu_seqlens_k: Optional[torch.Tensor] = None, total_q: Optional[int] = None) -> torch.Tensor:
     """int32 scores [B, Hq, Nq, Nk] from the attention kernel's QK^T tile code,
-    or int64 row checksums [B, Hq, Nq, 2] (sum_j S_ij, sum_j (j+1) S_ij)."""
+    or int64 row checksums [B, Hq, Nq, 2] (sum_j S_ij, sum_j (j+1) S_ij).  For
+    a varlen batch (cu_seqlens given) only the checksums exist, int64
+    [Hq, total_q, 2], over each row's own sequence."""
     L = A.load()
     dev = qk.q8.device
+    if cu_seqlens_q is not None:
+        if not checksums or cu_seqlens_k is None or total_q is None:
+            raise ValueError("varlen scores come as checksums, with cu_seqlens_q, cu_seqlens_k and total_q")
+        buf = torch.empty((qk.Hq, int(total_q), 2), dtype=torch.int64, device=dev)
+        vp = A.AttnVarlenParams()
+        vp.base.struct_size = ctypes.sizeof(A.AttnVarlenParams)
+        vp.base.q8, vp.base.k8 = _ptr(qk.q8), _ptr(qk.k8)
+        vp.base.B, vp.base.Hq, vp.base.Hkv, vp.base.Nq, vp.base.Nk, vp.base.d = qk.B, qk.Hq, qk.Hkv, qk.Nq, qk.Nk, qk.d
+        vp.base.gran = _GRAN[qk.gran]
+        vp.cu_seqlens_q, vp.cu_seqlens_k, vp.total_q = _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(total_q)
+        A.check(L.sage_debug_qk_scores_varlen(ctypes.byref(vp), _ptr(buf), _stream()))
+        return buf
     if checksums:
         buf = torch.empty((qk.B, qk.Hq, qk.Nq, 2), dtype=torch.int64, device=dev)
     else:
@@ -420,10 +435,11 @@ def sage_merge_states(out_parts: torch.Tensor, lse_parts: torch.Tensor, *, tenso
     return (out, lse) if return_lse else out
 
 
-def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: str = "HND",
-             is_causal: bool = False, sm_scale: Optional[float] = None, return_lse: bool = False, *,
-             qk_quant_gran: str = "per_thread", pv_accum_dtype: str = "fp32+fp32", smooth_k: bool = True,
-             smooth_v: bool = False, v_dtype: str = "fp8", kv_splits=None):
+def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout="HND", is_causal=False,
+             sm_scale: Optional[float] = None, return_lse=False, *, qk_quant_gran: str = "per_thread",
+             pv_accum_dtype: str = "fp32+fp32", smooth_k: bool = True, smooth_v: bool = False, v_dtype: str = "fp8",
+             kv_splits=None, attn_mask=None, dropout_p: float = 0.0, scale: Optional[float] = None,
+             enable_gqa: Optional[bool] = None):
     """Quantized attention forward: out = softmax(q k^T * sm_scale) v.
 
     q, k, v: fp16/bf16 CUDA tensors, (B, H, N, D) for HND or (B, N, H, D) for
@@ -432,11 +448,41 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout: s
     split-KV forward (key ranges in parallel, merged by log-sum-exp) for few
     queries against many keys -- non-causal only.
     Returns out (same dtype and layout as q) and, with return_lse, the fp32
-    log-sum-exp [B, Hq, Nq]."""
+    log-sum-exp [B, Hq, Nq].
+
+    Drop-in for torch.nn.functional.scaled_dot_product_attention (deployment
+    guide sec. 5.1 assigns sageattn to it): SDPA's keywords attn_mask,
+    dropout_p, is_causal, scale and enable_gqa are accepted, and so is SDPA's
+    positional order (q, k, v, attn_mask, dropout_p, is_causal, scale), told
+    apart by a fourth argument that is not a layout string.  SDPA tensors are
+    (..., H, N, D): 4-D is HND, 3-D (H, N, D) gets a batch of one.  A mask or
+    a nonzero dropout raises NotImplementedError, which a caller can catch to
+    fall back to the original function (the pages' advice for unsupported
+    calls); grouped K/V heads need no enable_gqa."""
+    if not isinstance(tensor_layout, str):
+        # SDPA's positional order: (q, k, v, attn_mask, dropout_p, is_causal, scale)
+        attn_mask, dropout_p, is_causal = tensor_layout, is_causal, sm_scale
+        scale = None if isinstance(return_lse, bool) else return_lse      # seventh positional, if given
+        tensor_layout, sm_scale, return_lse = "HND", None, False
+        dropout_p = 0.0 if dropout_p is False else dropout_p
+        is_causal = bool(is_causal) if is_causal is not None else False
+    if attn_mask is not None:
+        raise NotImplementedError("sageattn does not take an attention mask (use is_causal)")
+    if dropout_p:
+        raise NotImplementedError("sageattn is a forward without dropout (dropout_p must be 0)")
+    if scale is not None:
+        if sm_scale is not None and sm_scale != scale:
+            raise ValueError("give sm_scale or scale, not both")
+        sm_scale = scale
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must have the same dtype (deployment guide sec. 4.1)")
     if not (q.device == k.device == v.device) or q.device.type != "cuda":
         raise ValueError("q, k, v must be on the same GPU")
+    if q.dim() == 3 and k.dim() == 3 and v.dim() == 3 and tensor_layout == "HND":
+        res = sageattn(q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0), "HND", is_causal, sm_scale, return_lse,
+                       qk_quant_gran=qk_quant_gran, pv_accum_dtype=pv_accum_dtype, smooth_k=smooth_k,
+                       smooth_v=smooth_v, v_dtype=v_dtype, kv_splits=kv_splits)
+        return (res[0][0], res[1][0]) if return_lse else res[0]
     if kv_splits is not None and is_causal:
         raise NotImplementedError("kv_splits needs a non-causal call")
     qk, qv = sage_quant_qkv(q, k, v, tensor_layout=tensor_layout, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k,

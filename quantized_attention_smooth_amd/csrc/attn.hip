@@ -1464,6 +1464,12 @@ __global__ __launch_bounds__(kThreads) void qk_scores_kernel(AttnArgs a) {
     const int qt = blockIdx.x % nqt, bh = blockIdx.x / nqt, h = bh % a.Hq, b = bh / a.Hq;
     const int hk = h / (a.Hq / a.Hkv);
     const int qrow = qt * kDbgBQ + wave * 32 + n;
+    int Lq = a.Nq, Lk = a.Nk, qoff = 0;                 // varlen: this sequence's lengths (as the forward cuts them)
+    if (a.cu_q) {
+        qoff = a.cu_q[b];
+        Lq = min(max(a.cu_q[b + 1] - qoff, 0), a.Nq);
+        Lk = min(max(a.cu_k[b + 1] - a.cu_k[b], 0), a.Nk);
+    }
     const int64_t qhead = (int64_t)b * a.Hq + h;
     const int8_t* q8row = a.q8 + (qhead * a.nq_pad + qrow) * DP;
     // the same fragment code as the attention kernel, with both row blocks
@@ -1473,7 +1479,7 @@ __global__ __launch_bounds__(kThreads) void qk_scores_kernel(AttnArgs a) {
     for (int cb = 0; cb < DP / 32; ++cb)
         qf[0][cb] = qf[1][cb] = *reinterpret_cast<const v4i*>(q8row + cb * 32 + hh * 16);
     const int8_t* kbase = a.k8 + ((int64_t)b * a.Hkv + hk) * a.nk_pad * DP;
-    const int ntiles = (a.Nk + kBK - 1) / kBK;
+    const int ntiles = (Lk + kBK - 1) / kBK;
     unsigned long long s1 = 0, s2 = 0;
     constexpr int KCPR = DP / 16, K_LOADS = kBK * DP / (16 * kThreads);
     for (int t = 0; t < ntiles; ++t) {
@@ -1498,9 +1504,9 @@ __global__ __launch_bounds__(kThreads) void qk_scores_kernel(AttnArgs a) {
             for (int i = 0; i < 16; ++i) {
                 const int key = t * kBK + kb * 32 + 8 * (i >> 2) + 4 * hh + (i & 3);
                 const int S = acc[0][kb][i] - kAccBiasBits;
-                if (key < a.Nk) {
+                if (key < Lk) {
                     if (a.dbg_mode == 0) {
-                        if (qrow < a.Nq)
+                        if (qrow < Lq)
                             reinterpret_cast<int32_t*>(a.dbg)[(qhead * a.Nq + qrow) * a.Nk + key] = S;
                     } else {
                         s1 += (unsigned long long)(long long)S;
@@ -1512,8 +1518,9 @@ __global__ __launch_bounds__(kThreads) void qk_scores_kernel(AttnArgs a) {
     if (a.dbg_mode == 1) {
         s1 += __shfl_xor(s1, 32);
         s2 += __shfl_xor(s2, 32);
-        if (hh == 0 && qrow < a.Nq) {
-            unsigned long long* d = reinterpret_cast<unsigned long long*>(a.dbg) + (qhead * a.Nq + qrow) * 2;
+        if (hh == 0 && qrow < Lq) {
+            const int64_t row = a.cu_q ? (int64_t)h * a.total_q + qoff + qrow : qhead * a.Nq + qrow;
+            unsigned long long* d = reinterpret_cast<unsigned long long*>(a.dbg) + row * 2;
             d[0] = s1;
             d[1] = s2;
         }

@@ -23,9 +23,11 @@
 // Bit-exactness: a mean is fl32(fl64(exact sum) / N).  fp16 inputs are
 // summed as multiples of 2^-24 (every fp16 value is one): each thread adds
 // its 16 values in fp64, which is exact (|sum| < 2^44 units), and the
-// threads' and chunks' sums are combined as int64 (exact for N < 2^23).  bf16 inputs are summed in fp64, which is exact -- and therefore
-// independent of the summation order -- when a column's values span fewer
-// than 53 bits including log2(N).  The quantizer's fp32 operations are single
+// threads' and chunks' sums are combined as int64 (exact for N < 2^23).
+// bf16 inputs are summed in fp64, which is exact -- and therefore independent
+// of the summation order -- when the column's sum of |x| is below 2^53 times
+// the smallest bf16 ulp among its nonzero values (every partial sum is then a
+// multiple of that ulp that fp64 holds exactly).  The quantizer's fp32 operations are single
 // IEEE operations (no contraction), so codes and scales are reproducible.
 #include <type_traits>
 

@@ -464,6 +464,30 @@ int sage_debug_qk_scores(const sage_attn_params* p, int mode, void* scores, void
     return ok();
 }
 
+int sage_debug_qk_scores_varlen(const sage_attn_varlen_params* p, void* checksums, void* stream) {
+    if (!p) return fail(SAGE_EINVAL, "params is NULL");
+    if (p->base.struct_size < sizeof(sage_attn_varlen_params))
+        return fail(SAGE_EINVAL, "struct_size too small (pass sizeof(sage_attn_varlen_params))");
+    const sage_attn_params* b = &p->base;
+    if (int r = check_sizes(b->B, b->Hq, b->Hkv, b->Nq, b->Nk, b->d)) return r;
+    if (!b->q8 || !b->k8 || !checksums || !p->cu_seqlens_q || !p->cu_seqlens_k)
+        return fail(SAGE_EINVAL, "NULL pointer");
+    if (!aligned(b->q8, 16) || !aligned(b->k8, 16) || !aligned(checksums, 8) || !aligned(p->cu_seqlens_q, 4) ||
+        !aligned(p->cu_seqlens_k, 4))
+        return fail(SAGE_EINVAL, "misaligned pointer");
+    if (p->total_q < 1) return fail(SAGE_EINVAL, "total_q must be >= 1");
+    sage::AttnArgs a = attn_args(b);
+    a.cu_q = p->cu_seqlens_q;
+    a.cu_k = p->cu_seqlens_k;
+    a.total_q = p->total_q;
+    a.dbg = checksums;
+    a.dbg_mode = 1;
+    if (int r = hip_status(sage::launch_qk_scores(a, dp_of(b->d), reinterpret_cast<hipStream_t>(stream)),
+                           "varlen score checksum launch"))
+        return r;
+    return ok();
+}
+
 namespace {
 struct SplitPlan {
     int splits, split_len;

@@ -48,6 +48,20 @@ COS_EXACT = 0.999
 LSE_TOL_EMU = 1e-3
 
 
+def bf16_sum_exact_in_fp64(col: np.ndarray) -> bool:
+    """Whether fp64 sums bf16 values exactly in any order: every value is a
+    multiple of u, the smallest bf16 ulp among the nonzero values
+    (2^(floor(log2|x|) - 7), subnormals 2^-133), so is every partial sum, and
+    fp64 holds every multiple of u below 2^53 u; all partial sums are at most
+    sum |x|.  The library's bf16 means are bit-exact under this condition."""
+    x = np.abs(np.asarray(col, dtype=np.float64))
+    nz = x[x != 0]
+    if nz.size == 0:
+        return True
+    u = np.exp2(np.maximum(np.floor(np.log2(nz)), -126.0) - 7.0).min()
+    return float(x.sum()) < 2.0 ** 53 * u
+
+
 def out_ulp(ref: np.ndarray, dtype: str) -> np.ndarray:
     mbits, emin = (7, -126) if dtype == "bf16" else (10, -14)
     a = np.maximum(np.abs(ref), 2.0 ** emin)

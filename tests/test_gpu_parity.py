@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 import quantized_attention_smooth_amd as sage
-from parity_utils import Case, cosine, sample_rows, scale_down
+from parity_utils import Case, bf16_sum_exact_in_fp64, cosine, sample_rows, scale_down
 
 pytestmark = pytest.mark.gpu
 
@@ -88,6 +88,29 @@ def test_workload_score_checksums(name, big_cases):
             np.testing.assert_array_equal(got[b, h, rows, 1], s2)
 
 
+def test_varlen_score_checksums(big_cases):
+    """The varlen batch's int32 scores, row checksums per sequence, against
+    the oracle's integer codes."""
+    c = _big("varlen16_h16", big_cases)
+    if not hasattr(c, "ref"):
+        c.run_oracle(attention=False)
+    cu = c.inp["cu_seqlens"]
+    got = sage.sage_debug_qk_scores(c.qk, checksums=True, cu_seqlens_q=cu.cuda(), cu_seqlens_k=cu.cuda(),
+                                    total_q=int(cu[-1])).cpu().numpy().view(np.uint64)
+    grp = c.w.Hq // c.w.Hkv
+    for b in range(c.n_seq()):
+        nq = c.ref["q8"][b].shape[1]
+        rows = sample_rows(c.w.seed, 16)(b, nq)
+        for h in range(c.w.Hq):
+            q8 = c.ref["q8"][b][h][rows].astype(np.float64)
+            k8 = c.ref["k8"][b][h // grp].astype(np.float64)
+            S = (q8 @ k8.T).astype(np.int64)
+            s1 = S.sum(axis=1).astype(np.uint64)
+            s2 = (S * (np.arange(k8.shape[0], dtype=np.int64) + 1)[None, :]).sum(axis=1).astype(np.uint64)
+            np.testing.assert_array_equal(got[h, c.cu_np[b] + rows, 0], s1)
+            np.testing.assert_array_equal(got[h, c.cu_np[b] + rows, 1], s2)
+
+
 @pytest.mark.parametrize("name", BIG)
 def test_workload_outputs(name, big_cases):
     c = _big(name, big_cases)
@@ -153,6 +176,38 @@ def test_varlen_small_matches_oracle(causal):
     c = Case(w, inp).run_gpu(return_lse=True).run_oracle(exact=True)
     c.check_quantized_bitexact()
     c.check_outputs(lse=True)
+
+
+# ------------------------------------------------------------------ bf16 means over wide magnitude spans
+@pytest.mark.parametrize("n, e_lo, e_hi, within", [(8, -20, 21, True), (4096, -25, 20, False)])
+def test_bf16_means_wide_span(n, e_lo, e_hi, within):
+    """bf16 K and V whose columns span 41 (N = 8) or 45 (N = 4096) binades:
+    sign * (1 + m/128) * 2^e with e uniform in [e_lo, e_hi).  The K and V means
+    (smooth_k, smooth_v) must equal the oracle's correctly rounded means
+    (math.fsum) bit for bit.  The first case satisfies the exactness condition
+    the library states for bf16 sums (every partial sum exact in fp64); the
+    second lies beyond it and is checked as it comes out on this seed."""
+    _announce(f"bf16 means, N={n}, exponents [{e_lo}, {e_hi}), seed {70 + n}")
+    rng = np.random.default_rng(70 + n)
+    shape = (1, 2, n, 64)
+
+    def wide():
+        mant = 1.0 + rng.integers(0, 128, size=shape) / 128.0
+        x = np.where(rng.random(shape) < 0.5, -1.0, 1.0) * mant * np.exp2(rng.integers(e_lo, e_hi, size=shape))
+        t = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16)
+        assert np.array_equal(t.float().numpy(), x.astype(np.float32))      # exactly bf16 values
+        return t, x.astype(np.float32)
+
+    k, kx = wide()
+    v, vx = wide()
+    q = torch.randn(shape, generator=torch.Generator().manual_seed(70)).bfloat16()
+    cols = [kx[0, h, :, c] for h in range(2) for c in range(64)] + [vx[0, h, :, c] for h in range(2) for c in range(64)]
+    assert all(bf16_sum_exact_in_fp64(c) for c in cols) == within
+    qk, qv = sage.sage_quant_qkv(q.cuda(), k.cuda(), v.cuda(), smooth_k=True, smooth_v=True, v_dtype="fp16")
+    torch.cuda.synchronize()
+    for h in range(2):
+        np.testing.assert_array_equal(qk.k_mean[0, h].cpu().numpy(), oracle.exact_mean(kx[0, h]))
+        np.testing.assert_array_equal(qv.v_mean[0, h].cpu().numpy(), oracle.exact_mean(vx[0, h]))
 
 
 # ------------------------------------------------------------------ structural invariants (bit-exact)

@@ -1,5 +1,6 @@
 """Host-side logic of the Python binding that needs no GPU: argument checks
 that raise before any library call, and the split-KV range-count plan."""
+import numpy as np
 import pytest
 import torch
 
@@ -103,3 +104,45 @@ def test_attn_varlen_and_merge_reject_wrong_out():
     for out in (torch.empty((1, 2, 10, 32), dtype=torch.float16), torch.empty((1, 2, 10, 64), dtype=torch.bfloat16)):
         with pytest.raises(ValueError):
             sage.sage_merge_states(parts, lse, out=out)
+
+
+# ---------------------------------------------------------------- SDPA call convention
+@pytest.mark.parametrize("kw", [dict(attn_mask=torch.zeros(1)), dict(dropout_p=0.1)])
+def test_sdpa_convention_unsupported_raises_not_implemented(kw):
+    """A mask or dropout is refused with NotImplementedError (before any
+    library call), which an SDPA caller can catch to fall back."""
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.float16)
+    with pytest.raises(NotImplementedError):
+        sage.sageattn(q, q, q, **kw)
+
+
+def test_sdpa_positional_mask_is_recognised():
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.float16)
+    with pytest.raises(NotImplementedError):
+        sage.sageattn(q, q, q, torch.zeros(8, 8))          # SDPA order: attn_mask fourth
+    with pytest.raises(NotImplementedError):
+        sage.sageattn(q, q, q, None, 0.5)                  # dropout_p fifth
+    with pytest.raises(ValueError):                        # supported call, but CPU tensors
+        sage.sageattn(q, q, q, None, 0.0, True, 0.1)
+
+
+# ---------------------------------------------------------------- bf16 mean exactness condition
+def test_bf16_sum_exactness_condition():
+    from parity_utils import bf16_sum_exact_in_fp64 as ok
+    assert ok(np.array([1.0, 2.0 ** -45]))                 # u = 2^-52: 1 < 2^53 u = 2
+    assert not ok(np.array([1.0, 2.0 ** -46]))             # u = 2^-53: 1 + 2^-46 >= 2^53 u = 1
+    assert ok(np.zeros(5)) and ok(np.array([0.0, -3.0]))
+    assert ok(np.array([2.0 ** -133, 2.0 ** -120]))        # subnormal ulp 2^-133
+    # the condition is what it claims: fp64 sums of such columns are exact in any order
+    import math
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        e = rng.integers(-20, 18, 64)
+        x = rng.choice([-1.0, 1.0], 64) * (1 + rng.integers(0, 128, 64) / 128) * np.exp2(e)
+        if ok(x):
+            exact = math.fsum(x.tolist())
+            for order in (x, x[::-1], rng.permutation(x)):
+                s = 0.0
+                for v in order:
+                    s += float(v)
+                assert s == exact
