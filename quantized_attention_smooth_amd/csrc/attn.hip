@@ -65,6 +65,20 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 typedef float v4f __attribute__((ext_vector_type(4)));
 
+// A value the whole wavefront shares, moved to scalar registers.  Head and
+// batch indices come out of integer divisions, which the compiler evaluates
+// with vector instructions; buffer resources built from such values would
+// stay in vector registers and every buffer load would need a loop over the
+// lanes' distinct resources.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+template <class T>
+__device__ __forceinline__ T* uniform(T* p) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
 template <int DP, int PV, int NW = 4, int NR = NW>
 struct AttnCfg {
     static constexpr int NCB = DP / 32;                 // 32-channel blocks
@@ -1191,9 +1205,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const float cq = ((qscale * a.sm_scale) * kLog2e) * kAccScale;   // times 2^26, exact
 
     const int64_t khead = (int64_t)b * a.Hkv + hk;
-    const int8_t* kbase = a.k8 + khead * a.nk_pad * DP + (int64_t)kb0 * DP;
-    const float* ksbase = a.ks + khead * (a.nk_pad >> a.gk_shift) + (kb0 >> a.gk_shift);
-    const uint8_t* vbase = reinterpret_cast<const uint8_t*>(a.vt) + khead * DP * a.nk_pad + kb0;
+    const int8_t* kbase = uniform(a.k8 + khead * a.nk_pad * DP + (int64_t)kb0 * DP);
+    const float* ksbase = uniform(a.ks + khead * (a.nk_pad >> a.gk_shift) + (kb0 >> a.gk_shift));
+    const uint8_t* vbase = uniform(reinterpret_cast<const uint8_t*>(a.vt) + khead * DP * a.nk_pad + kb0);
     const int64_t vrow_stride = a.nk_pad;
     const bool ks16 = a.gk_shift == 4;
 
