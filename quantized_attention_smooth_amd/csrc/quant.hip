@@ -55,6 +55,34 @@ __device__ __forceinline__ void load8(const uint16_t* row, int c0, int d, float 
     }
 }
 
+// The 8 raw 16-bit values of channels c0 .. c0+7 of a row, zeros past d.
+// The row must exist: every access stays inside it (channels past d read
+// channel 0 or d - 1 and are then replaced by zeros), and there is no branch,
+// so that a thread's loads of several rows are all in flight together.
+template <bool VEC>
+__device__ __forceinline__ uint4 load_raw8(const uint16_t* row, int c0, int d) {
+    if constexpr (VEC) {
+        const bool in = c0 < d;
+        const uint4 r = *reinterpret_cast<const uint4*>(row + (in ? c0 : 0));
+        return in ? r : make_uint4(0u, 0u, 0u, 0u);
+    } else {
+        uint16_t e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint16_t x = row[min(c0 + j, d - 1)];
+            e[j] = c0 + j < d ? x : (uint16_t)0;
+        }
+        return make_uint4(e[0] | ((uint32_t)e[1] << 16), e[2] | ((uint32_t)e[3] << 16), e[4] | ((uint32_t)e[5] << 16),
+                          e[6] | ((uint32_t)e[7] << 16));
+    }
+}
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const uint4& raw, float v[8]) {
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = Half<BF16>::to_f(e[j]);
+}
+
 // Workgroup id -> (unit, head, sequence), the head varying fastest: with
 // token-major layouts (NHD, packed varlen) the rows of all heads of a token
 // are adjacent, so workgroups that run together read adjacent memory.
@@ -116,64 +144,139 @@ __device__ __forceinline__ void finish_stats(typename std::conditional<BF16, dou
 }
 
 // Statistics of one kStatsChunk-token chunk of one (sequence, head): per-channel sum
-// (exact, see above) and, for FP8 V, min and max.
-template <bool BF16, int DP, bool VEC>
-__device__ __forceinline__ void stats_body(const StatsArgs& a, int chunk, int h, int b) {
+// (exact, see above) and, with MINMAX (FP8 V), min and max.  fp16 minima and
+// maxima are taken on the fp16 values themselves, two per instruction (exact:
+// the conversion to fp32 is exact and monotonic).
+template <bool BF16, int DP, bool VEC, bool MINMAX>
+__device__ __forceinline__ void stats_body(const StatsArgs& a, int chunk, int h, int b,
+                                           typename std::conditional<BF16, double, long long>::type* s_sum,
+                                           float* s_mn, float* s_mx) {
     constexpr int TPR = DP / 8;
     constexpr int RPP = kThreads / TPR;
     constexpr int ITER = kStatsChunk / RPP;
     using Acc = typename std::conditional<BF16, double, long long>::type;
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     int n0, N;
     seq_range(a.cu, b, a.N, n0, N);
     const int tid = threadIdx.x, cg = tid % TPR, rr = tid / TPR;
     const int t_lo = chunk * a.chunk_len, t_hi = min(N, t_lo + a.chunk_len);
     double sum[8];
     float mn[8], mx[8];
+    h2 mn2[4], mx2[4];
 #pragma unroll
     for (int j = 0; j < 8; ++j) { sum[j] = 0.0; mn[j] = INFINITY; mx[j] = -INFINITY; }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        mn2[q] = h2{(_Float16)INFINITY, (_Float16)INFINITY};
+        mx2[q] = h2{(_Float16)-INFINITY, (_Float16)-INFINITY};
+    }
+    // The ITER rows of a step are loaded raw first (independent loads, all in
+    // flight together), then converted and summed in row order.
     for (int t0 = t_lo; t0 < t_hi; t0 += kStatsChunk) {
-        // the ITER loads of a step are independent: unrolled, they are in flight together
+        uint4 raw[ITER];
+#pragma unroll
+        for (int it = 0; it < ITER; ++it) {             // rows past the chunk reread its last row (ignored below)
+            const int n = min(t0 + it * RPP + rr, t_hi - 1);
+            raw[it] = load_raw8<VEC>(row_ptr(a.x, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d);
+        }
 #pragma unroll
         for (int it = 0; it < ITER; ++it) {
-            const int n = t0 + it * RPP + rr;
-            if (n < t_hi) {
+            if (t0 + it * RPP + rr < t_hi) {
                 float v[8];
-                load8<BF16, VEC>(row_ptr(a.x, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d, v);
+                unpack8<BF16>(raw[it], v);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    sum[j] += (double)v[j];
-                    mn[j] = fminf(mn[j], v[j]);
-                    mx[j] = fmaxf(mx[j], v[j]);
+                for (int j = 0; j < 8; ++j) sum[j] += (double)v[j];
+                if constexpr (MINMAX && BF16) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        mn[j] = fminf(mn[j], v[j]);
+                        mx[j] = fmaxf(mx[j], v[j]);
+                    }
+                } else if constexpr (MINMAX) {
+                    const uint32_t w[4] = {raw[it].x, raw[it].y, raw[it].z, raw[it].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const h2 x = __builtin_bit_cast(h2, w[q]);
+                        mn2[q] = __builtin_elementwise_min(mn2[q], x);
+                        mx2[q] = __builtin_elementwise_max(mx2[q], x);
+                    }
                 }
+            }
+            __builtin_amdgcn_sched_barrier(0);          // one row at a time: few conversions live at once
+        }
+    }
+    if constexpr (MINMAX && !BF16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            mn[j] = (float)mn2[j >> 1][j & 1];
+            mx[j] = (float)mx2[j >> 1][j & 1];
+        }
+    }
+    // Reduce over the RPP threads that share a channel group: first the
+    // threads of one wavefront (lanes 16 apart when TPR is 16), by lane
+    // exchange, then the wavefronts, through LDS.  The partial sums are exact
+    // (integers for fp16, exact fp64 sums for bf16), so the order is free.
+    constexpr int LPW = 64 / TPR;                       // threads of a channel group per wavefront
+    constexpr int NWV = kThreads / 64;
+    Acc acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if constexpr (BF16) acc[j] = sum[j];
+        else acc[j] = (long long)(sum[j] * 16777216.0);   // an integer below 2^53: exact
+    }
+#pragma unroll
+    for (int off = TPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            acc[j] += __shfl_xor(acc[j], off);
+            if constexpr (MINMAX) {
+                mn[j] = fminf(mn[j], __shfl_xor(mn[j], off));
+                mx[j] = fmaxf(mx[j], __shfl_xor(mx[j], off));
             }
         }
     }
-    // reduce over the RPP threads that share a channel group, in a fixed order
-    __shared__ Acc s_sum[RPP][DP];
-    __shared__ float s_mn[RPP][DP], s_mx[RPP][DP];
+    static_assert(LPW * TPR == 64, "whole channel groups per wavefront");
+    const int lane = tid & 63, wv = tid >> 6;
+    if (lane < TPR) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        if constexpr (BF16) s_sum[rr][cg * 8 + j] = sum[j];
-        else s_sum[rr][cg * 8 + j] = (long long)(sum[j] * 16777216.0);   // an integer below 2^53: exact
-        s_mn[rr][cg * 8 + j] = mn[j];
-        s_mx[rr][cg * 8 + j] = mx[j];
+        for (int j = 0; j < 8; ++j) {
+            s_sum[wv * DP + cg * 8 + j] = acc[j];
+            if constexpr (MINMAX) {
+                s_mn[wv * DP + cg * 8 + j] = mn[j];
+                s_mx[wv * DP + cg * 8 + j] = mx[j];
+            }
+        }
     }
     __syncthreads();
     if (tid < DP) {
         Acc s = 0;
         float lo = INFINITY, hi = -INFINITY;
-        for (int r = 0; r < RPP; ++r) {
-            s += s_sum[r][tid];
-            lo = fminf(lo, s_mn[r][tid]);
-            hi = fmaxf(hi, s_mx[r][tid]);
+#pragma unroll
+        for (int r = 0; r < NWV; ++r) {
+            s += s_sum[r * DP + tid];
+            if constexpr (MINMAX) {
+                lo = fminf(lo, s_mn[r * DP + tid]);
+                hi = fmaxf(hi, s_mx[r * DP + tid]);
+            }
         }
         const int64_t o = (((int64_t)b * a.H + h) * a.chunks + chunk) * DP + tid;
         reinterpret_cast<Acc*>(a.part_sum)[o] = s;
-        if (a.want_minmax) {
+        if constexpr (MINMAX) {
             a.part_min[o] = lo;
             a.part_max[o] = hi;
         }
     }
+}
+
+// The statistics workgroup body with min and max when the call asks for them.
+// (one LDS area serves both).
+template <bool BF16, int DP, bool VEC>
+__device__ __forceinline__ void stats_any(const StatsArgs& a, int chunk, int h, int b) {
+    using Acc = typename std::conditional<BF16, double, long long>::type;
+    __shared__ Acc s_sum[kThreads / 64 * DP];
+    __shared__ float s_mn[kThreads / 64 * DP], s_mx[kThreads / 64 * DP];
+    if (a.want_minmax) stats_body<BF16, DP, VEC, true>(a, chunk, h, b, s_sum, s_mn, s_mx);
+    else stats_body<BF16, DP, VEC, false>(a, chunk, h, b, s_sum, s_mn, s_mx);
 }
 
 // Channel statistics of one (sequence, head) for a tile workgroup: threads
@@ -195,14 +298,35 @@ __device__ __forceinline__ void tile_stats(const StatsArgs& a, int tile, int h, 
     const int64_t base = ((int64_t)b * a.H + h) * a.chunks * a.dp + c;
     Acc sum = 0;
     float lo = INFINITY, hi = -INFINITY;
+    // Batches of up to 8 slots per thread: every slot of a batch loads
+    // (slots past the last chunk reread chunk 0 and are ignored), so that a
+    // batch's loads are in flight together; a batch runs only if some chunk
+    // falls in it (a uniform branch).
+    constexpr int NB = 8 < PER ? 8 : PER;
+    static_assert(PER % NB == 0, "whole batches");
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int k = part + TPC * i;
-        if (k < a.chunks) {
-            sum += reinterpret_cast<const Acc*>(a.part_sum)[base + (int64_t)k * a.dp];
+    for (int i0 = 0; i0 < PER; i0 += NB) {
+        if (TPC * i0 >= a.chunks) break;
+        Acc ps[NB];
+        float pl[NB], ph[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int k = part + TPC * (i0 + i);
+            const int64_t o = base + (int64_t)(k < a.chunks ? k : 0) * a.dp;
+            ps[i] = reinterpret_cast<const Acc*>(a.part_sum)[o];
             if (a.want_minmax) {
-                lo = fminf(lo, a.part_min[base + (int64_t)k * a.dp]);
-                hi = fmaxf(hi, a.part_max[base + (int64_t)k * a.dp]);
+                pl[i] = a.part_min[o];
+                ph[i] = a.part_max[o];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            if (part + TPC * (i0 + i) < a.chunks) {
+                sum += ps[i];
+                if (a.want_minmax) {
+                    lo = fminf(lo, pl[i]);
+                    hi = fmaxf(hi, ph[i]);
+                }
             }
         }
     }
@@ -246,16 +370,23 @@ __device__ __forceinline__ void quant_rows_body(const QuantRowsArgs& a, int tile
     const int tid = threadIdx.x, cg = tid % TPR, rr = tid / TPR;
     const int row0 = tile * kPad;
     __shared__ float rmax[kPad];
+    // all row loads first (rows past the sequence reread its last row), then
+    // the conversion; rows past the sequence become zeros
+    uint4 raw[PASSES];
+    if (N > 0) {
+#pragma unroll
+        for (int p = 0; p < PASSES; ++p) {
+            const int n = min(row0 + p * RPP + rr, N - 1);
+            raw[p] = load_raw8<VEC>(row_ptr(a.x, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d);
+        }
+    }
     float vals[PASSES][8];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
-        const int n = row0 + p * RPP + rr;
-        if (n < N) {
-            load8<BF16, VEC>(row_ptr(a.x, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d, vals[p]);
-        } else {
+        const bool in = row0 + p * RPP + rr < N;
+        unpack8<BF16>(N > 0 ? raw[p] : make_uint4(0u, 0u, 0u, 0u), vals[p]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) vals[p][j] = 0.f;
-        }
+        for (int j = 0; j < 8; ++j) vals[p][j] = in ? vals[p][j] : 0.f;
     }
     __shared__ float s_mu[DP];
     if (ks) tile_stats<BF16, DP>(*ks, tile, h, b, s_mu, nullptr);
@@ -319,7 +450,7 @@ __global__ __launch_bounds__(kThreads) void qk_pass1_kernel(QuantRowsArgs q, Qua
     bid -= nq_blocks;
     if (smooth) {
         const UnitHeadB u = unit_head_b(bid, ks.chunks, ks.H);
-        stats_body<BF16, DP, VEC>(ks, u.unit, u.h, u.b);
+        stats_any<BF16, DP, VEC>(ks, u.unit, u.h, u.b);
     } else {
         const int tiles = k.npad / kPad;
         const UnitHeadB u = unit_head_b(bid, tiles, k.H);
@@ -341,7 +472,7 @@ template <bool BF16, int DP, bool VEC>
 __global__ __launch_bounds__(kThreads) void v_stats_kernel(StatsArgs vs) {
     const int bid = blockIdx.x;
     const UnitHeadB u = unit_head_b(bid, vs.chunks, vs.H);
-    stats_body<BF16, DP, VEC>(vs, u.unit, u.h, u.b);
+    stats_any<BF16, DP, VEC>(vs, u.unit, u.h, u.b);
 }
 
 // V -> V^T codes for one 128-key tile.  With statistics, the workgroup
@@ -366,16 +497,21 @@ __device__ __forceinline__ void quant_v_body(const QuantVArgs& a, const StatsArg
     const int row0 = tile * kPad;
     __shared__ __attribute__((aligned(16))) uint8_t sv[DP * ROWB];
     const int64_t hb = ((int64_t)b * a.H + h) * DP;
+    uint4 raw[KPG];
+    if (N > 0) {
+#pragma unroll
+        for (int p = 0; p < KPG; ++p) {                 // keys past the sequence reread its last key
+            const int n = min(row0 + g * KPG + p, N - 1);
+            raw[p] = load_raw8<VEC>(row_ptr(a.v, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d);
+        }
+    }
     float v[KPG][8];
 #pragma unroll
     for (int p = 0; p < KPG; ++p) {
-        const int n = row0 + g * KPG + p;
-        if (n < N) {
-            load8<BF16, VEC>(row_ptr(a.v, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d, v[p]);
-        } else {
+        const bool in = row0 + g * KPG + p < N;
+        unpack8<BF16>(N > 0 ? raw[p] : make_uint4(0u, 0u, 0u, 0u), v[p]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[p][j] = 0.f;
-        }
+        for (int j = 0; j < 8; ++j) v[p][j] = in ? v[p][j] : 0.f;
     }
     __shared__ float s_mu[DP], s_inv[DP];
     if (have_stats) tile_stats<BF16, DP>(vs, tile, h, b, s_mu, s_inv);
@@ -444,25 +580,19 @@ __global__ __launch_bounds__(kThreads) void quant_v_kernel(QuantVArgs a, StatsAr
 
 // ---------------------------------------------------------------------------
 // Q, K and V in two launches (the same workgroup bodies as above).
-// Pass 1: Q tiles; K statistics chunks (smooth_k) or K tiles; V statistics
-// chunks (when V needs them).  Pass 2: K tiles minus their means (smooth_k);
-// V tiles.
+// Pass 1: K statistics chunks (smooth_k) or K tiles; V statistics chunks
+// (when V needs them); Q tiles -- in that order of workgroup ids, so that the
+// statistics workgroups, whose reduction follows their loads, start first.
+// Pass 2: K tiles minus their means (smooth_k); V tiles.
 template <bool BF16, int DP, bool VEC>
 __global__ __launch_bounds__(kThreads) void qkv_pass1_kernel(QuantRowsArgs q, QuantRowsArgs k, StatsArgs ks,
                                                              StatsArgs vs, int nq_blocks, int nk_blocks,
                                                              int smooth_k) {
     int bid = blockIdx.x;
-    if (bid < nq_blocks) {
-        const int tiles = q.npad / kPad;
-        const UnitHeadB u = unit_head_b(bid, tiles, q.H);
-        quant_rows_body<BF16, DP, VEC>(q, u.unit, u.h, u.b, nullptr);
-        return;
-    }
-    bid -= nq_blocks;
     if (bid < nk_blocks) {
         if (smooth_k) {
             const UnitHeadB u = unit_head_b(bid, ks.chunks, ks.H);
-            stats_body<BF16, DP, VEC>(ks, u.unit, u.h, u.b);
+            stats_any<BF16, DP, VEC>(ks, u.unit, u.h, u.b);
         } else {
             const int tiles = k.npad / kPad;
             const UnitHeadB u = unit_head_b(bid, tiles, k.H);
@@ -471,8 +601,16 @@ __global__ __launch_bounds__(kThreads) void qkv_pass1_kernel(QuantRowsArgs q, Qu
         return;
     }
     bid -= nk_blocks;
-    const UnitHeadB u = unit_head_b(bid, vs.chunks, vs.H);
-    stats_body<BF16, DP, VEC>(vs, u.unit, u.h, u.b);
+    const int nv_blocks = (int)gridDim.x - nk_blocks - nq_blocks;
+    if (bid < nv_blocks) {
+        const UnitHeadB u = unit_head_b(bid, vs.chunks, vs.H);
+        stats_any<BF16, DP, VEC>(vs, u.unit, u.h, u.b);
+        return;
+    }
+    bid -= nv_blocks;
+    const int tiles = q.npad / kPad;
+    const UnitHeadB u = unit_head_b(bid, tiles, q.H);
+    quant_rows_body<BF16, DP, VEC>(q, u.unit, u.h, u.b, nullptr);
 }
 
 template <bool BF16, int DP, bool FP8, bool VEC>

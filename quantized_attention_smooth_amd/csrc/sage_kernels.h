@@ -125,7 +125,7 @@ hipError_t launch_merge(const MergeArgs& a, bool bf16, bool vec, hipStream_t s);
 // Statistics chunks: kStatsChunk tokens, or longer for long sequences so
 // that a (b, h) has at most kMaxChunks partials (every tile workgroup of the
 // quantize pass reduces all partials of its (b, h)).
-constexpr int kStatsChunk = 128;
+constexpr int kStatsChunk = 256;
 // Query heads sharing a K/V head are packed into one workgroup's rows when
 // each has at most this many queries.
 constexpr int kPackMaxNq = 128;

@@ -214,7 +214,7 @@ def test_workspace_size(lib):
     assert lib.sage_quant_workspace_size(0, 1, 1, 64) == 0
     assert lib.sage_quant_workspace_size(1, 1, 1, 129) == 0
     # 8-byte sums + fp32 min/max per (b, h, chunk, channel); about 256 chunks over all heads, 8 to 32 per head,
-    # each a multiple of 128 tokens
+    # each a multiple of 256 tokens
     n = lib.sage_quant_workspace_size(2, 8, 4096, 128)
     cells = 2 * 8 * 16 * 128
     assert n >= cells * 16
