@@ -414,24 +414,35 @@ __device__ __forceinline__ void quant_rows_body(const QuantRowsArgs& a, int tile
         if (tid < kPad && (tid & (2 * s - 1)) == 0) rmax[tid] = fmaxf(rmax[tid], rmax[tid + s]);
         __syncthreads();
     }
+    // one thread per group: the scale and its inverse (each a single
+    // correctly rounded division)
+    __shared__ float rinv[kPad];
+    if (tid < kPad && (tid & (G - 1)) == 0) {
+        const float amax = rmax[tid];
+        rinv[tid] = amax > 0.f ? 127.0f / amax : 0.f;
+        a.scale[((int64_t)b * a.H + h) * (a.npad >> a.group_shift) + ((row0 + tid) >> a.group_shift)] =
+            amax > 0.f ? amax / 127.0f : 0.f;
+    }
+    __syncthreads();
+    // code = rint(fl(x * inv)): adding 1.5 * 2^23 rounds fl(x * inv) to an
+    // integer (ties to even) held in the low bits of the sum, whose low byte
+    // is the code in two's complement.  No clamp is needed: with
+    // inv = fl(127 / amax) and |x| <= amax, |fl(x * inv)| < 127.5.
+    constexpr float kRound = 12582912.0f;
     int8_t* obase = a.out + (((int64_t)b * a.H + h) * a.npad + row0) * DP;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const int r = p * RPP + rr;
-        const float amax = rmax[r & ~(G - 1)];
-        const float inv = amax > 0.f ? 127.0f / amax : 0.f;
-        uint32_t w[2] = {0u, 0u};
+        const float inv = rinv[r & ~(G - 1)];
+        uint32_t c[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            float t = vals[p][j] * inv;
-            t = __builtin_rintf(t);
-            t = fminf(fmaxf(t, -127.f), 127.f);
-            w[j >> 2] |= ((uint32_t)((int)t & 0xff)) << (8 * (j & 3));
-        }
-        *reinterpret_cast<uint2*>(obase + (int64_t)r * DP + cg * 8) = make_uint2(w[0], w[1]);
-        if (cg == 0 && (r & (G - 1)) == 0)
-            a.scale[((int64_t)b * a.H + h) * (a.npad >> a.group_shift) + ((row0 + r) >> a.group_shift)] =
-                amax > 0.f ? amax / 127.0f : 0.f;
+        for (int j = 0; j < 8; ++j) c[j] = __float_as_uint(vals[p][j] * inv + kRound);
+        // low bytes of c[0..3] and c[4..7] into one word each
+        const uint32_t w0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u), 0x05040100u);
+        const uint32_t w1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(c[7], c[6], 0x0c0c0400u),
+                                                  __builtin_amdgcn_perm(c[5], c[4], 0x0c0c0400u), 0x05040100u);
+        *reinterpret_cast<uint2*>(obase + (int64_t)r * DP + cg * 8) = make_uint2(w0, w1);
     }
 }
 
