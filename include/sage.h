@@ -41,6 +41,9 @@
  * consumed by sage_attn_fwd / sage_attn_varlen_fwd):
  *   Nq_pad = round_up(Nq, 128), Nk_pad = round_up(Nk, 128); for varlen calls
  *   Nq, Nk are the maximum sequence lengths and B the number of sequences.
+ *   Rows past a sequence's length and inside its last 128-row tile hold
+ *   zeros; for varlen calls the tiles after that one (and their scale
+ *   groups) are left unwritten -- no call reads them.
  *   q8      int8   [B][Hq ][Nq_pad][Dp]   rows >= Nq (per sequence) are 0
  *   q_scale float  [B][Hq ][Nq_pad / Gq]  Gq = 128 / 32 / 1 for
  *                                          per_block / per_warp / per_thread

@@ -369,6 +369,8 @@ __device__ __forceinline__ void quant_rows_body(const QuantRowsArgs& a, int tile
     seq_range(a.cu, b, a.N, n0, N);
     const int tid = threadIdx.x, cg = tid % TPR, rr = tid / TPR;
     const int row0 = tile * kPad;
+    // a varlen sequence's tiles past its end are never read: not written
+    if (a.cu && row0 >= N) return;
     __shared__ float rmax[kPad];
     // all row loads first (rows past the sequence reread its last row), then
     // the conversion; rows past the sequence become zeros
@@ -506,6 +508,7 @@ __device__ __forceinline__ void quant_v_body(const QuantVArgs& a, const StatsArg
     seq_range(a.cu, b, a.N, n0, N);
     const int tid = threadIdx.x, cg = tid % TPR, g = tid / TPR;
     const int row0 = tile * kPad;
+    if (a.cu && row0 >= N) return;                      // (as for the row tiles)
     __shared__ __attribute__((aligned(16))) uint8_t sv[DP * ROWB];
     const int64_t hb = ((int64_t)b * a.H + h) * DP;
     uint4 raw[KPG];

@@ -103,6 +103,34 @@ def v_unpermute(vt: np.ndarray, n: int) -> np.ndarray:
     return np.swapaxes(vt[..., pos], -1, -2)
 
 
+def written_quant_outputs(qk, qv, lens=None) -> dict:
+    """The quantize outputs as a dict of tensors, with, for each varlen
+    sequence (lens given), the 128-row tiles after its last one -- which the
+    quantizer leaves unwritten -- set to zero, so that two calls' outputs can
+    be compared whole."""
+    out = {}
+    for obj, names in ((qk, ("q8", "q_scale", "k8", "k_scale", "k_mean")), (qv, ("vt", "v_scale", "v_mean"))):
+        for f in names:
+            x = getattr(obj, f)
+            if x is None:
+                out[f] = None
+                continue
+            x = x.clone()
+            if lens is not None and f in ("q8", "k8", "q_scale", "k_scale", "vt"):
+                axis = 3 if f == "vt" else 2
+                rows = x.shape[axis] if f in ("q8", "k8", "vt") else None
+                for b, n in enumerate(lens):
+                    end = -(-int(n) // 128) * 128
+                    if f in ("q_scale", "k_scale"):
+                        npad = (qk.q8 if f == "q_scale" else qk.k8).shape[2]
+                        end = end * x.shape[axis] // npad
+                    elif end > rows:
+                        end = rows
+                    x[b].narrow(axis - 1, end, x.shape[axis] - end).zero_()
+            out[f] = x
+    return out
+
+
 def sample_rows(seed: int, per: int):
     """rows(b, n): the first and last rows, rows around 64/128-row tile edges,
     and a seeded random sample."""
@@ -198,15 +226,19 @@ class Case:
         vt = (vt.numpy() if self.v_dtype == "fp8" else vt.float().numpy())
         vs = None if self.qv.v_scale is None else self.qv.v_scale.cpu().numpy()
         vm = None if self.qv.v_mean is None else self.qv.v_mean.cpu().numpy()
+        # padding rows are zero up to the end of the sequence's last 128-row
+        # tile; for varlen calls the tiles after it are left unwritten
+        tile_end = (lambda n, total: -(-n // 128) * 128) if w.varlen else (lambda n, total: total)
         for b in range(self.n_seq()):
             nq = self.ref["q8"][b].shape[1]
             nk = self.ref["k8"][b].shape[1]
+            eq, ek = tile_end(nq, q8.shape[2]), tile_end(nk, k8.shape[2])
             np.testing.assert_array_equal(q8[b][:, :nq], self.ref["q8"][b], err_msg=f"q8 seq {b}")
-            assert not q8[b][:, nq:].any(), "padding rows of q8 must be zero"
+            assert not q8[b][:, nq:eq].any(), "padding rows of q8 must be zero"
             ngq = -(-nq // gq)
             np.testing.assert_array_equal(qs[b][:, :ngq], self.ref["q_scale"][b], err_msg=f"q_scale seq {b}")
             np.testing.assert_array_equal(k8[b][:, :nk], self.ref["k8"][b], err_msg=f"k8 seq {b}")
-            assert not k8[b][:, nk:].any()
+            assert not k8[b][:, nk:ek].any()
             ngk = -(-nk // gk)
             np.testing.assert_array_equal(ks[b][:, :ngk], self.ref["k_scale"][b], err_msg=f"k_scale seq {b}")
             if w.smooth_k:
@@ -218,7 +250,7 @@ class Case:
                 np.testing.assert_array_equal(vs[b], self.ref["v_scale"][b], err_msg=f"v_scale seq {b}")
             else:
                 np.testing.assert_array_equal(vb[:, :nk], self.ref["v16"][b], err_msg=f"v16 seq {b}")
-            assert not vb[:, nk:].any(), "padding keys of V must be zero"
+            assert not vb[:, nk:ek].any(), "padding keys of V must be zero"
             if w.smooth_v:
                 np.testing.assert_array_equal(vm[b], self.ref["v_mean"][b], err_msg=f"v_mean seq {b}")
 

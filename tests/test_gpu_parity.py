@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 import quantized_attention_smooth_amd as sage
-from parity_utils import Case, bf16_sum_exact_in_fp64, cosine, sample_rows, scale_down
+from parity_utils import Case, bf16_sum_exact_in_fp64, cosine, sample_rows, scale_down, written_quant_outputs
 
 pytestmark = pytest.mark.gpu
 
@@ -385,16 +385,12 @@ def test_fused_quantize_equals_separate_calls(name):
     a_qk, a_v = _quant_pair(inp, w, fused=False)
     b_qk, b_v = _quant_pair(inp, w, fused=True)
     torch.cuda.synchronize()
-    for f in ("q8", "q_scale", "k8", "k_scale", "k_mean"):
-        x, y = getattr(a_qk, f), getattr(b_qk, f)
-        assert (x is None) == (y is None), f
-        if x is not None:
-            assert torch.equal(x, y), f
-    for f in ("vt", "v_scale", "v_mean"):
-        x, y = getattr(a_v, f), getattr(b_v, f)
-        assert (x is None) == (y is None), f
-        if x is not None:
-            assert torch.equal(x, y), f
+    lens = inp["lens"] if w.varlen else None
+    a, b = written_quant_outputs(a_qk, a_v, lens), written_quant_outputs(b_qk, b_v, lens)
+    for f in a:
+        assert (a[f] is None) == (b[f] is None), f
+        if a[f] is not None:
+            assert torch.equal(a[f], b[f]), f
 
 
 @pytest.mark.parametrize("v_dtype,smooth_v", [("fp8", True), ("fp16", False), ("fp16", True)])

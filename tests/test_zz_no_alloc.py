@@ -10,6 +10,7 @@ import torch
 
 import workloads
 import quantized_attention_smooth_amd as sage
+from parity_utils import written_quant_outputs
 
 pytestmark = pytest.mark.gpu
 
@@ -33,13 +34,14 @@ def _both(inp, w, v_dtype, smooth_v):
     return ref, got
 
 
-def _same(ref, got, what):
-    for obj_r, obj_g, fields in ((ref[0], got[0], FIELDS_QK), (ref[1], got[1], FIELDS_V)):
-        for f in fields:
-            x, y = getattr(obj_r, f), getattr(obj_g, f)
-            assert (x is None) == (y is None), (what, f)
-            if x is not None:
-                assert torch.equal(x, y), (what, f)
+def _same(ref, got, what, lens=None):
+    a = written_quant_outputs(*ref, lens)
+    b = written_quant_outputs(*got, lens)
+    for f in FIELDS_QK + FIELDS_V:
+        x, y = a[f], b[f]
+        assert (x is None) == (y is None), (what, f)
+        if x is not None:
+            assert torch.equal(x, y), (what, f)
 
 
 def test_noalloc_equals_workspace_call_on_shrinking_calls():
@@ -62,18 +64,18 @@ def test_noalloc_equals_workspace_call_on_shrinking_calls():
         need = sage.load_library().sage_quant_qkv_noalloc_scratch_size(B, w.Hkv, N, w.d)
         sizes.append(need)
         ref, got = _both(inp, w, v_dtype, smooth_v)
-        _same(ref, got, name)
+        _same(ref, got, name, inp["lens"] if w.varlen else None)
     assert sizes[1] < sizes[0] and sizes[2] < sizes[0]
 
 
 def test_noalloc_rejects_oversize_without_launching():
     print("[gpu-case] no-alloc quantize: oversize request rejected on the host", flush=True)
     dev = torch.device("cuda:0")
-    # sizes whose statistics exceed the static array (600 heads of 8 chunks);
-    # the call fails on the host before its first HIP call
-    w = dataclasses.replace(workloads.WORKLOADS["b2h8n4096d128"], B=1, Hq=600, Hkv=600, Nq=1024, Nk=1024, seed=33)
-    q = torch.zeros((1, 600, 1024, 128), dtype=torch.float16, device=dev)
-    need = sage.load_library().sage_quant_qkv_noalloc_scratch_size(1, 600, 1024, 128)
+    # sizes whose statistics exceed the static array (600 heads of 8 chunks of
+    # 256 tokens); the call fails on the host before its first HIP call
+    w = dataclasses.replace(workloads.WORKLOADS["b2h8n4096d128"], B=1, Hq=600, Hkv=600, Nq=2048, Nk=2048, seed=33)
+    q = torch.zeros((1, 600, 2048, 128), dtype=torch.float16, device=dev)
+    need = sage.load_library().sage_quant_qkv_noalloc_scratch_size(1, 600, 2048, 128)
     assert need > 16 << 20
     with pytest.raises(ValueError, match="too large for the no-alloc call"):
         sage.sage_quant_qkv_noalloc(q, q, q, qk_quant_gran=w.gran)
