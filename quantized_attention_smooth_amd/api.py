@@ -435,18 +435,37 @@ def sage_merge_states(out_parts: torch.Tensor, lse_parts: torch.Tensor, *, tenso
     return (out, lse) if return_lse else out
 
 
+def auto_kv_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, is_causal: bool, kv_splits="auto") -> int:
+    """Number of key ranges sageattn runs: 1 is the one-pass forward.
+    "auto" splits a non-causal call whose row tiles leave compute units idle
+    (splitkv_plan gives at least 2 ranges: few queries against many keys);
+    None or 1 is one pass; an int n >= 2 asks for n ranges (non-causal only)."""
+    if kv_splits is None:
+        return 1
+    if kv_splits == "auto":
+        return 1 if is_causal else splitkv_plan(B, Hq, Nq, Nk, None, Hkv)
+    n = int(kv_splits)
+    if n < 1:
+        raise ValueError("kv_splits must be 'auto', None or an int >= 1")
+    if n > 1 and is_causal:
+        raise NotImplementedError("kv_splits needs a non-causal call")
+    return n
+
+
 def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout="HND", is_causal=False,
              sm_scale: Optional[float] = None, return_lse=False, *, qk_quant_gran: str = "per_thread",
              pv_accum_dtype: str = "fp32+fp32", smooth_k: bool = True, smooth_v: bool = False, v_dtype: str = "fp8",
-             kv_splits=None, attn_mask=None, dropout_p: float = 0.0, scale: Optional[float] = None,
+             kv_splits="auto", attn_mask=None, dropout_p: float = 0.0, scale: Optional[float] = None,
              enable_gqa: Optional[bool] = None):
     """Quantized attention forward: out = softmax(q k^T * sm_scale) v.
 
     q, k, v: fp16/bf16 CUDA tensors, (B, H, N, D) for HND or (B, N, H, D) for
     NHD, same dtype; Hq must be a multiple of Hkv; D <= 128.
-    kv_splits: None runs one pass over the keys; "auto" or an int runs the
-    split-KV forward (key ranges in parallel, merged by log-sum-exp) for few
-    queries against many keys -- non-causal only.
+    kv_splits: "auto" (default) runs the split-KV forward (key ranges in
+    parallel, merged by log-sum-exp) when a non-causal call has too few row
+    tiles to fill the GPU -- few queries against many keys -- and one pass
+    over the keys otherwise; None or 1 always runs one pass; an int n >= 2
+    asks for n ranges (non-causal only).
     Returns out (same dtype and layout as q) and, with return_lse, the fp32
     log-sum-exp [B, Hq, Nq].
 
@@ -483,14 +502,13 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout="H
                        qk_quant_gran=qk_quant_gran, pv_accum_dtype=pv_accum_dtype, smooth_k=smooth_k,
                        smooth_v=smooth_v, v_dtype=v_dtype, kv_splits=kv_splits)
         return (res[0][0], res[1][0]) if return_lse else res[0]
-    if kv_splits is not None and is_causal:
-        raise NotImplementedError("kv_splits needs a non-causal call")
+    auto_kv_splits(1, 1, 1, 1, 1, is_causal, kv_splits)          # rejects a bad request before any work
     qk, qv = sage_quant_qkv(q, k, v, tensor_layout=tensor_layout, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k,
                             v_dtype=v_dtype, smooth_v=smooth_v)
-    if kv_splits is not None:
-        return sage_attn_fwd_splitkv(qk, qv, n_splits=None if kv_splits == "auto" else int(kv_splits),
-                                     tensor_layout=tensor_layout, sm_scale=sm_scale, return_lse=return_lse,
-                                     pv_accum_dtype=pv_accum_dtype)
+    n_splits = auto_kv_splits(qk.B, qk.Hq, qk.Hkv, qk.Nq, qk.Nk, is_causal, kv_splits)
+    if n_splits > 1:
+        return sage_attn_fwd_splitkv(qk, qv, n_splits=n_splits, tensor_layout=tensor_layout, sm_scale=sm_scale,
+                                     return_lse=return_lse, pv_accum_dtype=pv_accum_dtype)
     return sage_attn_fwd(qk, qv, tensor_layout=tensor_layout, is_causal=is_causal, sm_scale=sm_scale,
                          return_lse=return_lse, pv_accum_dtype=pv_accum_dtype)
 

@@ -143,6 +143,26 @@ def test_sageattn_kv_splits_matches_oracle():
         sage.sageattn(q, k, v, is_causal=True, kv_splits=2)
 
 
+def test_sageattn_splits_by_default_only_when_the_gpu_is_not_filled():
+    """sageattn's default (kv_splits="auto") is the split-KV forward on a
+    decode shape and the one-pass forward on a shape whose row tiles fill the
+    GPU, bit for bit."""
+    dev = torch.device("cuda:0")
+    w = workloads.WORKLOADS["b2h8n4096d128"]
+    for shape, split in (({"B": 2, "Hq": 8, "Hkv": 8, "Nq": 8, "Nk": 5000, "d": 64}, True),
+                         ({"B": 2, "Hq": 8, "Hkv": 8, "Nq": 4096, "Nk": 1024, "d": 64}, False)):
+        print(f"[gpu-case] sageattn default kv_splits on {shape} seed 2", flush=True)
+        inp = workloads.make_inputs(w, shape)
+        q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+        out = sage.sageattn(q, k, v)
+        qk, qv = sage.sage_quant_qkv(q, k, v, qk_quant_gran="per_thread")
+        ns = sage.splitkv_plan(shape["B"], shape["Hq"], shape["Nq"], shape["Nk"], Hkv=shape["Hkv"])
+        assert (ns > 1) == split
+        ref = sage.sage_attn_fwd_splitkv(qk, qv, n_splits=ns) if split else sage.sage_attn_fwd(qk, qv)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
 def test_one_range_fp16_v_is_bit_identical_to_attn_fwd():
     print("[gpu-case] split-KV fp16 V one range vs sage_attn_fwd: B1 H4 Nq200 Nk700 d128 bf16 seed 2", flush=True)
     w = workloads.WORKLOADS["b2h8n4096d128"]

@@ -55,6 +55,19 @@ def test_splitkv_plan():
         assert len(oracle.splitkv_ranges(Nk, n)) <= n
 
 
+def test_sageattn_splits_automatically_only_when_compute_units_idle():
+    assert sage.auto_kv_splits(2, 8, 8, 4096, 4096, False) == 1            # 256 row tiles fill the GPU
+    n = sage.auto_kv_splits(4, 32, 8, 16, 32768, False)                      # decode: 32 packed row tiles
+    assert n == sage.splitkv_plan(4, 32, 16, 32768, Hkv=8) and n >= 2
+    assert sage.auto_kv_splits(4, 32, 8, 16, 32768, True) == 1              # causal calls run one pass
+    assert sage.auto_kv_splits(4, 32, 8, 16, 32768, False, None) == 1       # None: one pass
+    assert sage.auto_kv_splits(4, 32, 8, 16, 32768, False, 3) == 3
+    with pytest.raises(NotImplementedError):
+        sage.auto_kv_splits(1, 1, 1, 1, 1, True, 2)
+    with pytest.raises(ValueError):
+        sage.auto_kv_splits(1, 1, 1, 1, 1, False, 0)
+
+
 def test_sageattn_refuses_cpu_tensors():
     q = torch.zeros(1, 2, 4, 64, dtype=torch.float16)
     with pytest.raises(ValueError):                     # CPU tensors are refused first
