@@ -5,8 +5,13 @@ One step = one pass of the whole hot path over one batch already resident in
 HBM: sage_quant_qkv (K mean and V statistics, INT8 Q/K, FP8 V^T, in two
 launches) and sage_attn_fwd (INT8 QK^T, online softmax, FP8 P.V).  The step
 rate (`value`) comes from eager launches (`--graph` replays the step captured
-in a HIP graph instead); kernel times come from HIP events around the eager
-launches.  Before any of it, untimed steps run
+in a HIP graph instead).  Kernel times (`attn_kernel_ms`, `quant_ms`) come
+from HIP events around a burst of back-to-back launches of each call after the
+timed steps, where the GPU never waits for the host.  The timed steps carry no
+events; a second run of as many steps with events around each call gives
+`attn_in_step_ms` and `quant_in_step_ms`, which also see the gaps between the
+step's launches.  Before any of it,
+untimed steps run
 for --settle-ms of wall time (the GPU clock rises over the first tens of
 milliseconds of work), then the --warmup steps.  The default workload
 is B=2, H=8, N=4096, head_dim=128, fp16, per_warp INT8 Q/K, FP8 V;
@@ -127,24 +132,51 @@ def make_step(w, inp):
     else:
         qkw = dict(tensor_layout=w.layout)
 
+    def quant():
+        return sage.sage_quant_qkv(q, k, v, qk_quant_gran=w.gran, smooth_k=w.smooth_k, v_dtype=w.v_dtype,
+                                   smooth_v=w.smooth_v, workspace_k=ws_k, workspace_v=ws_v, **qkw)
+
+    def attn(qk, qv):
+        if w.varlen:
+            return sage.sage_attn_varlen_fwd(qk, qv, cu, cu, q.shape[0], is_causal=w.causal,
+                                             return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
+        return sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, is_causal=w.causal,
+                                  return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
+
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        qk, qv = sage.sage_quant_qkv(q, k, v, qk_quant_gran=w.gran, smooth_k=w.smooth_k, v_dtype=w.v_dtype,
-                                     smooth_v=w.smooth_v, workspace_k=ws_k, workspace_v=ws_v, **qkw)
+        qk, qv = quant()
         if ev is not None:
             ev[1].record(stream)
-        if w.varlen:
-            out = sage.sage_attn_varlen_fwd(qk, qv, cu, cu, q.shape[0], is_causal=w.causal,
-                                            return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
-        else:
-            out = sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, is_causal=w.causal,
-                                     return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
+        out = attn(qk, qv)
         if ev is not None:
             ev[2].record(stream)
+        step.operands = (qk, qv)
         return out
 
+    step.quant, step.attn = quant, attn
     return step
+
+
+def burst_ms(fn, n: int) -> float:
+    """Average time per call of n back-to-back calls of fn, from HIP events
+    on the stream the kernels run on.  The host queues the launches faster
+    than the GPU runs them, so the GPU never waits for the host and the time
+    per call is the kernels' own duration plus the short gap between
+    consecutive kernels (a step's events also see the host's gaps)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
 
 
 def settle_clock(step, settle_ms: float) -> tuple:
@@ -193,17 +225,26 @@ def time_workload(w, steps: int, warmup: int, calibrate: bool = False, settle_ms
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    torch.cuda.synchronize()
+    # the timed steps carry no instrumentation (an event record costs the
+    # stream a few microseconds)
     t0 = time.perf_counter()
     for i in range(steps):
-        step(events[i])
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / steps
-    quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / steps
-    attn_ms = sum(e[1].elapsed_time(e[2]) for e in events) / steps
-    return inp, (ms_per_step, quant_ms, attn_ms), settle
+    # the same number of steps again with HIP events around each call
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    quant_step_ms = sum(e[0].elapsed_time(e[1]) for e in events) / steps
+    attn_step_ms = sum(e[1].elapsed_time(e[2]) for e in events) / steps
+    # each kernel's own duration: back-to-back launches of the step's calls
+    qk, qv = step.operands
+    attn_ms = burst_ms(lambda: step.attn(qk, qv), max(steps, 20))
+    quant_ms = burst_ms(step.quant, max(steps, 20))
+    return inp, (ms_per_step, quant_ms, attn_ms, quant_step_ms, attn_step_ms), settle
 
 
 def time_step_graph(w, inp, steps: int, warmup: int):
@@ -471,7 +512,7 @@ def main() -> int:
     import workloads
 
     w = workloads.WORKLOADS[args.workload]
-    inp, (ms_eager, quant_ms, attn_ms), (settle_ms, settle_steps) = time_workload(
+    inp, (ms_eager, quant_ms, attn_ms, quant_step_ms, attn_step_ms), (settle_ms, settle_steps) = time_workload(
         w, args.steps, args.warmup, args.traffic_calibration, args.settle_ms)
     ms_per_step, launch = ms_eager, "eager"
     if args.graph:
@@ -520,14 +561,16 @@ def main() -> int:
         "attn_kernel_ms": round(attn_ms, 5),
         "attn_kernel_tops": round(attn_tops, 2),
         "attn_pct_of_peak": round(100.0 * attn_tops / peak, 2),
+        "attn_in_step_ms": round(attn_step_ms, 5),
         "quant_ms": round(quant_ms, 5),
         "quant_gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
+        "quant_in_step_ms": round(quant_step_ms, 5),
         "roofline": {"bound": "mfma", "achieved": round(attn_tops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(attn_tops / peak, 4), "traffic": measured_traffic(w.name)},
     }
     if args.secondary != "none" and args.secondary != w.name:
         w2 = workloads.WORKLOADS[args.secondary]
-        _, (ms2, qms2, ams2), _ = time_workload(w2, 10, 20)
+        _, (ms2, qms2, ams2, _, _), _ = time_workload(w2, 10, 20)
         ops2 = workloads.attention_ops(w2)
         at2 = ops2 / (ams2 * 1e-3) / 1e12
         rec["secondary"] = {"workload": w2.name, "seq_len": w2.Nq, "head_dim": w2.d, "B": w2.B, "Hq": w2.Hq,

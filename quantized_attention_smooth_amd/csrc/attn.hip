@@ -297,6 +297,15 @@ __device__ __forceinline__ void store_out4(void* out, bool out_f32, bool vec4, i
     }
 }
 
+// Channels c0 .. c0+3 of a per-channel array of one head, padded to Dp
+// channels (c0 + 3 < Dp: the reads stay inside the padded row).  Four
+// unconditional 4-byte loads (the arrays need only 4-byte alignment); an
+// epilogue loads all its factors this way before using any, so that the loads
+// are in flight together instead of one round trip each.
+__device__ __forceinline__ v4f load_ch4(const float* p, int c0) {
+    return v4f{p[c0], p[c0 + 1], p[c0 + 2], p[c0 + 3]};
+}
+
 // Row sums of P with one small MFMA: the lane's P values are the B operand of
 // a 16x16xK MFMA whose K blocks come from the four 16-lane groups.  Groups 0/2
 // hold queries 0..15 (lane halves 0/1), groups 1/3 queries 16..31, so an A
@@ -1039,8 +1048,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     o_guard<DP>(o[1]);
 
     // ---- epilogue: normalise, add back V's mean, write in the caller's layout
-    const float* vsc = PV == 0 ? a.vs + khead * DP : nullptr;
-    const float* vmu = a.vmean ? a.vmean + khead * DP : nullptr;
+    // the lane's channels' V scale (FP8 V only) and mean factors, all loads
+    // issued before any use (the means under one uniform branch)
+    const bool has_mu = a.vmean != nullptr;
+    v4f sc4[NCB][4], mu4[NCB][4];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            if constexpr (PV == 0) sc4[cb][r4] = load_ch4(a.vs + khead * DP, cb * 32 + 8 * r4 + 4 * hh);
+            mu4[cb][r4] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+    if (has_mu) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) mu4[cb][r4] = load_ch4(a.vmean + khead * DP, cb * 32 + 8 * r4 + 4 * hh);
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int qrow = wq0 + 32 * j + n;
@@ -1058,12 +1082,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                     if (c0 >= a.d) continue;
                     float val[4];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int c = min(c0 + e, a.d - 1);
+                    for (int e = 0; e < 4; ++e) {           // channels past d are not stored
                         val[e] = o[j][cb][4 * r4 + e];
-                        if constexpr (PV == 0) val[e] *= vsc[c] * inv_l;
+                        if constexpr (PV == 0) val[e] *= sc4[cb][r4][e] * inv_l;
                         else val[e] *= inv_l;
-                        if (vmu) val[e] += vmu[c];
+                        if (has_mu) val[e] += mu4[cb][r4][e];
                     }
                     store_out4<OUT_BF16>(a.out, a.out_f32, a.out_vec4, row_off, c0, a.d, val);
                 }
@@ -1416,8 +1439,32 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     if (!live) return;
 
     // ---- epilogue: normalise, add back V's mean, write in the caller's layout
-    const float* vsc = a.vs + khead * DP;
-    const float* vmu = a.vmean ? a.vmean + khead * DP : nullptr;
+    // the lane's channels' V scale and mean factors, all loads issued first
+    // (without a mean the scale row is read a second time and not used).  The
+    // head's offset is recomputed from an opaque copy of its index, so that
+    // the compiler does not share it with the key loop's address arithmetic
+    // and keep it live through the loop.
+    int64_t kh = khead;
+#if __HIP_DEVICE_COMPILE__
+    asm volatile("" : "+s"(kh));
+#endif
+    const float* vsc = a.vs + kh * DP;
+    const bool has_mu = a.vmean != nullptr;
+    const float* vmu = has_mu ? a.vmean + kh * DP : vsc;
+    // (at Dp = 64 the batched loads change how the compiler allocates the key
+    // loop's scalar registers, and that costs more than the epilogue saves:
+    // there each factor is loaded where it is used)
+    constexpr bool kBatch = DP == 128;
+    v4f sc4[NCB][4], mu4[NCB][4];
+    if constexpr (kBatch) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                sc4[cb][r4] = load_ch4(vsc, cb * 32 + 8 * r4 + 4 * hh);
+                mu4[cb][r4] = load_ch4(vmu, cb * 32 + 8 * r4 + 4 * hh);
+            }
+    }
     const float l_tot = ls[0];
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (lane_ok) {
@@ -1432,10 +1479,15 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
                 if (c0 >= a.d) continue;
                 float val[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int c = min(c0 + e, a.d - 1);
-                    val[e] = o[cb][4 * r4 + e] * (vsc[c] * inv_l);
-                    if (vmu) val[e] += vmu[c];
+                for (int e = 0; e < 4; ++e) {               // channels past d are not stored
+                    if constexpr (kBatch) {
+                        val[e] = o[cb][4 * r4 + e] * (sc4[cb][r4][e] * inv_l);
+                        if (has_mu) val[e] += mu4[cb][r4][e];
+                    } else {
+                        const int c = min(c0 + e, a.d - 1);
+                        val[e] = o[cb][4 * r4 + e] * (vsc[c] * inv_l);
+                        if (has_mu) val[e] += vmu[c];
+                    }
                 }
                 store_out4<OUT_BF16>(a.out, a.out_f32, a.out_vec4, row_off, c0, a.d, val);
             }
@@ -1444,13 +1496,21 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         constexpr float p_log2_scale = kPLog2Scale<0>;
         float part = 0.f;
         if (a.kmean) {
-            const float* km = a.kmean + khead * DP;
+            const float* km = a.kmean + kh * DP;
+            v4f km4[NCB][4];                            // all loads first (at Dp = 128)
+            if constexpr (kBatch) {
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) km4[cb][u] = load_ch4(km, cb * 32 + hh * 16 + 4 * u);
+            }
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int code = (int)(int8_t)((qf[cb][e >> 2] >> (8 * (e & 3))) & 0xff);
-                    part += (float)code * km[cb * 32 + hh * 16 + e];
+                    if constexpr (kBatch) part += (float)code * km4[cb][e >> 2][e & 3];
+                    else part += (float)code * km[cb * 32 + hh * 16 + e];
                 }
         }
         const float dot = swap_half_sum(part);
