@@ -891,11 +891,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
         block_sync();
     };
 
-    // ---- prologue: tiles 0 .. AHEAD-1 in flight; wait for tiles 0 and 1
+    // ---- prologue: tiles 0 .. AHEAD-1 in flight; wait for tiles 0 and 1.
+    // The copies are unconditional (past the last tile they copy it again,
+    // into stages no step reads), so that the number of loads in flight is
+    // the same on every path and the compiler waits for the Q fragments
+    // without waiting for the whole prologue.
 #pragma unroll
-    for (int u = 0; u < AHEAD; ++u) issue(u);
-    if (ntiles >= AHEAD) wait_vmcnt<LPT * (AHEAD - 2)>();
-    else wait_vmcnt<0>();
+    for (int u = 0; u < AHEAD; ++u) copier.issue_all(stage_of(u), max(min(u, ntiles - 1), 0));
+    wait_vmcnt<LPT * (AHEAD - 2)>();
     block_sync();
 
     // ---- pipelined main loop over the unmasked tiles.  The two row blocks
@@ -1287,10 +1290,14 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         block_sync();
     };
 
+    // prologue: tiles 0 .. AHEAD-1 in flight, tiles 0 .. 2 landed.  The
+    // copies are unconditional (past the last tile they copy it again, into
+    // stages no step reads), so that the number of loads in flight is the
+    // same on every path and the compiler waits for the Q fragments without
+    // waiting for the whole prologue.
 #pragma unroll
-    for (int u = 0; u < AHEAD; ++u) issue(u);
-    if (ntiles >= AHEAD) wait_vmcnt<LPT * (AHEAD - 3)>();
-    else wait_vmcnt<0>();
+    for (int u = 0; u < AHEAD; ++u) copier.issue_all(stage_of(u), max(min(u, ntiles - 1), 0));
+    wait_vmcnt<LPT * (AHEAD - 3)>();
     block_sync();
 
     constexpr int NQK = 2 * NCB;
