@@ -114,7 +114,9 @@ def cpu_baseline(w, inp, seconds: float) -> dict:
 def make_step(w, inp):
     """The hot-path step of workload w on its inputs, moved to the GPU once:
     sage_quant_qkv (two launches, caller workspaces) then sage_attn_fwd (or
-    sage_attn_varlen_fwd).  step(ev) records ev[0], ev[1], ev[2] before the
+    sage_attn_varlen_fwd).  Where the attention kernel takes Q in its input
+    precision and quantizes it itself (as sageattn does), the quantize call
+    handles K and V only.  step(ev) records ev[0], ev[1], ev[2] before the
     quantize call, between the calls and after the attention call, on the
     stream the kernels run on."""
     import torch
@@ -131,10 +133,13 @@ def make_step(w, inp):
         qkw = dict(cu_seqlens_q=cu, cu_seqlens_k=cu, max_seqlen_q=n_max, max_seqlen_k=n_max)
     else:
         qkw = dict(tensor_layout=w.layout)
+    g = sage.api._geometry(q, w.layout, cu if w.varlen else None, n_max if w.varlen else None)
+    fuse_q = sage.q_fusable(q, g.B, w.Hq, w.Hkv, g.N, w.d, w.gran, w.v_dtype, w.causal, w.varlen, (g.sb, g.sh, g.sn))
 
     def quant():
         return sage.sage_quant_qkv(q, k, v, qk_quant_gran=w.gran, smooth_k=w.smooth_k, v_dtype=w.v_dtype,
-                                   smooth_v=w.smooth_v, workspace_k=ws_k, workspace_v=ws_v, **qkw)
+                                   smooth_v=w.smooth_v, workspace_k=ws_k, workspace_v=ws_v, quantize_q=not fuse_q,
+                                   **qkw)
 
     def attn(qk, qv):
         if w.varlen:
@@ -155,7 +160,7 @@ def make_step(w, inp):
         step.operands = (qk, qv)
         return out
 
-    step.quant, step.attn = quant, attn
+    step.quant, step.attn, step.fuse_q = quant, attn, fuse_q
     return step
 
 
@@ -212,6 +217,7 @@ def time_workload(w, steps: int, warmup: int, calibrate: bool = False, settle_ms
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
     step = make_step(w, inp)
+    inp["fuse_q"] = step.fuse_q
 
     if calibrate:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -528,11 +534,13 @@ def main() -> int:
     attn_tops = ops / (attn_ms * 1e-3) / 1e12
     peak = PEAK_TOPS[w.v_dtype]
     # quantize-pass bytes: read Q, K, V once, K and V a second time for the
-    # statistics, write INT8 Q/K and FP8 V (+ small scale arrays)
+    # statistics, write INT8 Q/K and FP8 V (+ small scale arrays); Q not at
+    # all where the attention kernel quantizes it
     tok_q = int(sum(lens)) if w.varlen else w.B * w.Nq
     tok_k = int(sum(lens)) if w.varlen else w.B * w.Nk
-    elem = (w.Hq * tok_q + 2 * w.Hkv * tok_k) * w.d
-    quant_bytes = 2 * elem + 2 * 2 * w.Hkv * tok_k * w.d + elem
+    kv_elem = 2 * w.Hkv * tok_k * w.d
+    q_elem = 0 if inp["fuse_q"] else w.Hq * tok_q * w.d
+    quant_bytes = 2 * (q_elem + kv_elem) + 2 * kv_elem + (q_elem + kv_elem)
     config = {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "seq_len": w.Nq, "head_dim": w.d,
               "in_dtype": w.dtype, "layout": w.layout, "causal": w.causal, "qk_quant_gran": w.gran,
               "v_dtype": w.v_dtype, "pv_accum_dtype": w.pv_accum, "smooth_k": w.smooth_k,
@@ -562,6 +570,7 @@ def main() -> int:
         "attn_kernel_tops": round(attn_tops, 2),
         "attn_pct_of_peak": round(100.0 * attn_tops / peak, 2),
         "attn_in_step_ms": round(attn_step_ms, 5),
+        "q_quantized_in": "attention kernel" if inp["fuse_q"] else "quantize pass",
         "quant_ms": round(quant_ms, 5),
         "quant_gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
         "quant_in_step_ms": round(quant_step_ms, 5),

@@ -109,7 +109,8 @@ enum sage_pv_accum { SAGE_ACC_FP32 = 0, SAGE_ACC_FP16 = 1, SAGE_ACC_FP16_FP32 = 
  * every sequence length (max_seqlen) and means, groups and scales restart at
  * each sequence.
  * Outputs: q8, q_scale, k8, k_scale (layouts above); k_mean when smooth_k
- * (may be NULL otherwise).
+ * (may be NULL otherwise).  q, q8 and q_scale all NULL: K only (for an
+ * attention call that quantizes Q itself, see sage_attn_fwd).
  * workspace: device scratch of at least sage_quant_workspace_size() bytes
  * (contents need not be initialised).
  * Errors: SAGE_EINVAL for null/misaligned pointers (16-byte alignment for
@@ -225,8 +226,17 @@ int sage_quant_qkv_noalloc(const sage_quant_qk_params* qk, const sage_quant_v_pa
  * when k_mean is given).
  * out: element (b, h, n, c) at out + b*o_stride_b + h*o_stride_h +
  * n*o_stride_n + c for c < d, dtype out_dtype.
+ * Q in its input precision (q non-NULL; q8 and q_scale are then not read and
+ * may be NULL): the kernel quantizes each query row itself, in registers, to
+ * the codes and scales sage_quant_qk would write for the same gran (neither
+ * is stored), so the results are those of the q8/q_scale call bit for bit.
+ * q has dtype in_dtype and the layout of sage_quant_qk's q with these
+ * element strides (varlen: q_stride_b is ignored).  Accepted when
+ * sage_attn_q_fusable() says so for the call's sizes, with q 16-byte aligned
+ * and every stride a multiple of 8 elements.
  * Errors: SAGE_EINVAL for invalid sizes/enums/pointers (q8/k8/vt 16-byte
- * aligned), sm_scale not finite; SAGE_EUNSUPPORTED for none.
+ * aligned), sm_scale not finite; SAGE_EUNSUPPORTED for q given on a call that
+ * sage_attn_q_fusable() rejects.
  * ------------------------------------------------------------------------- */
 typedef struct sage_attn_params {
     size_t struct_size;
@@ -249,9 +259,20 @@ typedef struct sage_attn_params {
     int out_dtype;                      /* enum sage_dtype */
     int64_t o_stride_b, o_stride_h, o_stride_n;
     float* lse;                         /* NULL: no LSE */
+    const void* q;                      /* NULL: q8 / q_scale are the query operand */
+    int64_t q_stride_b, q_stride_h, q_stride_n;
 } sage_attn_params;
 
 int sage_attn_fwd(const sage_attn_params* p, void* stream);
+
+/* sage_attn_q_fusable: 1 if an attention call (sage_attn_fwd, its varlen and
+ * split-KV forms) with these sizes takes Q in its input precision, else 0.
+ * It does when V is FP8 (the kernel with a 256-row query tile), head_dim is a
+ * multiple of 8, and the query tile's quantization groups lie inside one
+ * head: always for dense or varlen rows of one head per tile; with the query
+ * heads of a K/V head packed into one tile (grouped heads, non-causal, dense,
+ * Nq <= 128) per_warp needs Nq % 32 == 0 and per_block Nq % 128 == 0. */
+int sage_attn_q_fusable(int B, int Hq, int Hkv, int Nq, int d, int gran, int v_dtype, int is_causal, int varlen);
 
 /* ---------------------------------------------------------------------------
  * sage_attn_varlen_fwd: as sage_attn_fwd for a packed batch of sequences

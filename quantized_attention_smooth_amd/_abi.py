@@ -56,6 +56,7 @@ class AttnParams(ctypes.Structure):
         ("gran", I), ("v_dtype", I), ("pv_accum", I), ("is_causal", I), ("sm_scale", ctypes.c_float),
         ("in_dtype", I), ("out", VP), ("out_dtype", I),
         ("o_stride_b", I64), ("o_stride_h", I64), ("o_stride_n", I64), ("lse", VP),
+        ("q", VP), ("q_stride_b", I64), ("q_stride_h", I64), ("q_stride_n", I64),
     ]
 
 
@@ -74,7 +75,7 @@ class MergeParams(ctypes.Structure):
 EXPORTS = ["sage_quant_qk", "sage_quant_workspace_size", "sage_quant_v", "sage_quant_qkv",
            "sage_quant_qkv_noalloc_scratch_size", "sage_quant_qkv_noalloc", "sage_attn_fwd",
            "sage_attn_varlen_fwd", "sage_debug_qk_scores", "sage_debug_qk_scores_varlen", "sage_merge_states", "sage_attn_splitkv_workspace_size",
-           "sage_attn_fwd_splitkv", "sage_last_error", "sage_version"]
+           "sage_attn_fwd_splitkv", "sage_attn_q_fusable", "sage_last_error", "sage_version"]
 
 _lib = None
 
@@ -104,6 +105,8 @@ def load(path: str = LIB_PATH):
     L.sage_quant_qkv_noalloc_scratch_size.restype = SZ
     L.sage_attn_fwd.argtypes = [ctypes.POINTER(AttnParams), VP]
     L.sage_attn_fwd.restype = I
+    L.sage_attn_q_fusable.argtypes = [I, I, I, I, I, I, I, I, I]
+    L.sage_attn_q_fusable.restype = I
     L.sage_attn_varlen_fwd.argtypes = [ctypes.POINTER(AttnVarlenParams), VP]
     L.sage_attn_varlen_fwd.restype = I
     L.sage_debug_qk_scores.argtypes = [ctypes.POINTER(AttnParams), I, VP, VP]

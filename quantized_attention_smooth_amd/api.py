@@ -95,8 +95,11 @@ def _check_out(out: torch.Tensor, shape, device: torch.device, name: str = "out"
 
 @dataclasses.dataclass
 class QuantQK:
-    q8: torch.Tensor
-    q_scale: torch.Tensor
+    """Quantized K with INT8 Q (q8, q_scale) or, for an attention call that
+    quantizes Q itself, Q in its input precision (q and its element strides
+    (b, h, n); q8 and q_scale None)."""
+    q8: Optional[torch.Tensor]
+    q_scale: Optional[torch.Tensor]
     k8: torch.Tensor
     k_scale: torch.Tensor
     k_mean: Optional[torch.Tensor]
@@ -108,6 +111,12 @@ class QuantQK:
     Nk: int
     d: int
     dtype: torch.dtype
+    q: Optional[torch.Tensor] = None
+    q_strides: tuple = (0, 0, 0)
+
+    @property
+    def device(self) -> torch.device:
+        return self.k8.device
 
 
 @dataclasses.dataclass
@@ -123,7 +132,8 @@ def workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 
 def _quant_qk_params(q: torch.Tensor, k: torch.Tensor, tensor_layout: str, qk_quant_gran: str, smooth_k: bool,
-                     cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, workspace, alloc_workspace=True):
+                     cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, workspace, alloc_workspace=True,
+                     quantize_q=True):
     if qk_quant_gran not in _GRAN:
         raise ValueError(f"qk_quant_gran must be one of {sorted(_GRAN)}")
     if q.dtype != k.dtype or q.device != k.device:
@@ -135,8 +145,11 @@ def _quant_qk_params(q: torch.Tensor, k: torch.Tensor, tensor_layout: str, qk_qu
     dp = padded_head_dim(gq.d)
     dev = q.device
     nq_pad, nk_pad = _round_up(gq.N, PAD), _round_up(gk.N, PAD)
-    q8 = torch.empty((gq.B, gq.H, nq_pad, dp), dtype=torch.int8, device=dev)
-    qs = torch.empty((gq.B, gq.H, nq_pad // _QG[qk_quant_gran]), dtype=torch.float32, device=dev)
+    if quantize_q:
+        q8 = torch.empty((gq.B, gq.H, nq_pad, dp), dtype=torch.int8, device=dev)
+        qs = torch.empty((gq.B, gq.H, nq_pad // _QG[qk_quant_gran]), dtype=torch.float32, device=dev)
+    else:
+        q8 = qs = None
     k8 = torch.empty((gk.B, gk.H, nk_pad, dp), dtype=torch.int8, device=dev)
     ks = torch.empty((gk.B, gk.H, nk_pad // _KG[qk_quant_gran]), dtype=torch.float32, device=dev)
     km = torch.empty((gk.B, gk.H, dp), dtype=torch.float32, device=dev) if smooth_k else None
@@ -144,7 +157,7 @@ def _quant_qk_params(q: torch.Tensor, k: torch.Tensor, tensor_layout: str, qk_qu
         workspace = torch.empty(workspace_bytes(gk.B, gk.H, gk.N, gk.d), dtype=torch.uint8, device=dev)
     p = A.QuantQKParams()
     p.struct_size = ctypes.sizeof(A.QuantQKParams)
-    p.q, p.k, p.dtype = _ptr(q), _ptr(k), _DT[q.dtype]
+    p.q, p.k, p.dtype = _ptr(q) if quantize_q else None, _ptr(k), _DT[q.dtype]
     p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d = gq.B, gq.H, gk.H, gq.N, gk.N, gq.d
     p.q_stride_b, p.q_stride_h, p.q_stride_n = gq.sb, gq.sh, gq.sn
     p.k_stride_b, p.k_stride_h, p.k_stride_n = gk.sb, gk.sh, gk.sn
@@ -153,7 +166,8 @@ def _quant_qk_params(q: torch.Tensor, k: torch.Tensor, tensor_layout: str, qk_qu
     p.q8, p.q_scale, p.k8, p.k_scale, p.k_mean = _ptr(q8), _ptr(qs), _ptr(k8), _ptr(ks), _ptr(km)
     p.workspace = _ptr(workspace)
     p.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    res = QuantQK(q8, qs, k8, ks, km, qk_quant_gran, gq.B, gq.H, gk.H, gq.N, gk.N, gq.d, q.dtype)
+    res = QuantQK(q8, qs, k8, ks, km, qk_quant_gran, gq.B, gq.H, gk.H, gq.N, gk.N, gq.d, q.dtype,
+                  None if quantize_q else q, (gq.sb, gq.sh, gq.sn))
     return p, res, workspace
 
 
@@ -211,14 +225,16 @@ def sage_quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, tensor_
                    smooth_v: bool = False, cu_seqlens_q: Optional[torch.Tensor] = None,
                    cu_seqlens_k: Optional[torch.Tensor] = None, max_seqlen_q: Optional[int] = None,
                    max_seqlen_k: Optional[int] = None, workspace_k: Optional[torch.Tensor] = None,
-                   workspace_v: Optional[torch.Tensor] = None):
+                   workspace_v: Optional[torch.Tensor] = None, quantize_q: bool = True):
     """sage_quant_qk and sage_quant_v in one call (two kernel launches);
-    the K and V workspaces, when given, must be distinct buffers."""
+    the K and V workspaces, when given, must be distinct buffers.  With
+    quantize_q=False, Q is left in its input precision for an attention call
+    that quantizes it itself (see q_fusable)."""
     L = A.load()
     if v.dtype != k.dtype or v.device != k.device:
         raise ValueError("k and v must share dtype and device")
     pk, rqk, _ = _quant_qk_params(q, k, tensor_layout, qk_quant_gran, smooth_k, cu_seqlens_q, cu_seqlens_k,
-                                  max_seqlen_q, max_seqlen_k, workspace_k)
+                                  max_seqlen_q, max_seqlen_k, workspace_k, quantize_q=quantize_q)
     pv, rv, _ = _quant_v_params(v, tensor_layout, v_dtype, smooth_v, cu_seqlens_k, max_seqlen_k, workspace_v)
     A.check(L.sage_quant_qkv(ctypes.byref(pk), ctypes.byref(pv), _stream()))
     return rqk, rv
@@ -251,6 +267,9 @@ def _attn_params(qk: QuantQK, qv: QuantV, out: torch.Tensor, lse: Optional[torch
     p = A.AttnParams()
     p.struct_size = ctypes.sizeof(A.AttnParams)
     p.q8, p.q_scale, p.k8, p.k_scale, p.k_mean = _ptr(qk.q8), _ptr(qk.q_scale), _ptr(qk.k8), _ptr(qk.k_scale), _ptr(qk.k_mean)
+    if qk.q is not None:
+        p.q = _ptr(qk.q)
+        p.q_stride_b, p.q_stride_h, p.q_stride_n = qk.q_strides
     p.vt, p.v_scale, p.v_mean = _ptr(qv.vt), _ptr(qv.v_scale), _ptr(qv.v_mean)
     p.B, p.Hq, p.Hkv, p.Nq, p.Nk, p.d = qk.B, qk.Hq, qk.Hkv, qk.Nq, qk.Nk, qk.d
     p.gran = _GRAN[qk.gran]
@@ -269,7 +288,7 @@ def sage_attn_fwd(qk: QuantQK, qv: QuantV, *, tensor_layout: str = "HND", is_cau
                   sm_scale: Optional[float] = None, return_lse: bool = False, pv_accum_dtype: str = "fp32+fp32",
                   out: Optional[torch.Tensor] = None):
     L = A.load()
-    dev = qk.q8.device
+    dev = qk.device
     if tensor_layout not in ("HND", "NHD"):
         raise ValueError(f"tensor_layout must be 'HND' or 'NHD', not {tensor_layout!r}")
     shape = (qk.B, qk.Hq, qk.Nq, qk.d) if tensor_layout == "HND" else (qk.B, qk.Nq, qk.Hq, qk.d)
@@ -313,7 +332,7 @@ def sage_attn_fwd_splitkv(qk: QuantQK, qv: QuantV, *, n_splits: Optional[int] = 
     """sage_attn_fwd with the keys cut into ranges that run in parallel and are
     merged by their log-sum-exp (few queries, many keys; non-causal)."""
     L = A.load()
-    dev = qk.q8.device
+    dev = qk.device
     if tensor_layout not in ("HND", "NHD"):
         raise ValueError(f"tensor_layout must be 'HND' or 'NHD', not {tensor_layout!r}")
     shape = (qk.B, qk.Hq, qk.Nq, qk.d) if tensor_layout == "HND" else (qk.B, qk.Nq, qk.Hq, qk.d)
@@ -337,7 +356,7 @@ def sage_attn_varlen_fwd(qk: QuantQK, qv: QuantV, cu_seqlens_q: torch.Tensor, cu
                          return_lse: bool = False, pv_accum_dtype: str = "fp32+fp32",
                          out: Optional[torch.Tensor] = None):
     L = A.load()
-    dev = qk.q8.device
+    dev = qk.device
     if out is None:
         out = torch.empty((total_q, qk.Hq, qk.d), dtype=qk.dtype, device=dev)
     else:
@@ -358,7 +377,9 @@ def sage_debug_qk_scores(qk: QuantQK, checksums: bool = False, cu_seqlens_q: Opt
     a varlen batch (cu_seqlens given) only the checksums exist, int64
     [Hq, total_q, 2], over each row's own sequence."""
     L = A.load()
-    dev = qk.q8.device
+    dev = qk.device
+    if qk.q8 is None:
+        raise ValueError("the score dump reads the INT8 Q of sage_quant_qk (quantize_q=True)")
     if cu_seqlens_q is not None:
         if not checksums or cu_seqlens_k is None or total_q is None:
             raise ValueError("varlen scores come as checksums, with cu_seqlens_q, cu_seqlens_k and total_q")
@@ -435,6 +456,21 @@ def sage_merge_states(out_parts: torch.Tensor, lse_parts: torch.Tensor, *, tenso
     return (out, lse) if return_lse else out
 
 
+def q_fusable(q: torch.Tensor, B: int, Hq: int, Hkv: int, Nq: int, d: int, qk_quant_gran: str, v_dtype: str,
+              is_causal: bool, varlen: bool, strides) -> bool:
+    """Whether the attention call takes this Q in its input precision and
+    quantizes it in its own kernel (sage_attn_q_fusable for the sizes, a
+    16-byte aligned q, strides in multiples of 8 elements)."""
+    if qk_quant_gran not in _GRAN or v_dtype not in ("fp8", "fp16"):
+        return False
+    L = A.load()
+    vd = A.SAGE_V_FP8 if v_dtype == "fp8" else A.SAGE_V_FP16
+    if not L.sage_attn_q_fusable(B, Hq, Hkv, Nq, d, _GRAN[qk_quant_gran], vd, int(bool(is_causal)), int(varlen)):
+        return False
+    sb, sh, sn = strides
+    return q.data_ptr() % 16 == 0 and sh % 8 == 0 and sn % 8 == 0 and (varlen or sb % 8 == 0)
+
+
 def auto_kv_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, is_causal: bool, kv_splits="auto") -> int:
     """Number of key ranges sageattn runs: 1 is the one-pass forward.
     "auto" splits a non-causal call whose row tiles leave compute units idle
@@ -503,8 +539,10 @@ def sageattn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, tensor_layout="H
                        smooth_v=smooth_v, v_dtype=v_dtype, kv_splits=kv_splits)
         return (res[0][0], res[1][0]) if return_lse else res[0]
     auto_kv_splits(1, 1, 1, 1, 1, is_causal, kv_splits)          # rejects a bad request before any work
+    gq, gk = _geometry(q, tensor_layout, None, None), _geometry(k, tensor_layout, None, None)
+    fuse = q_fusable(q, gq.B, gq.H, gk.H, gq.N, gq.d, qk_quant_gran, v_dtype, is_causal, False, (gq.sb, gq.sh, gq.sn))
     qk, qv = sage_quant_qkv(q, k, v, tensor_layout=tensor_layout, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k,
-                            v_dtype=v_dtype, smooth_v=smooth_v)
+                            v_dtype=v_dtype, smooth_v=smooth_v, quantize_q=not fuse)
     n_splits = auto_kv_splits(qk.B, qk.Hq, qk.Hkv, qk.Nq, qk.Nk, is_causal, kv_splits)
     if n_splits > 1:
         return sage_attn_fwd_splitkv(qk, qv, n_splits=n_splits, tensor_layout=tensor_layout, sm_scale=sm_scale,
@@ -525,9 +563,12 @@ def sageattn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlen
         raise ValueError("q, k, v must have the same dtype")
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
         raise ValueError("cu_seqlens must be int32")
+    gq = _geometry(q, "NHD", cu_seqlens_q, max_seqlen_q)
+    fuse = q_fusable(q, gq.B, gq.H, k.shape[1] if k.dim() == 3 else gq.H, gq.N, gq.d, qk_quant_gran, v_dtype,
+                     is_causal, True, (gq.sb, gq.sh, gq.sn))
     qk, qv = sage_quant_qkv(q, k, v, qk_quant_gran=qk_quant_gran, smooth_k=smooth_k, v_dtype=v_dtype,
                             smooth_v=smooth_v, cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
-                            max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+                            max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, quantize_q=not fuse)
     return sage_attn_varlen_fwd(qk, qv, cu_seqlens_q, cu_seqlens_k, q.shape[0], is_causal=is_causal,
                                 sm_scale=sm_scale, return_lse=return_lse, pv_accum_dtype=pv_accum_dtype)
 

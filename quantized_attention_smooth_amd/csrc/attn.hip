@@ -257,6 +257,9 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Waits until this wavefront's LDS accesses are done.
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
 // Workgroup barrier that also keeps the compiler from moving LDS accesses
 // across it (the hardware ordering comes from the explicit vmcnt waits).
 __device__ __forceinline__ void block_sync() {
@@ -1219,7 +1222,23 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const int64_t qhead = (int64_t)b * a.Hq + h;
     v4i qf[NCB];
     float qscale = 0.f;
-    if (live) {
+    // With Q in its input precision the lane loads the 8-channel slices
+    // cb*32 + hh*16 + 8e of its row here and quantizes them after the
+    // prologue's copies are issued (rows past the sequence load its first row
+    // and slices past d the first slice; both become zeros).
+    const bool q_in = a.qraw != nullptr;
+    uint4 qraw[2 * NCB];
+    if (q_in) {
+        const int qr = lane_ok ? qrow : 0;
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.qraw) +
+                             (a.cu_q ? (int64_t)(qoff + qr) * a.qsn + (int64_t)h * a.qsh
+                                     : (int64_t)b * a.qsb + (int64_t)h * a.qsh + (int64_t)qr * a.qsn);
+#pragma unroll
+        for (int i = 0; i < 2 * NCB; ++i) {
+            const int c0 = (i >> 1) * 32 + hh * 16 + 8 * (i & 1);
+            qraw[i] = *reinterpret_cast<const uint4*>(qp + (c0 < a.d ? c0 : 0));
+        }
+    } else if (live) {
         const int8_t* q8row = a.q8 + (qhead * a.nq_pad + qrow) * DP;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) qf[cb] = *reinterpret_cast<const v4i*>(q8row + cb * 32 + hh * 16);
@@ -1228,7 +1247,6 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) qf[cb] = v4i{0, 0, 0, 0};
     }
-    const float cq = ((qscale * a.sm_scale) * kLog2e) * kAccScale;   // times 2^26, exact
 
     const int64_t khead = (int64_t)b * a.Hkv + hk;
     const int8_t* kbase = uniform(a.k8 + khead * a.nk_pad * DP + (int64_t)kb0 * DP);
@@ -1297,8 +1315,51 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     // waiting for the whole prologue.
 #pragma unroll
     for (int u = 0; u < AHEAD; ++u) copier.issue_all(stage_of(u), max(min(u, ntiles - 1), 0));
+
+    // Q in its input precision -> INT8 codes and scales, as the quantize pass
+    // makes them: the absolute maximum of the row (its two lanes), of the
+    // wavefront's 32 rows (per_warp), or of 4 wavefronts' 128 rows through
+    // LDS (per_block).
+    __shared__ float s_qmax[kWaves8];
+    float qx[2 * NCB][8];
+    float qm = 0.f;
+    if (q_in) {
+#pragma unroll
+        for (int i = 0; i < 2 * NCB; ++i) {
+            const bool ok = lane_ok && (i >> 1) * 32 + hh * 16 + 8 * (i & 1) < a.d;
+            float f16[8], b16[8];
+            unpack8<false>(qraw[i], f16);
+            unpack8<true>(qraw[i], b16);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                qx[i][j] = ok ? (a.q_bf16 ? b16[j] : f16[j]) : 0.f;
+                qm = fmaxf(qm, fabsf(qx[i][j]));
+            }
+        }
+        qm = fmaxf(qm, __shfl_xor(qm, 32));
+        if (a.gq_shift >= 5) {
+#pragma unroll
+            for (int off = 1; off < 32; off <<= 1) qm = fmaxf(qm, __shfl_xor(qm, off));
+        }
+        if (a.gq_shift == 7 && lane == 0) s_qmax[wave] = qm;
+        wait_lgkm0();
+    }
     wait_vmcnt<LPT * (AHEAD - 3)>();
     block_sync();
+    if (q_in) {
+        if (a.gq_shift == 7) {
+            const int w0 = wave & ~3;
+            qm = fmaxf(fmaxf(s_qmax[w0], s_qmax[w0 + 1]), fmaxf(s_qmax[w0 + 2], s_qmax[w0 + 3]));
+        }
+        float inv;
+        int8_group_scale(qm, qscale, inv);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+            const uint2 lo = int8_codes8(qx[2 * cb], inv), hi = int8_codes8(qx[2 * cb + 1], inv);
+            qf[cb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
+        }
+    }
+    const float cq = ((qscale * a.sm_scale) * kLog2e) * kAccScale;   // times 2^26, exact
 
     constexpr int NQK = 2 * NCB;
     constexpr int NPV = NCB;

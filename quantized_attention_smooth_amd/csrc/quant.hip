@@ -76,12 +76,6 @@ __device__ __forceinline__ uint4 load_raw8(const uint16_t* row, int c0, int d) {
                           e[6] | ((uint32_t)e[7] << 16));
     }
 }
-template <bool BF16>
-__device__ __forceinline__ void unpack8(const uint4& raw, float v[8]) {
-    const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = Half<BF16>::to_f(e[j]);
-}
 
 // Workgroup id -> (unit, head, sequence), the head varying fastest: with
 // token-major layouts (NHD, packed varlen) the rows of all heads of a token
@@ -416,35 +410,20 @@ __device__ __forceinline__ void quant_rows_body(const QuantRowsArgs& a, int tile
         if (tid < kPad && (tid & (2 * s - 1)) == 0) rmax[tid] = fmaxf(rmax[tid], rmax[tid + s]);
         __syncthreads();
     }
-    // one thread per group: the scale and its inverse (each a single
-    // correctly rounded division)
+    // one thread per group: the scale and its multiplier
     __shared__ float rinv[kPad];
     if (tid < kPad && (tid & (G - 1)) == 0) {
-        const float amax = rmax[tid];
-        rinv[tid] = amax > 0.f ? 127.0f / amax : 0.f;
-        a.scale[((int64_t)b * a.H + h) * (a.npad >> a.group_shift) + ((row0 + tid) >> a.group_shift)] =
-            amax > 0.f ? amax / 127.0f : 0.f;
+        float sc, iv;
+        int8_group_scale(rmax[tid], sc, iv);
+        rinv[tid] = iv;
+        a.scale[((int64_t)b * a.H + h) * (a.npad >> a.group_shift) + ((row0 + tid) >> a.group_shift)] = sc;
     }
     __syncthreads();
-    // code = rint(fl(x * inv)): adding 1.5 * 2^23 rounds fl(x * inv) to an
-    // integer (ties to even) held in the low bits of the sum, whose low byte
-    // is the code in two's complement.  No clamp is needed: with
-    // inv = fl(127 / amax) and |x| <= amax, |fl(x * inv)| < 127.5.
-    constexpr float kRound = 12582912.0f;
     int8_t* obase = a.out + (((int64_t)b * a.H + h) * a.npad + row0) * DP;
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const int r = p * RPP + rr;
-        const float inv = rinv[r & ~(G - 1)];
-        uint32_t c[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) c[j] = __float_as_uint(vals[p][j] * inv + kRound);
-        // low bytes of c[0..3] and c[4..7] into one word each
-        const uint32_t w0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u),
-                                                  __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u), 0x05040100u);
-        const uint32_t w1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(c[7], c[6], 0x0c0c0400u),
-                                                  __builtin_amdgcn_perm(c[5], c[4], 0x0c0c0400u), 0x05040100u);
-        *reinterpret_cast<uint2*>(obase + (int64_t)r * DP + cg * 8) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2*>(obase + (int64_t)r * DP + cg * 8) = int8_codes8(vals[p], rinv[r & ~(G - 1)]);
     }
 }
 
@@ -647,7 +626,7 @@ template <bool BF16, int DP, bool FP8, bool VEC>
 static hipError_t quant_qkv_dispatch(const QuantRowsArgs& q, const QuantRowsArgs& k, const StatsArgs& ks,
                                      bool smooth_k, const QuantVArgs& v, const StatsArgs& vs, bool v_stats,
                                      hipStream_t s) {
-    const int nq = (q.npad / kPad) * q.H * q.B;
+    const int nq = q.out ? (q.npad / kPad) * q.H * q.B : 0;       // no Q output: K and V only
     const int k_tiles = (k.npad / kPad) * k.H * k.B;
     const int nk1 = smooth_k ? ks.chunks * ks.H * ks.B : k_tiles;
     const int nv1 = v_stats ? vs.chunks * vs.H * vs.B : 0;
@@ -681,7 +660,7 @@ hipError_t launch_quant_qkv(const QuantRowsArgs& q, const QuantRowsArgs& k, cons
 template <bool BF16, int DP, bool VEC>
 static hipError_t quant_qk_dispatch(const QuantRowsArgs& q, const QuantRowsArgs& k, const StatsArgs& ks, bool smooth,
                                     hipStream_t s) {
-    const int nq = (q.npad / kPad) * q.H * q.B;
+    const int nq = q.out ? (q.npad / kPad) * q.H * q.B : 0;       // no Q output: K only
     const int n2 = smooth ? ks.chunks * ks.H * ks.B : (k.npad / kPad) * k.H * k.B;
     qk_pass1_kernel<BF16, DP, VEC><<<nq + n2, kThreads, 0, s>>>(q, k, ks, nq, smooth ? 1 : 0);
     if (smooth) {

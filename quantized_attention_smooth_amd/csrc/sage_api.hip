@@ -140,10 +140,11 @@ int prepare_qk(const sage_quant_qk_params* p, QKPrep& o, bool own_ws = true) {
     if (!valid_dtype(p->dtype)) return fail(SAGE_EINVAL, "unknown dtype %d", p->dtype);
     if (int r = check_sizes(p->B, p->Hq, p->Hkv, p->Nq, p->Nk, p->d)) return r;
     if (!valid_gran(p->gran)) return fail(SAGE_EINVAL, "unknown qk_quant_gran %d", p->gran);
-    if (!p->q || !p->k || !p->q8 || !p->q_scale || !p->k8 || !p->k_scale)
+    const bool with_q = p->q || p->q8 || p->q_scale;    // all three NULL: K only
+    if ((with_q && (!p->q || !p->q8 || !p->q_scale)) || !p->k || !p->k8 || !p->k_scale)
         return fail(SAGE_EINVAL, "NULL tensor pointer");
     if (p->smooth_k && !p->k_mean) return fail(SAGE_EINVAL, "smooth_k needs k_mean");
-    if (!aligned(p->q, 2) || !aligned(p->k, 2)) return fail(SAGE_EINVAL, "q/k not 2-byte aligned");
+    if (!aligned(p->q, 2) || !aligned(p->k, 2)) return fail(SAGE_EINVAL, "q/k not 2-byte aligned");   // (NULL is aligned)
     if (!aligned(p->q8, 16) || !aligned(p->k8, 16)) return fail(SAGE_EINVAL, "q8/k8 must be 16-byte aligned");
     if (!aligned(p->q_scale, 4) || !aligned(p->k_scale, 4) || (p->k_mean && !aligned(p->k_mean, 4)))
         return fail(SAGE_EINVAL, "scales/means must be 4-byte aligned");
@@ -177,7 +178,7 @@ int prepare_qk(const sage_quant_qk_params* p, QKPrep& o, bool own_ws = true) {
     ka.x = p->k; ka.sb = p->k_stride_b; ka.sh = p->k_stride_h; ka.sn = p->k_stride_n; ka.cu = p->cu_seqlens_k;
     ka.B = p->B; ka.H = p->Hkv; ka.N = p->Nk; ka.npad = nk_pad; ka.d = p->d;
     ka.group_shift = k_group_shift(p->gran); ka.out = p->k8; ka.scale = p->k_scale;
-    const bool vec = vec_ok(p->q, p->q_stride_b, p->q_stride_h, p->q_stride_n) &&
+    const bool vec = (!with_q || vec_ok(p->q, p->q_stride_b, p->q_stride_h, p->q_stride_n)) &&
                      vec_ok(p->k, p->k_stride_b, p->k_stride_h, p->k_stride_n);
     o.qa = qa;
     o.ka = ka;
@@ -362,6 +363,21 @@ int sage_quant_qkv_noalloc(const sage_quant_qk_params* qk, const sage_quant_v_pa
     return ok();
 }
 
+// Whether the attention kernel for these sizes quantizes Q itself: the
+// 256-row tile kernel (FP8 V), whole 8-channel slices, and quantization groups
+// that never straddle two heads inside a tile of packed query heads.
+static bool q_fusable(int B, int Hq, int Hkv, int Nq, int d, int gran, int v_dtype, int is_causal, bool varlen) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || d < 1 || d > 128 || Hq % Hkv) return false;
+    if (v_dtype != SAGE_V_FP8 || d % 8 || !valid_gran(gran)) return false;
+    const bool packed = !varlen && !is_causal && Hq > Hkv && Nq <= sage::kPackMaxNq;
+    if (packed && Nq % (1 << q_group_shift(gran))) return false;
+    return true;
+}
+
+int sage_attn_q_fusable(int B, int Hq, int Hkv, int Nq, int d, int gran, int v_dtype, int is_causal, int varlen) {
+    return q_fusable(B, Hq, Hkv, Nq, d, gran, v_dtype, is_causal, varlen != 0) ? 1 : 0;
+}
+
 static int check_attn(const sage_attn_params* p, bool varlen) {
     if (int r = check_sizes(p->B, p->Hq, p->Hkv, p->Nq, p->Nk, p->d)) return r;
     if (!valid_gran(p->gran)) return fail(SAGE_EINVAL, "unknown qk_quant_gran %d", p->gran);
@@ -369,11 +385,18 @@ static int check_attn(const sage_attn_params* p, bool varlen) {
     if (p->pv_accum < SAGE_ACC_FP32 || p->pv_accum > SAGE_ACC_FP32_FP32)
         return fail(SAGE_EINVAL, "unknown pv_accum %d", p->pv_accum);
     if (!valid_dtype(p->in_dtype) || !valid_dtype(p->out_dtype)) return fail(SAGE_EINVAL, "unknown dtype");
-    if (!p->q8 || !p->q_scale || !p->k8 || !p->k_scale || !p->vt || !p->out)
+    if ((!p->q && (!p->q8 || !p->q_scale)) || !p->k8 || !p->k_scale || !p->vt || !p->out)
         return fail(SAGE_EINVAL, "NULL tensor pointer");
     if (p->v_dtype == SAGE_V_FP8 && !p->v_scale) return fail(SAGE_EINVAL, "FP8 V needs v_scale");
     if (!aligned(p->q8, 16) || !aligned(p->k8, 16) || !aligned(p->vt, 16))
         return fail(SAGE_EINVAL, "q8/k8/vt must be 16-byte aligned");
+    if (p->q) {
+        if (!q_fusable(p->B, p->Hq, p->Hkv, p->Nq, p->d, p->gran, p->v_dtype, p->is_causal, varlen))
+            return fail(SAGE_EUNSUPPORTED, "this call cannot take Q in its input precision (sage_attn_q_fusable)");
+        if (!aligned(p->q, 16) || p->q_stride_n <= 0 || p->q_stride_h < 0 || (!varlen && p->q_stride_b < 0) ||
+            p->q_stride_n % 8 || p->q_stride_h % 8 || (!varlen && p->q_stride_b % 8))
+            return fail(SAGE_EINVAL, "q must be 16-byte aligned with non-negative strides that are multiples of 8");
+    }
     if (!aligned(p->q_scale, 4) || !aligned(p->k_scale, 4) || (p->v_scale && !aligned(p->v_scale, 4)) ||
         (p->k_mean && !aligned(p->k_mean, 4)) || (p->v_mean && !aligned(p->v_mean, 4)) ||
         (p->lse && !aligned(p->lse, 4)))
@@ -388,6 +411,8 @@ static int check_attn(const sage_attn_params* p, bool varlen) {
 static sage::AttnArgs attn_args(const sage_attn_params* p) {
     sage::AttnArgs a{};
     a.q8 = p->q8; a.qs = p->q_scale; a.k8 = p->k8; a.ks = p->k_scale; a.kmean = p->k_mean;
+    a.qraw = p->q; a.qsb = p->q_stride_b; a.qsh = p->q_stride_h; a.qsn = p->q_stride_n;
+    a.q_bf16 = p->in_dtype == SAGE_BF16 ? 1 : 0;
     a.vt = p->vt; a.vs = p->v_scale; a.vmean = p->v_mean; a.out = p->out; a.lse = p->lse;
     a.B = p->B; a.Hq = p->Hq; a.Hkv = p->Hkv; a.Nq = p->Nq; a.Nk = p->Nk; a.d = p->d;
     a.nq_pad = (int)round_up(p->Nq, sage::kPad);

@@ -45,6 +45,14 @@ template <> struct Half<true> {
     __device__ static uint16_t from_f(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 };
 
+// The 8 fp16 or bf16 values packed in 16 bytes, as fp32 (exact).
+template <bool BF16>
+__device__ __forceinline__ void unpack8(const uint4& raw, float v[8]) {
+    const uint16_t* e = reinterpret_cast<const uint16_t*>(&raw);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = Half<BF16>::to_f(e[j]);
+}
+
 // Order of keys inside an aligned block of 64 in the transposed V operand:
 // position 32*h + 16*b + 4*r + e holds key 32*b + 8*r + 4*h + e.  This is the
 // order in which a lane of the S^T = K Q^T accumulator holds its keys (lane
@@ -85,6 +93,33 @@ __device__ __forceinline__ float swap_half_max(float x) {
 __device__ __forceinline__ float swap_half_sum(float x) {
     auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false, false);
     return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+// INT8 quantization of Q and K (the quantize pass and the attention kernel's
+// own quantization of Q share these, so that both give the same bits).
+// A group with absolute maximum amax has scale amax / 127 and multiplier
+// fl(127 / amax), each one correctly rounded division (both 0 for an
+// all-zero group).
+__device__ __forceinline__ void int8_group_scale(float amax, float& scale, float& inv) {
+    scale = amax > 0.f ? amax / 127.0f : 0.f;
+    inv = amax > 0.f ? 127.0f / amax : 0.f;
+}
+// The codes rint(fl(x * inv)) of 8 values as 8 bytes, first value in the low
+// byte.  Adding 1.5 * 2^23 rounds fl(x * inv) to an integer (ties to even)
+// held in the low bits of the sum, whose low byte is the code in two's
+// complement; with |x| <= amax, |fl(x * inv)| < 127.5, so no clamp is needed.
+// Product and sum are rounded separately (never one fused operation).
+__device__ __forceinline__ uint2 int8_codes8(const float (&x)[8], float inv) {
+#pragma clang fp contract(off)
+    constexpr float kRound = 12582912.0f;
+    uint32_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = __float_as_uint(x[j] * inv + kRound);
+    const uint32_t w0 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(c[3], c[2], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(c[1], c[0], 0x0c0c0400u), 0x05040100u);
+    const uint32_t w1 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(c[7], c[6], 0x0c0c0400u),
+                                              __builtin_amdgcn_perm(c[5], c[4], 0x0c0c0400u), 0x05040100u);
+    return make_uint2(w0, w1);
 }
 
 }  // namespace sage

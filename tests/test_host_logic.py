@@ -55,6 +55,35 @@ def test_splitkv_plan():
         assert len(oracle.splitkv_ranges(Nk, n)) <= n
 
 
+def test_attention_takes_q_in_its_input_precision_only_where_groups_fit_a_tile():
+    """The C ABI's rule (pure host code): FP8 V, head_dim a multiple of 8, and
+    with packed query heads (grouped heads, non-causal, dense, Nq <= 128)
+    whole quantization groups per head."""
+    L = sage.load_library()
+    P_THREAD, P_WARP, P_BLOCK = 2, 1, 0
+    FP8, FP16 = 0, 1
+
+    def ok(B, Hq, Hkv, Nq, d, gran, vd=FP8, causal=0, varlen=0):
+        return L.sage_attn_q_fusable(B, Hq, Hkv, Nq, d, gran, vd, causal, varlen) == 1
+
+    assert (sage.api._GRAN["per_thread"], sage.api._GRAN["per_warp"], sage.api._GRAN["per_block"]) == \
+        (P_THREAD, P_WARP, P_BLOCK)
+    assert ok(2, 8, 8, 4096, 128, P_WARP)
+    assert not ok(2, 8, 8, 4096, 128, P_WARP, vd=FP16)         # the FP16-V kernel reads INT8 Q
+    assert not ok(2, 8, 8, 4096, 100, P_WARP)                   # 8-channel slices
+    assert ok(2, 8, 8, 4096, 96, P_BLOCK)
+    assert ok(4, 32, 8, 17, 128, P_THREAD)                      # packed rows: one row per group
+    assert not ok(4, 32, 8, 40, 128, P_WARP)                    # packed rows: a group would straddle heads
+    assert ok(4, 32, 8, 64, 128, P_WARP)
+    assert not ok(4, 32, 8, 64, 128, P_BLOCK)
+    assert ok(4, 32, 8, 128, 128, P_BLOCK)
+    assert ok(4, 32, 8, 40, 128, P_WARP, causal=1)              # causal calls are not packed
+    assert ok(4, 32, 8, 40, 128, P_WARP, varlen=1)              # nor varlen ones
+    assert ok(4, 32, 8, 200, 128, P_WARP)                       # more than 128 queries: not packed
+    assert not ok(1, 6, 4, 64, 128, P_WARP)                     # Hq not a multiple of Hkv
+    assert not ok(1, 8, 8, 64, 128, 7)                          # unknown granularity
+
+
 def test_sageattn_splits_automatically_only_when_compute_units_idle():
     assert sage.auto_kv_splits(2, 8, 8, 4096, 4096, False) == 1            # 256 row tiles fill the GPU
     n = sage.auto_kv_splits(4, 32, 8, 16, 32768, False)                      # decode: 32 packed row tiles
