@@ -268,7 +268,8 @@ int sage_attn_fwd(const sage_attn_params* p, void* stream);
 /* sage_attn_q_fusable: 1 if an attention call (sage_attn_fwd, its varlen and
  * split-KV forms) with these sizes takes Q in its input precision, else 0.
  * It does when V is FP8 (the kernel with a 256-row query tile), head_dim is a
- * multiple of 8, and the query tile's quantization groups lie inside one
+ * multiple of 8 above 64 (128 padded channels), and the query tile's
+ * quantization groups lie inside one
  * head: always for dense or varlen rows of one head per tile; with the query
  * heads of a K/V head packed into one tile (grouped heads, non-causal, dense,
  * Nq <= 128) per_warp needs Nq % 32 == 0 and per_block Nq % 128 == 0. */

@@ -240,6 +240,37 @@ def sage_quant_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, tensor_
     return rqk, rv
 
 
+class QuantQKVPlan:
+    """sage_quant_qkv with its outputs, workspaces and parameter blocks made
+    once: run() launches the two quantize kernels into the same output tensors
+    on the current stream each time, for loops over inputs of one shape held
+    in the same buffers (each run overwrites the previous results).  qk and qv
+    are the outputs, as sage_quant_qkv returns them."""
+
+    def __init__(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, **kw):
+        self._keep = (q, k, v, kw.get("cu_seqlens_q"), kw.get("cu_seqlens_k"))
+        layout = kw.pop("tensor_layout", "HND")
+        gran = kw.pop("qk_quant_gran", "per_thread")
+        smooth_k = kw.pop("smooth_k", True)
+        v_dtype = kw.pop("v_dtype", "fp8")
+        smooth_v = kw.pop("smooth_v", False)
+        cq, ck = kw.pop("cu_seqlens_q", None), kw.pop("cu_seqlens_k", None)
+        mq, mk = kw.pop("max_seqlen_q", None), kw.pop("max_seqlen_k", None)
+        quantize_q = kw.pop("quantize_q", True)
+        if kw:
+            raise TypeError(f"unexpected arguments {sorted(kw)}")
+        if v.dtype != k.dtype or v.device != k.device:
+            raise ValueError("k and v must share dtype and device")
+        self._pk, self.qk, self._wk = _quant_qk_params(q, k, layout, gran, smooth_k, cq, ck, mq, mk, None,
+                                                       quantize_q=quantize_q)
+        self._pv, self.qv, self._wv = _quant_v_params(v, layout, v_dtype, smooth_v, ck, mk, None)
+        self._L = A.load()
+
+    def run(self):
+        A.check(self._L.sage_quant_qkv(ctypes.byref(self._pk), ctypes.byref(self._pv), _stream()))
+        return self.qk, self.qv
+
+
 def sage_quant_qkv_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, tensor_layout: str = "HND",
                            qk_quant_gran: str = "per_thread", smooth_k: bool = True, v_dtype: str = "fp8",
                            smooth_v: bool = False, cu_seqlens_q: Optional[torch.Tensor] = None,

@@ -1151,7 +1151,7 @@ __device__ __forceinline__ void pv8_all(const VA<DP, 0>& va, const PHalf<0>& P, 
 constexpr int kWaves8 = 8;
 constexpr int kThreads8 = 64 * kWaves8;
 
-template <int DP, bool OUT_BF16, bool KS16, bool PACK>
+template <int DP, bool OUT_BF16, bool KS16, bool PACK, bool QIN>
 __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     constexpr int PV = 0, NW = kWaves8;                 // every wavefront copies its share
     using C = AttnCfg<DP, PV, NW, NW>;
@@ -1222,13 +1222,12 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const int64_t qhead = (int64_t)b * a.Hq + h;
     v4i qf[NCB];
     float qscale = 0.f;
-    // With Q in its input precision the lane loads the 8-channel slices
+    // With Q in its input precision (QIN) the lane loads the 8-channel slices
     // cb*32 + hh*16 + 8e of its row here and quantizes them after the
     // prologue's copies are issued (rows past the sequence load its first row
     // and slices past d the first slice; both become zeros).
-    const bool q_in = a.qraw != nullptr;
-    uint4 qraw[2 * NCB];
-    if (q_in) {
+    v4i qraw[2 * NCB];
+    if constexpr (QIN) {
         const int qr = lane_ok ? qrow : 0;
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.qraw) +
                              (a.cu_q ? (int64_t)(qoff + qr) * a.qsn + (int64_t)h * a.qsh
@@ -1236,7 +1235,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 2 * NCB; ++i) {
             const int c0 = (i >> 1) * 32 + hh * 16 + 8 * (i & 1);
-            qraw[i] = *reinterpret_cast<const uint4*>(qp + (c0 < a.d ? c0 : 0));
+            qraw[i] = *reinterpret_cast<const v4i*>(qp + (c0 < a.d ? c0 : 0));
         }
     } else if (live) {
         const int8_t* q8row = a.q8 + (qhead * a.nq_pad + qrow) * DP;
@@ -1247,6 +1246,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) qf[cb] = v4i{0, 0, 0, 0};
     }
+    float cq = 0.f;                                     // log2-domain row factor times 2^26 (exact)
+    if constexpr (!QIN) cq = ((qscale * a.sm_scale) * kLog2e) * kAccScale;
 
     const int64_t khead = (int64_t)b * a.Hkv + hk;
     const int8_t* kbase = uniform(a.k8 + khead * a.nk_pad * DP + (int64_t)kb0 * DP);
@@ -1319,17 +1320,27 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     // Q in its input precision -> INT8 codes and scales, as the quantize pass
     // makes them: the absolute maximum of the row (its two lanes), of the
     // wavefront's 32 rows (per_warp), or of 4 wavefronts' 128 rows through
-    // LDS (per_block).
-    __shared__ float s_qmax[kWaves8];
+    // LDS (per_block).  The raw values pass through an empty asm statement
+    // first, so that no part of their unpacking is moved above the copies
+    // (which would wait for the Q loads before the copies are issued).  The
+    // LDS slots are the first bytes of the ring's last stage, which no copy
+    // fills before step 2, when every wavefront has long read them (a
+    // separate LDS array would keep the compiler from telling the ring's
+    // reads apart from its copies, and it would then wait for every copy in
+    // flight before each read).
+    float* s_qmax = reinterpret_cast<float*>(smem + (NST - 1) * C::KT_BYTES);
     float qx[2 * NCB][8];
     float qm = 0.f;
-    if (q_in) {
+    if constexpr (QIN) {
+#pragma unroll
+        for (int i = 0; i < 2 * NCB; ++i) asm volatile("" : "+v"(qraw[i]));
 #pragma unroll
         for (int i = 0; i < 2 * NCB; ++i) {
             const bool ok = lane_ok && (i >> 1) * 32 + hh * 16 + 8 * (i & 1) < a.d;
+            const uint4 r = __builtin_bit_cast(uint4, qraw[i]);
             float f16[8], b16[8];
-            unpack8<false>(qraw[i], f16);
-            unpack8<true>(qraw[i], b16);
+            unpack8<false>(r, f16);
+            unpack8<true>(r, b16);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 qx[i][j] = ok ? (a.q_bf16 ? b16[j] : f16[j]) : 0.f;
@@ -1346,7 +1357,7 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     }
     wait_vmcnt<LPT * (AHEAD - 3)>();
     block_sync();
-    if (q_in) {
+    if constexpr (QIN) {
         if (a.gq_shift == 7) {
             const int w0 = wave & ~3;
             qm = fmaxf(fmaxf(s_qmax[w0], s_qmax[w0 + 1]), fmaxf(s_qmax[w0 + 2], s_qmax[w0 + 3]));
@@ -1358,8 +1369,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
             const uint2 lo = int8_codes8(qx[2 * cb], inv), hi = int8_codes8(qx[2 * cb + 1], inv);
             qf[cb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
         }
+        cq = ((qscale * a.sm_scale) * kLog2e) * kAccScale;
     }
-    const float cq = ((qscale * a.sm_scale) * kLog2e) * kAccScale;   // times 2^26, exact
 
     constexpr int NQK = 2 * NCB;
     constexpr int NPV = NCB;
@@ -1670,24 +1681,37 @@ __global__ __launch_bounds__(kThreads) void qk_scores_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The 8-wavefront kernel with INT8 Q, or (128 channels) the one that
+// quantizes Q itself; the host accepts Q in its input precision only there.
+template <int DP, bool OUT_BF16, bool KS16, bool PACK>
+static void launch8(const AttnArgs& a, hipStream_t s) {
+    if constexpr (DP == 128) {
+        if (a.qraw) {
+            attn8_fwd_kernel<DP, OUT_BF16, KS16, PACK, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+            return;
+        }
+    }
+    attn8_fwd_kernel<DP, OUT_BF16, KS16, PACK, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+}
+
 template <int DP, int PV>
 static void attn_dispatch_out(const AttnArgs& a, bool out_bf16, hipStream_t s) {
     if constexpr (PV == 0) {
         const bool ks16 = a.gk_shift == 4;              // per_thread K groups of 16 keys
         if (a.pack_gqa) {
             if (out_bf16) {
-                if (ks16) attn8_fwd_kernel<DP, true, true, true><<<a.num_wg, kThreads8, 0, s>>>(a);
-                else attn8_fwd_kernel<DP, true, false, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+                if (ks16) launch8<DP, true, true, true>(a, s);
+                else launch8<DP, true, false, true>(a, s);
             } else {
-                if (ks16) attn8_fwd_kernel<DP, false, true, true><<<a.num_wg, kThreads8, 0, s>>>(a);
-                else attn8_fwd_kernel<DP, false, false, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+                if (ks16) launch8<DP, false, true, true>(a, s);
+                else launch8<DP, false, false, true>(a, s);
             }
         } else if (out_bf16) {
-            if (ks16) attn8_fwd_kernel<DP, true, true, false><<<a.num_wg, kThreads8, 0, s>>>(a);
-            else attn8_fwd_kernel<DP, true, false, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+            if (ks16) launch8<DP, true, true, false>(a, s);
+            else launch8<DP, true, false, false>(a, s);
         } else {
-            if (ks16) attn8_fwd_kernel<DP, false, true, false><<<a.num_wg, kThreads8, 0, s>>>(a);
-            else attn8_fwd_kernel<DP, false, false, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+            if (ks16) launch8<DP, false, true, false>(a, s);
+            else launch8<DP, false, false, false>(a, s);
         }
     } else {
         if (out_bf16) attn_fwd_kernel<DP, PV, true><<<a.num_wg, kThreads, 0, s>>>(a);

@@ -364,11 +364,13 @@ int sage_quant_qkv_noalloc(const sage_quant_qk_params* qk, const sage_quant_v_pa
 }
 
 // Whether the attention kernel for these sizes quantizes Q itself: the
-// 256-row tile kernel (FP8 V), whole 8-channel slices, and quantization groups
-// that never straddle two heads inside a tile of packed query heads.
+// 256-row tile kernel (FP8 V) at 128 padded channels, whole 8-channel slices,
+// and quantization groups that never straddle two heads inside a tile of
+// packed query heads.  (At 64 channels the key loop of a kernel that also
+// quantizes Q compiles to slower code than the quantize pass saves.)
 static bool q_fusable(int B, int Hq, int Hkv, int Nq, int d, int gran, int v_dtype, int is_causal, bool varlen) {
     if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || d < 1 || d > 128 || Hq % Hkv) return false;
-    if (v_dtype != SAGE_V_FP8 || d % 8 || !valid_gran(gran)) return false;
+    if (v_dtype != SAGE_V_FP8 || d <= 64 || d % 8 || !valid_gran(gran)) return false;
     const bool packed = !varlen && !is_causal && Hq > Hkv && Nq <= sage::kPackMaxNq;
     if (packed && Nq % (1 << q_group_shift(gran))) return false;
     return true;

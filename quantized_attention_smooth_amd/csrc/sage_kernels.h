@@ -56,11 +56,6 @@ struct QuantVArgs {
 struct AttnArgs {
     const int8_t* q8;
     const float* qs;
-    // Q in its input precision instead of q8 / qs (nullptr: not given); the
-    // kernel quantizes it.  Element strides; varlen rows at (cu_q[b] + n) * qsn.
-    const void* qraw;
-    int64_t qsb, qsh, qsn;
-    int q_bf16;
     const int8_t* k8;
     const float* ks;
     const float* kmean;
@@ -93,6 +88,11 @@ struct AttnArgs {
     // debug score dump (sage_debug_qk_scores)
     void* dbg;
     int dbg_mode;
+    // Q in its input precision instead of q8 / qs (nullptr: not given); the
+    // kernel quantizes it.  Element strides; varlen rows at (cu_q[b] + n) * qsn.
+    const void* qraw;
+    int64_t qsb, qsh, qsn;
+    int q_bf16;
 };
 
 // Merge of partial attention results over disjoint key sets (merge.hip).

@@ -25,7 +25,7 @@ DEV = torch.device("cuda:0")
 CASES = [
     # B, Hq, Hkv, Nq, Nk, d, dtype, layout, gran, causal, smooth_v, lse
     (2, 4, 4, 1000, 777, 128, "fp16", "HND", "per_warp", False, False, True),
-    (1, 8, 2, 333, 1200, 64, "bf16", "NHD", "per_thread", True, True, True),
+    (1, 8, 2, 333, 1200, 72, "bf16", "NHD", "per_thread", True, True, True),
     (1, 4, 4, 700, 700, 96, "fp16", "HND", "per_block", False, False, False),
     (1, 4, 4, 600, 650, 128, "bf16", "NHD", "per_block", True, False, True),
     (1, 8, 2, 64, 2000, 128, "bf16", "HND", "per_warp", False, False, True),      # packed rows, Nq % 32 == 0
@@ -129,3 +129,25 @@ def test_sageattn_quantizes_q_in_the_kernel_when_it_can():
                                  quantize_q=False)
     with pytest.raises(NotImplementedError, match="input precision"):
         sage.sage_attn_fwd(qk, qv, tensor_layout="HND")
+
+
+@pytest.mark.parametrize("quantize_q", [True, False])
+def test_quant_plan_matches_the_call(quantize_q):
+    """QuantQKVPlan (outputs and parameter blocks made once) writes what
+    sage_quant_qkv writes, on every run into the same buffers."""
+    w = workloads.WORKLOADS["gqa_prefill_n8192"]
+    print(f"[gpu-case] quantize plan: gqa shape scaled down, quantize_q={quantize_q}", flush=True)
+    inp = workloads.make_inputs(w, {"Nq": 700, "Nk": 700})
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    kw = dict(tensor_layout=w.layout, qk_quant_gran=w.gran, smooth_k=True, v_dtype="fp8", smooth_v=True,
+              quantize_q=quantize_q)
+    ref = sage.sage_quant_qkv(q, k, v, **kw)
+    plan = sage.QuantQKVPlan(q, k, v, **kw)
+    for _ in range(2):
+        got = plan.run()
+        torch.cuda.synchronize()
+        _same_kv(ref, got, "plan")
+        if quantize_q:
+            assert torch.equal(ref[0].q8, got[0].q8) and torch.equal(ref[0].q_scale, got[0].q_scale)
+        else:
+            assert got[0].q8 is None and got[0].q is q

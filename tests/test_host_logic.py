@@ -56,7 +56,7 @@ def test_splitkv_plan():
 
 
 def test_attention_takes_q_in_its_input_precision_only_where_groups_fit_a_tile():
-    """The C ABI's rule (pure host code): FP8 V, head_dim a multiple of 8, and
+    """The C ABI's rule (pure host code): FP8 V, head_dim a multiple of 8 above 64, and
     with packed query heads (grouped heads, non-causal, dense, Nq <= 128)
     whole quantization groups per head."""
     L = sage.load_library()
@@ -72,6 +72,7 @@ def test_attention_takes_q_in_its_input_precision_only_where_groups_fit_a_tile()
     assert not ok(2, 8, 8, 4096, 128, P_WARP, vd=FP16)         # the FP16-V kernel reads INT8 Q
     assert not ok(2, 8, 8, 4096, 100, P_WARP)                   # 8-channel slices
     assert ok(2, 8, 8, 4096, 96, P_BLOCK)
+    assert not ok(2, 8, 8, 4096, 64, P_THREAD)                  # the 64-channel kernel reads INT8 Q
     assert ok(4, 32, 8, 17, 128, P_THREAD)                      # packed rows: one row per group
     assert not ok(4, 32, 8, 40, 128, P_WARP)                    # packed rows: a group would straddle heads
     assert ok(4, 32, 8, 64, 128, P_WARP)
