@@ -2,12 +2,14 @@
 """Throughput of the quantized attention forward on one MI355X.
 
 One step = one pass of the whole hot path over one batch already resident in
-HBM: sage_quant_qkv (K mean and V statistics, INT8 Q/K, FP8 V^T, in two
-launches) and sage_attn_fwd (INT8 QK^T, online softmax, FP8 P.V).  The step
-rate (`value`) comes from eager launches (`--graph` replays the step captured
-in a HIP graph instead).  Kernel times (`attn_kernel_ms`, `quant_ms`) come
-from HIP events around a burst of back-to-back launches of each call after the
-timed steps, where the GPU never waits for the host.  The timed steps carry no
+HBM: sage_quant_qkv (K mean and V statistics, INT8 K, FP8 V^T, in two
+launches; INT8 Q too where the attention kernel does not quantize Q itself)
+and sage_attn_fwd (Q's INT8 codes, INT8 QK^T, online softmax, FP8 P.V).  The
+step rate (`value`) comes from eager launches (`--graph` replays the step
+captured in a HIP graph instead).  Kernel times (`attn_kernel_ms`,
+`quant_ms`) come from HIP events around a burst of back-to-back launches of
+each call after the timed steps, where the GPU never waits for the host (the
+quantize call through QuantQKVPlan, whose outputs are made once).  The timed steps carry no
 events; a second run of as many steps with events around each call gives
 `attn_in_step_ms` and `quant_in_step_ms`, which also see the gaps between the
 step's launches.  Before any of it,
@@ -114,7 +116,8 @@ def cpu_baseline(w, inp, seconds: float) -> dict:
 def make_step(w, inp):
     """The hot-path step of workload w on its inputs, moved to the GPU once:
     sage_quant_qkv (two launches, caller workspaces) then sage_attn_fwd (or
-    sage_attn_varlen_fwd).  Where the attention kernel takes Q in its input
+    sage_attn_varlen_fwd, or sage_attn_fwd_splitkv where sageattn would split
+    the keys).  Where the attention kernel takes Q in its input
     precision and quantizes it itself (as sageattn does), the quantize call
     handles K and V only.  step(ev) records ev[0], ev[1], ev[2] before the
     quantize call, between the calls and after the attention call, on the
@@ -141,10 +144,22 @@ def make_step(w, inp):
                                    smooth_v=w.smooth_v, workspace_k=ws_k, workspace_v=ws_v, quantize_q=not fuse_q,
                                    **qkw)
 
+    # key ranges as sageattn picks them (split-KV when the row tiles alone
+    # leave compute units idle: few queries against many keys)
+    n_splits = 1 if w.varlen else sage.auto_kv_splits(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.causal)
+    ws_split = None
+    if n_splits > 1:
+        need = sage.load_library().sage_attn_splitkv_workspace_size(w.B, w.Hq, w.Nq, w.Nk, w.d, n_splits)
+        ws_split = torch.empty(int(need), dtype=torch.uint8, device=dev)
+
     def attn(qk, qv):
         if w.varlen:
             return sage.sage_attn_varlen_fwd(qk, qv, cu, cu, q.shape[0], is_causal=w.causal,
                                              return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
+        if n_splits > 1:
+            return sage.sage_attn_fwd_splitkv(qk, qv, n_splits=n_splits, tensor_layout=w.layout,
+                                              return_lse=w.return_lse, pv_accum_dtype=w.pv_accum,
+                                              workspace=ws_split)
         return sage.sage_attn_fwd(qk, qv, tensor_layout=w.layout, is_causal=w.causal,
                                   return_lse=w.return_lse, pv_accum_dtype=w.pv_accum)
 
@@ -167,6 +182,7 @@ def make_step(w, inp):
     plan = sage.QuantQKVPlan(q, k, v, qk_quant_gran=w.gran, smooth_k=w.smooth_k, v_dtype=w.v_dtype,
                              smooth_v=w.smooth_v, quantize_q=not fuse_q, **qkw)
     step.quant, step.quant_launch, step.attn, step.fuse_q = quant, plan.run, attn, fuse_q
+    step.n_splits = n_splits
     return step
 
 
@@ -223,7 +239,7 @@ def time_workload(w, steps: int, warmup: int, calibrate: bool = False, settle_ms
     inp = workloads.make_inputs(w)
     dev = torch.device("cuda:0")
     step = make_step(w, inp)
-    inp["fuse_q"] = step.fuse_q
+    inp["fuse_q"], inp["n_splits"] = step.fuse_q, step.n_splits
 
     if calibrate:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
@@ -577,6 +593,7 @@ def main() -> int:
         "attn_pct_of_peak": round(100.0 * attn_tops / peak, 2),
         "attn_in_step_ms": round(attn_step_ms, 5),
         "q_quantized_in": "attention kernel" if inp["fuse_q"] else "quantize pass",
+        "attn_kv_splits": inp["n_splits"],
         "quant_ms": round(quant_ms, 5),
         "quant_gbps": round(quant_bytes / (quant_ms * 1e-3) / 1e9, 1),
         "quant_in_step_ms": round(quant_step_ms, 5),
