@@ -1335,18 +1335,21 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 2 * NCB; ++i) asm volatile("" : "+v"(qraw[i]));
 #pragma unroll
-        for (int i = 0; i < 2 * NCB; ++i) {
+        for (int i = 0; i < 2 * NCB; ++i) {           // rows past the sequence and slices past d: zeros
             const bool ok = lane_ok && (i >> 1) * 32 + hh * 16 + 8 * (i & 1) < a.d;
-            const uint4 r = __builtin_bit_cast(uint4, qraw[i]);
-            float f16[8], b16[8];
-            unpack8<false>(r, f16);
-            unpack8<true>(r, b16);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                qx[i][j] = ok ? (a.q_bf16 ? b16[j] : f16[j]) : 0.f;
-                qm = fmaxf(qm, fabsf(qx[i][j]));
-            }
+            qraw[i] = ok ? qraw[i] : v4i{0, 0, 0, 0};
         }
+        if (a.q_bf16) {
+#pragma unroll
+            for (int i = 0; i < 2 * NCB; ++i) unpack8<true>(__builtin_bit_cast(uint4, qraw[i]), qx[i]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2 * NCB; ++i) unpack8<false>(__builtin_bit_cast(uint4, qraw[i]), qx[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2 * NCB; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qm = fmaxf(qm, fabsf(qx[i][j]));
         qm = fmaxf(qm, __shfl_xor(qm, 32));
         if (a.gq_shift >= 5) {
 #pragma unroll

@@ -111,6 +111,23 @@ def test_q_in_kernel_varlen(gran):
         assert torch.equal(a[1], b[1]), causal
 
 
+def test_q_in_kernel_bf16_input_fp16_output():
+    """Q's element type is the call's input type, independent of the output's."""
+    w = workloads.WORKLOADS["b2h8n4096d128"]
+    print("[gpu-case] Q quantized in the attention kernel: bf16 Q/K/V, fp16 out, per_block", flush=True)
+    inp = workloads.make_inputs(w, {"B": 1, "Hq": 4, "Hkv": 4, "Nq": 520, "Nk": 600, "dtype": "bf16"})
+    q, k, v = (inp[x].to(DEV) for x in ("q", "k", "v"))
+    kw = dict(tensor_layout="HND", qk_quant_gran="per_block", smooth_k=True, v_dtype="fp8")
+    ref = sage.sage_quant_qkv(q, k, v, **kw)
+    fused = sage.sage_quant_qkv(q, k, v, quantize_q=False, **kw)
+    outs = []
+    for qk, qv in (ref, fused):
+        out = torch.empty(q.shape, dtype=torch.float16, device=DEV)
+        outs.append(sage.sage_attn_fwd(qk, qv, tensor_layout="HND", out=out))
+    torch.cuda.synchronize()
+    assert _bits_equal(outs[0], outs[1])
+
+
 def test_sageattn_quantizes_q_in_the_kernel_when_it_can():
     w = workloads.WORKLOADS["b2h8n4096d128"]
     print("[gpu-case] sageattn on b2h8n4096d128 (per_warp, fp16 HND): Q in the kernel", flush=True)
