@@ -120,6 +120,23 @@ def test_workload_outputs(name, big_cases):
     _announce(f"{name}: cos vs oracle {c_emu:.6f}, vs exact fp64 {c_ex:.6f}")
 
 
+@pytest.mark.parametrize("name", BIG)
+def test_benchmark_step_equals_checked_path(name, big_cases):
+    """The step bench.py times, in its launch configuration (Q quantized in
+    the attention kernel where the call allows it), gives the outputs and LSEs
+    of the path checked against the oracle above, bit for bit."""
+    import bench
+    c = _big(name, big_cases)
+    step = bench.make_step(c.w, c.inp)
+    res = step()
+    out, lse = res if isinstance(res, tuple) else (res, None)
+    torch.cuda.synchronize()
+    _announce(f"{name}: benchmark step with Q quantized in the {'attention kernel' if step.fuse_q else 'quantize pass'}")
+    assert np.array_equal(out.float().cpu().numpy(), c.gpu_out)
+    if c.gpu_lse is not None:
+        assert np.array_equal(lse.cpu().numpy(), c.gpu_lse)
+
+
 # ------------------------------------------------------------------ the longest sweep length
 @pytest.mark.parametrize("causal", [False, True])
 def test_sequence_32k_outputs(causal):
