@@ -120,6 +120,17 @@ def test_workload_outputs(name, big_cases):
     _announce(f"{name}: cos vs oracle {c_emu:.6f}, vs exact fp64 {c_ex:.6f}")
 
 
+def test_benchmark_workload_every_row(big_cases):
+    """Every output row of the benchmark workload (2 x 8 heads x 4096 rows)
+    against the oracle, element by element at the forward's tolerance, and
+    against exact fp64 attention by cosine."""
+    c = _big("b2h8n4096d128", big_cases)
+    _announce("b2h8n4096d128: every row against the oracle and exact fp64 attention (about half a minute on the CPU)")
+    c.run_oracle(rows=None, exact=True)
+    c_emu, c_ex = c.check_outputs()
+    _announce(f"b2h8n4096d128 every row: cos vs oracle {c_emu:.6f}, vs exact fp64 {c_ex:.6f}")
+
+
 @pytest.mark.parametrize("name", BIG)
 def test_benchmark_step_equals_checked_path(name, big_cases):
     """The step bench.py times, in its launch configuration (Q quantized in
