@@ -502,15 +502,24 @@ def q_fusable(q: torch.Tensor, B: int, Hq: int, Hkv: int, Nq: int, d: int, qk_qu
     return q.data_ptr() % 16 == 0 and sh % 8 == 0 and sn % 8 == 0 and (varlen or sb % 8 == 0)
 
 
+AUTO_MIN_KEYS_PER_RANGE = 1024
+
+
 def auto_kv_splits(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, is_causal: bool, kv_splits="auto") -> int:
     """Number of key ranges sageattn runs: 1 is the one-pass forward.
     "auto" splits a non-causal call whose row tiles leave compute units idle
-    (splitkv_plan gives at least 2 ranges: few queries against many keys);
-    None or 1 is one pass; an int n >= 2 asks for n ranges (non-causal only)."""
+    (splitkv_plan gives at least 2 ranges: few queries against many keys),
+    into ranges of at least AUTO_MIN_KEYS_PER_RANGE keys: shorter ranges
+    leave each workgroup too little work beside its fixed costs, and every
+    range rounds its own P, so a small call stays one pass.  None or 1 is one
+    pass; an int n >= 2 asks for n ranges (non-causal only)."""
     if kv_splits is None:
         return 1
     if kv_splits == "auto":
-        return 1 if is_causal else splitkv_plan(B, Hq, Nq, Nk, None, Hkv)
+        if is_causal:
+            return 1
+        n = min(splitkv_plan(B, Hq, Nq, Nk, None, Hkv), Nk // AUTO_MIN_KEYS_PER_RANGE)
+        return n if n >= 2 else 1
     n = int(kv_splits)
     if n < 1:
         raise ValueError("kv_splits must be 'auto', None or an int >= 1")

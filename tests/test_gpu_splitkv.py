@@ -156,7 +156,7 @@ def test_sageattn_splits_by_default_only_when_the_gpu_is_not_filled():
         q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
         out = sage.sageattn(q, k, v)
         qk, qv = sage.sage_quant_qkv(q, k, v, qk_quant_gran="per_thread")
-        ns = sage.splitkv_plan(shape["B"], shape["Hq"], shape["Nq"], shape["Nk"], Hkv=shape["Hkv"])
+        ns = sage.auto_kv_splits(shape["B"], shape["Hq"], shape["Hkv"], shape["Nq"], shape["Nk"], False)
         assert (ns > 1) == split
         ref = sage.sage_attn_fwd_splitkv(qk, qv, n_splits=ns) if split else sage.sage_attn_fwd(qk, qv)
         torch.cuda.synchronize()

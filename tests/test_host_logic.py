@@ -92,6 +92,9 @@ def test_sageattn_splits_automatically_only_when_compute_units_idle():
     assert sage.auto_kv_splits(4, 32, 8, 16, 32768, True) == 1              # causal calls run one pass
     assert sage.auto_kv_splits(4, 32, 8, 16, 32768, False, None) == 1       # None: one pass
     assert sage.auto_kv_splits(4, 32, 8, 16, 32768, False, 3) == 3
+    # ranges of at least 1024 keys: a small call stays one pass
+    assert sage.splitkv_plan(1, 2, 640, 640) >= 2 and sage.auto_kv_splits(1, 2, 2, 640, 640, False) == 1
+    assert sage.auto_kv_splits(2, 8, 8, 8, 5000, False) == 4              # 16 by the plan, 4 by the key count
     with pytest.raises(NotImplementedError):
         sage.auto_kv_splits(1, 1, 1, 1, 1, True, 2)
     with pytest.raises(ValueError):
