@@ -122,7 +122,7 @@ def test_packed_gqa_rows_equal_repeated_kv(nq):
 
 def test_sageattn_kv_splits_matches_oracle():
     """sageattn(..., kv_splits="auto") on a decode shape equals the oracle's
-    split emulation with the number of ranges the plan picks."""
+    split emulation with the number of ranges auto_kv_splits picks."""
     print("[gpu-case] sageattn kv_splits=auto: B2 Hq8 Hkv8 Nq8 Nk5000 d64 fp16 HND seed 2", flush=True)
     w = workloads.WORKLOADS["b2h8n4096d128"]
     inp = workloads.make_inputs(w, {"B": 2, "Hq": 8, "Hkv": 8, "Nq": 8, "Nk": 5000, "d": 64})
@@ -130,7 +130,7 @@ def test_sageattn_kv_splits_matches_oracle():
     q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
     out = sage.sageattn(q, k, v, kv_splits="auto")
     torch.cuda.synchronize()
-    ns = sage.splitkv_plan(2, 8, 8, 5000, Hkv=8)
+    ns = sage.auto_kv_splits(2, 8, 8, 8, 5000, False)
     assert ns > 1
     ref = oracle.reference_forward_splitkv(*(inp[x].float().numpy() for x in ("q", "k", "v")), dtype="fp16",
                                            n_splits=ns, exp_band=EXP_BAND)
