@@ -1159,7 +1159,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     constexpr int AHEAD = 5;                            // tiles in flight ahead of the one being read
     constexpr int NST = AHEAD + 3;                      // ring stages (see the key-loop comment)
     constexpr int LPT = C::NI + C::NSC;                 // copy instructions per copying wavefront per tile
-    __shared__ __attribute__((aligned(16))) uint8_t smem[NST * C::STAGE];
+    // the ring, then the epilogue's per-channel factors (V scale, V mean, K mean)
+    __shared__ __attribute__((aligned(16))) uint8_t smem[NST * C::STAGE + 3 * DP * 4];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1250,6 +1251,24 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     if constexpr (!QIN) cq = ((qscale * a.sm_scale) * kLog2e) * kAccScale;
 
     const int64_t khead = (int64_t)b * a.Hkv + hk;
+    // The epilogue's per-channel factors of this K/V head (V scale, V mean, K
+    // mean; V's scale row stands in for an absent mean) are loaded here and
+    // staged in LDS past the ring after the prologue's barrier: every lane
+    // needs 64 of them, and 512 threads reading them from L2 at the end took
+    // microseconds.
+    constexpr int FPL = DP / 64;                        // factors per lane per row
+    float fac[3][FPL];
+    {
+        const float* fs = a.vs + khead * DP;
+        const float* fm = a.vmean ? a.vmean + khead * DP : fs;
+        const float* fk = a.kmean ? a.kmean + khead * DP : fs;
+#pragma unroll
+        for (int j = 0; j < FPL; ++j) {
+            fac[0][j] = fs[lane * FPL + j];
+            fac[1][j] = fm[lane * FPL + j];
+            fac[2][j] = fk[lane * FPL + j];
+        }
+    }
     const int8_t* kbase = uniform(a.k8 + khead * a.nk_pad * DP + (int64_t)kb0 * DP);
     const float* ksbase = uniform(a.ks + khead * (a.nk_pad >> a.gk_shift) + (kb0 >> a.gk_shift));
     const uint8_t* vbase = uniform(reinterpret_cast<const uint8_t*>(a.vt) + khead * DP * a.nk_pad + kb0);
@@ -1373,6 +1392,14 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
             qf[cb] = v4i{(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
         }
         cq = ((qscale * a.sm_scale) * kLog2e) * kAccScale;
+    }
+    float* s_fac = reinterpret_cast<float*>(smem + NST * C::STAGE);
+    if (wave == 0) {                                    // read in the epilogue, after many barriers
+#pragma unroll
+        for (int f = 0; f < 3; ++f)
+#pragma unroll
+            for (int j = 0; j < FPL; ++j) s_fac[f * DP + lane * FPL + j] = fac[f][j];
+        wait_lgkm0();
     }
 
     constexpr int NQK = 2 * NCB;
@@ -1520,33 +1547,18 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     }
     if (!live) return;
 
-    // ---- epilogue: normalise, add back V's mean, write in the caller's layout
-    // the lane's channels' V scale and mean factors, all loads issued first
-    // (without a mean the scale row is read a second time and not used).  The
-    // head's offset is recomputed from an opaque copy of its index, so that
-    // the compiler does not share it with the key loop's address arithmetic
-    // and keep it live through the loop.
-    int64_t kh = khead;
-#if __HIP_DEVICE_COMPILE__
-    asm volatile("" : "+s"(kh));
-#endif
-    const float* vsc = a.vs + kh * DP;
+    // ---- epilogue: normalise, add back V's mean, write in the caller's layout,
+    // with the lane's channels' V scale and mean factors from LDS
     const bool has_mu = a.vmean != nullptr;
-    const float* vmu = has_mu ? a.vmean + kh * DP : vsc;
-    // (at Dp = 64 the batched loads change how the compiler allocates the key
-    // loop's scalar registers, and that costs more than the epilogue saves:
-    // there each factor is loaded where it is used)
-    constexpr bool kBatch = DP == 128;
     v4f sc4[NCB][4], mu4[NCB][4];
-    if constexpr (kBatch) {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb)
+    for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                sc4[cb][r4] = load_ch4(vsc, cb * 32 + 8 * r4 + 4 * hh);
-                mu4[cb][r4] = load_ch4(vmu, cb * 32 + 8 * r4 + 4 * hh);
-            }
-    }
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int c0 = cb * 32 + 8 * r4 + 4 * hh;
+            sc4[cb][r4] = *(lds_v4f*)(s_fac + c0);
+            mu4[cb][r4] = *(lds_v4f*)(s_fac + DP + c0);
+        }
     const float l_tot = ls[0];
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
     if (lane_ok) {
@@ -1562,14 +1574,8 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
                 float val[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {               // channels past d are not stored
-                    if constexpr (kBatch) {
-                        val[e] = o[cb][4 * r4 + e] * (sc4[cb][r4][e] * inv_l);
-                        if (has_mu) val[e] += mu4[cb][r4][e];
-                    } else {
-                        const int c = min(c0 + e, a.d - 1);
-                        val[e] = o[cb][4 * r4 + e] * (vsc[c] * inv_l);
-                        if (has_mu) val[e] += vmu[c];
-                    }
+                    val[e] = o[cb][4 * r4 + e] * (sc4[cb][r4][e] * inv_l);
+                    if (has_mu) val[e] += mu4[cb][r4][e];
                 }
                 store_out4<OUT_BF16>(a.out, a.out_f32, a.out_vec4, row_off, c0, a.d, val);
             }
@@ -1578,21 +1584,17 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         constexpr float p_log2_scale = kPLog2Scale<0>;
         float part = 0.f;
         if (a.kmean) {
-            const float* km = a.kmean + kh * DP;
-            v4f km4[NCB][4];                            // all loads first (at Dp = 128)
-            if constexpr (kBatch) {
+            v4f km4[NCB][4];
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb)
+            for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) km4[cb][u] = load_ch4(km, cb * 32 + hh * 16 + 4 * u);
-            }
+                for (int u = 0; u < 4; ++u) km4[cb][u] = *(lds_v4f*)(s_fac + 2 * DP + cb * 32 + hh * 16 + 4 * u);
 #pragma unroll
             for (int cb = 0; cb < NCB; ++cb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int code = (int)(int8_t)((qf[cb][e >> 2] >> (8 * (e & 3))) & 0xff);
-                    if constexpr (kBatch) part += (float)code * km4[cb][e >> 2][e & 3];
-                    else part += (float)code * km[cb * 32 + hh * 16 + e];
+                    part += (float)code * km4[cb][e >> 2][e & 3];
                 }
         }
         const float dot = swap_half_sum(part);
