@@ -1561,7 +1561,55 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
         }
     const float l_tot = ls[0];
     const float inv_l = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (lane_ok) {
+    auto out_val = [&](int cb, int r4, float (&val)[4]) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            val[e] = o[cb][4 * r4 + e] * (sc4[cb][r4][e] * inv_l);
+            if (has_mu) val[e] += mu4[cb][r4][e];
+        }
+    };
+    if (a.out_vec8) {
+        // 16-bit rows with 16-byte alignment: the wavefront stages its 32 rows
+        // in its own slice of the ring (free now: every copy has landed and
+        // every wavefront has passed the last barrier), rows padded by 16 bytes
+        // against bank conflicts, then stores whole 16-byte pieces, 64 of
+        // them per instruction over consecutive row memory.  (Straight from
+        // the MFMA layout, each store instruction wrote 8 bytes into each of
+        // 32 rows, and the stores took about half of the epilogue.)
+        constexpr int RS = DP * 2 + 16;                 // bytes per staged row
+        constexpr int CPR = DP / 8;                     // 16-byte pieces per row
+        uint8_t* wt = smem + wave * 32 * RS;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                float val[4];
+                out_val(cb, r4, val);
+                uint16_t hv[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) hv[e] = Half<OUT_BF16>::from_f(val[e]);
+                *reinterpret_cast<uint2*>(wt + n * RS + (cb * 32 + 8 * r4 + 4 * hh) * 2) =
+                    make_uint2((uint32_t)hv[0] | ((uint32_t)hv[1] << 16), (uint32_t)hv[2] | ((uint32_t)hv[3] << 16));
+            }
+        wait_lgkm0();                                   // the wavefront reads back only its own rows
+#pragma unroll
+        for (int i = 0; i < 32 * CPR / 64; ++i) {
+            const int q = i * 64 + lane, r = q / CPR, c8 = (q % CPR) * 8;
+            const int rr = wq0 + r;                     // row of the workgroup's row space
+            if (rr >= Lrows || c8 >= a.d) continue;
+            int hr = h0, qr = rr;
+            if (pack) {
+                const int hi = rr / Lq;
+                hr = h0 + hi;
+                qr = rr - hi * Lq;
+            }
+            const int64_t row_off = split * a.split_out +
+                                    (a.cu_q ? (int64_t)(qoff + qr) * a.on + (int64_t)hr * a.oh
+                                            : (int64_t)b * a.ob + (int64_t)hr * a.oh + (int64_t)qr * a.on);
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(a.out) + row_off + c8) =
+                *reinterpret_cast<const uint4*>(wt + r * RS + c8 * 2);
+        }
+    } else if (lane_ok) {
         const int64_t row_off = split * a.split_out +
                                 (a.cu_q ? (int64_t)(qoff + qrow) * a.on + (int64_t)h * a.oh
                                         : (int64_t)b * a.ob + (int64_t)h * a.oh + (int64_t)qrow * a.on);
@@ -1570,13 +1618,9 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int c0 = cb * 32 + 8 * r4 + 4 * hh;
-                if (c0 >= a.d) continue;
+                if (c0 >= a.d) continue;                // channels past d are not stored
                 float val[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {               // channels past d are not stored
-                    val[e] = o[cb][4 * r4 + e] * (sc4[cb][r4][e] * inv_l);
-                    if (has_mu) val[e] += mu4[cb][r4][e];
-                }
+                out_val(cb, r4, val);
                 store_out4<OUT_BF16>(a.out, a.out_f32, a.out_vec4, row_off, c0, a.d, val);
             }
     }

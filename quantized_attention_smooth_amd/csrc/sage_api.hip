@@ -425,6 +425,8 @@ static sage::AttnArgs attn_args(const sage_attn_params* p) {
     a.sm_scale = p->sm_scale > 0.f ? p->sm_scale : (float)(1.0 / std::sqrt((double)p->d));
     a.ob = p->o_stride_b; a.oh = p->o_stride_h; a.on = p->o_stride_n;
     a.out_vec4 = aligned(p->out, 8) && p->o_stride_n % 4 == 0 && p->o_stride_h % 4 == 0 && p->o_stride_b % 4 == 0;
+    a.out_vec8 = aligned(p->out, 16) && p->o_stride_n % 8 == 0 && p->o_stride_h % 8 == 0 && p->o_stride_b % 8 == 0 &&
+                 p->d % 8 == 0;
     a.n_qtiles = (int)((p->Nq + sage::kBQ - 1) / sage::kBQ);
     a.num_wg = p->B * p->Hq * a.n_qtiles;
     return a;
@@ -467,6 +469,8 @@ int sage_attn_varlen_fwd(const sage_attn_varlen_params* p, void* stream) {
     a.lse_varlen = 1;
     a.total_q = p->total_q;
     a.out_vec4 = aligned(p->base.out, 8) && p->base.o_stride_n % 4 == 0 && p->base.o_stride_h % 4 == 0;
+    a.out_vec8 = aligned(p->base.out, 16) && p->base.o_stride_n % 8 == 0 && p->base.o_stride_h % 8 == 0 &&
+                 p->base.d % 8 == 0;
     if (int r = hip_status(sage::launch_attn(a, dp_of(p->base.d), pv_kind(&p->base), p->base.out_dtype == SAGE_BF16,
                                              reinterpret_cast<hipStream_t>(stream)),
                            "varlen attention launch"))
@@ -557,6 +561,7 @@ int sage_attn_fwd_splitkv(const sage_attn_params* p, int n_splits, void* workspa
     sage::AttnArgs a = attn_args(p);
     a.out = ws;
     a.out_f32 = 1;
+    a.out_vec8 = 0;                                     // (fp32 partial results: the 8-byte path)
     a.ob = (int64_t)p->Hq * p->Nq * d;
     a.oh = (int64_t)p->Nq * d;
     a.on = d;

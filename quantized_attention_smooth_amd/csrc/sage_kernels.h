@@ -73,6 +73,7 @@ struct AttnArgs {
     float sm_scale;
     int64_t ob, oh, on;
     int out_vec4;                // 4 consecutive channels may be stored as one 8-byte (16-byte fp32) write
+    int out_vec8;                // 16-bit output whose rows take 16-byte writes of 8 channels (d % 8 == 0)
     int out_f32;                 // out holds fp32 values (split-KV partial results), strides in floats
     int lse_varlen;              // LSE layout [Hq][total_q] instead of [B][Hq][Nq]
     int total_q;
