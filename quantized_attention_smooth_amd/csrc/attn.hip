@@ -616,6 +616,16 @@ __device__ __forceinline__ bool softmax_half(const v16i (&S)[2], const float (&k
     return raise;
 }
 
+// Causal mask of one 32-key half of a tile in the pipelined loop.  Element i
+// of the lane's scores is key 8*(i/4) + 4*hh + i%4 of the half; lim is the
+// lane's row minus the half's first key minus 4*hh, so the key is visible iff
+// its offset 8*(i/4) + i%4 <= lim.  Masked scores become the -inf pattern,
+// which no group maximum takes and whose exponent is -inf (P = 0).
+__device__ __forceinline__ void causal_mask_half(v16i& Sk, int lim) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Sk[i] = 8 * (i >> 2) + (i & 3) <= lim ? Sk[i] : kNegInfBits;
+}
+
 // The unmasked softmax of one row block cut into pieces that the pipelined
 // loop interleaves with MFMAs: head<0..3>() compute the scale factors and the
 // tile maximum and take the raise decision (the same steps and roundings as
@@ -676,6 +686,14 @@ struct SoftmaxPieces {
 #pragma unroll
             for (int g = 0; g < 4; ++g) f[g] = f0;
         }
+    }
+    // A floor of FLT_MIN under the scale factors where scores can be masked:
+    // a masked score (the -inf pattern) times a factor of 0 would give NaN,
+    // with the floor it gives -inf.  The other exponents keep their values:
+    // the floor's products are below half an ulp of the offset they join.
+    __device__ __forceinline__ void floor_f() {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) f[g] = fmaxf(f[g], 1.17549435e-38f);
     }
     __device__ __forceinline__ void gmax(const v16i& Sk, int g) { group_max(Sk, g); }
     __device__ __forceinline__ void spec(float m_ref) {
@@ -1151,7 +1169,7 @@ __device__ __forceinline__ void pv8_all(const VA<DP, 0>& va, const PHalf<0>& P, 
 constexpr int kWaves8 = 8;
 constexpr int kThreads8 = 64 * kWaves8;
 
-template <int DP, bool OUT_BF16, bool KS16, bool PACK, bool QIN>
+template <int DP, bool OUT_BF16, bool KS16, bool PACK, bool QIN, bool CAUSAL>
 __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     constexpr int PV = 0, NW = kWaves8;                 // every wavefront copies its share
     using C = AttnCfg<DP, PV, NW, NW>;
@@ -1202,7 +1220,10 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     const int hk = h0 / grp;
     const int kend = a.causal ? min(Lk, q0 + kBQ) : Lk;
     const int ntiles = (kend + kBK - 1) / kBK;
-    const int n_main = (a.causal ? min(q0, Lk) : Lk) / kBK;
+    // CAUSAL: every full tile runs in the pipelined loop, the diagonal ones
+    // with the keys after each row masked; otherwise (and for the 4-wave
+    // kernel) the diagonal tiles run one at a time after the loop
+    const int n_main = CAUSAL ? kend / kBK : (a.causal ? min(q0, Lk) : Lk) / kBK;
 
     // ---- per-lane query state: row wq0 + n of the row space
     const int wq0 = q0 + wave * 32;
@@ -1463,7 +1484,10 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
                     rs_job<PV, 0>(P, ones, ls);
                 }
                 if constexpr (k >= 1 && k - 1 < NDMA) copier.template issue<k - 1>(st_copy, tc);
-                if constexpr (k == 0) sp.prep(ksv, cq);
+                if constexpr (k == 0) {
+                    sp.prep(ksv, cq);
+                    if constexpr (CAUSAL) sp.floor_f();
+                }
                 if constexpr (k == NQK - 1) {           // K of tile t+1 (kf is free once the last QK^T MFMA issued)
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb)
@@ -1473,6 +1497,12 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
                 }
                 // group maxima of tile t, one or two per P.V MFMA, then the
                 // raise decision
+                // a tile with keys after the wavefront's first row: the
+                // scores of keys after the lane's row become the -inf pattern
+                if constexpr (CAUSAL && (k == NQK + 1 || k == NQK + 2)) {
+                    constexpr int kb = k - NQK - 1;
+                    if (t * kBK + kBK - 1 > wq0) causal_mask_half(S[kb], qrow - t * kBK - kb * 32 - 4 * hh);
+                }
                 if constexpr (k == NQK + 1) { sp.gmax(S[0], 0); sp.gmax(S[0], 1); }
                 if constexpr (k == NQK + 2) { sp.gmax(S[1], 2); sp.gmax(S[1], 3); }
                 if constexpr (k == NH - 1) sp.decide(m_ref, m_prev);
@@ -1732,15 +1762,26 @@ __global__ __launch_bounds__(kThreads) void qk_scores_kernel(AttnArgs a) {
 // ---------------------------------------------------------------------------
 // The 8-wavefront kernel with INT8 Q, or (128 channels) the one that
 // quantizes Q itself; the host accepts Q in its input precision only there.
+template <int DP, bool OUT_BF16, bool KS16, bool PACK, bool QIN>
+static void launch8c(const AttnArgs& a, hipStream_t s) {
+    if constexpr (!PACK) {                              // packed rows are non-causal only
+        if (a.causal) {
+            attn8_fwd_kernel<DP, OUT_BF16, KS16, PACK, QIN, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+            return;
+        }
+    }
+    attn8_fwd_kernel<DP, OUT_BF16, KS16, PACK, QIN, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+}
+
 template <int DP, bool OUT_BF16, bool KS16, bool PACK>
 static void launch8(const AttnArgs& a, hipStream_t s) {
     if constexpr (DP == 128) {
         if (a.qraw) {
-            attn8_fwd_kernel<DP, OUT_BF16, KS16, PACK, true><<<a.num_wg, kThreads8, 0, s>>>(a);
+            launch8c<DP, OUT_BF16, KS16, PACK, true>(a, s);
             return;
         }
     }
-    attn8_fwd_kernel<DP, OUT_BF16, KS16, PACK, false><<<a.num_wg, kThreads8, 0, s>>>(a);
+    launch8c<DP, OUT_BF16, KS16, PACK, false>(a, s);
 }
 
 template <int DP, int PV>

@@ -349,6 +349,37 @@ def test_all_zero_k_gives_uniform_attention():
     assert torch.max(torch.abs(outc - refc)) < 2e-3
 
 
+@pytest.mark.parametrize("d, gran", [(128, "per_warp"), (128, "per_thread"), (64, "per_block"), (64, "per_thread")])
+def test_causal_zero_scales_fp8_v(d, gran):
+    """Causal FP8-V attention with zero scale factors on the diagonal tiles:
+    head 0's keys are all equal, so smooth_k leaves K at zero and every K
+    scale is 0; rows 100-299 of Q are zero (Q scale 0).  Every score is then
+    0, and masked keys must still get no weight.  Checked against the oracle
+    and exact attention; at 128 channels the call that quantizes Q in the
+    attention kernel must give the same bits."""
+    base = workloads.WORKLOADS["b2h8n4096d128"]
+    w = dataclasses.replace(base, B=1, Hq=2, Hkv=2, Nq=700, Nk=700, d=d, gran=gran, causal=True, seed=31)
+    _announce(f"causal zero scales: B1 H2 N700 d{d} {gran} V=fp8 seed 31")
+    inp = workloads.make_inputs(w)
+    k = inp["k"].clone()
+    k[:, 0] = k[:, 0, :1]                                   # HND: head 0's keys all equal to its first
+    q = inp["q"].clone()
+    q[:, :, 100:300] = 0
+    inp["k"], inp["q"] = k, q
+    c = Case(w, inp).run_gpu(return_lse=True).run_oracle(exact=True)
+    c.check_quantized_bitexact()
+    c.check_outputs(lse=True)
+    if sage.q_fusable(q.cuda(), 1, 2, 2, 700, d, gran, "fp8", True, False, (q.stride(0), q.stride(1), q.stride(2))):
+        qc, kc, vc = q.cuda(), k.cuda(), inp["v"].cuda()
+        kw = dict(tensor_layout="HND", qk_quant_gran=gran, smooth_k=True, v_dtype="fp8", smooth_v=w.smooth_v)
+        ref = sage.sage_attn_fwd(*sage.sage_quant_qkv(qc, kc, vc, **kw), is_causal=True, return_lse=True)
+        fused = sage.sage_attn_fwd(*sage.sage_quant_qkv(qc, kc, vc, quantize_q=False, **kw), is_causal=True,
+                                   return_lse=True)
+        torch.cuda.synchronize()
+        assert torch.equal(ref[0].view(torch.int16), fused[0].view(torch.int16))
+        assert torch.equal(ref[1], fused[1])
+
+
 def test_single_key_returns_its_value():
     _announce("one key")
     g = torch.Generator().manual_seed(11)
