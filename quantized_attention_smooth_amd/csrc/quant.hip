@@ -77,6 +77,21 @@ __device__ __forceinline__ uint4 load_raw8(const uint16_t* row, int c0, int d) {
     }
 }
 
+// load_raw8 in two halves, for a workgroup that issues other loads before it
+// reads the row values: the load (channel 0 in place of channels past d) and
+// the mask that zeroes those channels.  A select on the loaded value right
+// after the load would make the workgroup wait for it there.
+template <bool VEC>
+__device__ __forceinline__ uint4 load_raw8_unmasked(const uint16_t* row, int c0, int d) {
+    if constexpr (VEC) return *reinterpret_cast<const uint4*>(row + (c0 < d ? c0 : 0));
+    else return load_raw8<false>(row, c0, d);
+}
+template <bool VEC>
+__device__ __forceinline__ uint4 mask_raw8(const uint4& r, int c0, int d) {
+    if constexpr (VEC) return c0 < d ? r : make_uint4(0u, 0u, 0u, 0u);
+    else return r;
+}
+
 // Workgroup id -> (unit, head, sequence), the head varying fastest: with
 // token-major layouts (NHD, packed varlen) the rows of all heads of a token
 // are adjacent, so workgroups that run together read adjacent memory.
@@ -373,19 +388,21 @@ __device__ __forceinline__ void quant_rows_body(const QuantRowsArgs& a, int tile
 #pragma unroll
         for (int p = 0; p < PASSES; ++p) {
             const int n = min(row0 + p * RPP + rr, N - 1);
-            raw[p] = load_raw8<VEC>(row_ptr(a.x, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d);
+            raw[p] = load_raw8_unmasked<VEC>(row_ptr(a.x, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d);
         }
     }
+    // the statistics partials are read while the rows are in flight (one
+    // memory round trip instead of two)
+    __shared__ float s_mu[DP];
+    if (ks) tile_stats<BF16, DP>(*ks, tile, h, b, s_mu, nullptr);
     float vals[PASSES][8];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
         const bool in = row0 + p * RPP + rr < N;
-        unpack8<BF16>(N > 0 ? raw[p] : make_uint4(0u, 0u, 0u, 0u), vals[p]);
+        unpack8<BF16>(N > 0 ? mask_raw8<VEC>(raw[p], cg * 8, a.d) : make_uint4(0u, 0u, 0u, 0u), vals[p]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) vals[p][j] = in ? vals[p][j] : 0.f;
     }
-    __shared__ float s_mu[DP];
-    if (ks) tile_stats<BF16, DP>(*ks, tile, h, b, s_mu, nullptr);
     float mu[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) mu[j] = ks ? s_mu[cg * 8 + j] : 0.f;
@@ -495,19 +512,20 @@ __device__ __forceinline__ void quant_v_body(const QuantVArgs& a, const StatsArg
 #pragma unroll
         for (int p = 0; p < KPG; ++p) {                 // keys past the sequence reread its last key
             const int n = min(row0 + g * KPG + p, N - 1);
-            raw[p] = load_raw8<VEC>(row_ptr(a.v, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d);
+            raw[p] = load_raw8_unmasked<VEC>(row_ptr(a.v, a.sb, a.sh, a.sn, a.cu, b, h, n0, n), cg * 8, a.d);
         }
     }
+    // the statistics partials are read while the keys are in flight
+    __shared__ float s_mu[DP], s_inv[DP];
+    if (have_stats) tile_stats<BF16, DP>(vs, tile, h, b, s_mu, s_inv);
     float v[KPG][8];
 #pragma unroll
     for (int p = 0; p < KPG; ++p) {
         const bool in = row0 + g * KPG + p < N;
-        unpack8<BF16>(N > 0 ? raw[p] : make_uint4(0u, 0u, 0u, 0u), v[p]);
+        unpack8<BF16>(N > 0 ? mask_raw8<VEC>(raw[p], cg * 8, a.d) : make_uint4(0u, 0u, 0u, 0u), v[p]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) v[p][j] = in ? v[p][j] : 0.f;
     }
-    __shared__ float s_mu[DP], s_inv[DP];
-    if (have_stats) tile_stats<BF16, DP>(vs, tile, h, b, s_mu, s_inv);
     float mu[8], inv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
