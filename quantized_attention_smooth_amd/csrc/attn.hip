@@ -1198,15 +1198,12 @@ __global__ __launch_bounds__(kThreads8, 1) void attn8_fwd_kernel(AttnArgs a) {
     }
     const int nbh = a.num_wg / (a.n_qtiles * a.n_splits);
     int qt = lpt ? wg / nbh : wg % a.n_qtiles;
-    const int grp = a.Hq / a.Hkv;
-    int bh = lpt ? wg % nbh : wg / a.n_qtiles;
-    if (lpt && grp > 1 && !PACK) {
-        // Within a row of equally long tiles, the query heads of one K/V head
-        // are nkv workgroups apart, so that (nkv a multiple of the 8 XCDs,
-        // workgroups dealt to the XCDs in turn) they share one XCD and its L2.
-        const int nkv = nbh / grp;
-        bh = (bh % nkv) * grp + bh / nkv;
-    }
+    const int bh0 = lpt ? wg % nbh : wg / a.n_qtiles, grp = a.Hq / a.Hkv;
+    // Causal (longest rows first): within a row of equally long tiles, the
+    // query heads of one K/V head are nkv = nbh / grp workgroups apart, so
+    // that (nkv a multiple of the 8 XCDs, workgroups dealt to the XCDs in
+    // turn) they share one XCD and its L2.
+    const int bh = CAUSAL && grp > 1 ? (bh0 % (nbh / grp)) * grp + bh0 / (nbh / grp) : bh0;
     // packed GQA rows (non-causal, dense): the workgroup covers row r of the
     // rows of all grp query heads of one K/V head, query head
     // hk * grp + r / Nq, query r % Nq, so K and V stream once per group
